@@ -1,0 +1,557 @@
+/*
+ * zf_oracle.c -- CPU oracle for the sharded mixed-precision AdamW step.
+ *
+ * TEST INFRASTRUCTURE ONLY: see zf_oracle.h.  The product path never loads it.
+ *
+ * Every float expression is written as the binary32 operation sequence it
+ * defines; with -ffp-contract=off and SSE scalar arithmetic each operator
+ * rounds once, to nearest-even.  Double is used only where the reading of the
+ * pages says so (the squared-norm accumulation and the per-step scalars).
+ */
+#include "zf_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* Casts between binary32 and the two 16-bit formats.  IEEE round-to-nearest-
+ * even, written with integer arithmetic so that no library conversion is
+ * involved.  NaN maps to a quiet NaN of the same sign (never reached by an
+ * applied step: a non-finite gradient skips the step).                      */
+
+static uint32_t f2u(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+static float u2f(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+
+float or_bf16_to_f32(uint16_t h) { return u2f((uint32_t)h << 16); }
+
+float or_f16_to_f32(uint16_t h) {
+  uint32_t sign = (uint32_t)(h & 0x8000u) << 16;
+  uint32_t e = (h >> 10) & 0x1Fu;
+  uint32_t f = h & 0x3FFu;
+  if (e == 0x1F) return u2f(sign | 0x7F800000u | (f << 13));          /* inf / NaN */
+  if (e != 0) return u2f(sign | ((e - 15 + 127) << 23) | (f << 13));   /* normal */
+  /* zero or subnormal: value = f * 2^-24, exact in binary32 */
+  {
+    float mag = (float)f * 5.9604644775390625e-8f;
+    return (sign != 0u) ? -mag : mag;
+  }
+}
+
+uint16_t or_f32_to_bf16(float x) {
+  uint32_t u = f2u(x);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
+  /* add just under half an ulp, plus one if the kept lsb is odd (ties to even) */
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+uint16_t or_f32_to_f16(float x) {
+  uint32_t u = f2u(x);
+  uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+  uint32_t a = u & 0x7FFFFFFFu;
+  int32_t e;
+  uint32_t mant, q, rem, halfway;
+  int shift;
+  if (a > 0x7F800000u) return (uint16_t)(sign | 0x7E00u);   /* NaN */
+  if (a >= 0x47800000u) return (uint16_t)(sign | 0x7C00u);  /* |x| >= 2^16, or inf */
+  if (a < 0x00800000u) return sign;                          /* binary32 zero/subnormal */
+  e = (int32_t)(a >> 23) - 127;
+  mant = (a & 0x7FFFFFu) | 0x800000u;                        /* 24-bit significand */
+  if (e >= -14) {
+    /* normal binary16: keep 11 significant bits */
+    q = mant >> 13;
+    rem = mant & 0x1FFFu;
+    if (rem > 0x1000u || (rem == 0x1000u && (q & 1u))) q += 1u;
+    /* q in [0x400, 0x800]; a carry to 0x800 bumps the exponent, up to inf */
+    return (uint16_t)(sign | (uint16_t)((uint32_t)(e + 14) * 1024u + q));
+  }
+  /* subnormal binary16: units of 2^-24; value / 2^-24 = mant * 2^(e+1) */
+  shift = -(e + 1);
+  if (shift > 25) return sign;
+  q = mant >> shift;
+  rem = mant & ((1u << shift) - 1u);
+  halfway = 1u << (shift - 1);
+  if (rem > halfway || (rem == halfway && (q & 1u))) q += 1u;
+  return (uint16_t)(sign | q);
+}
+
+void or_cast_array(int32_t dtype, int64_t n, const float* src, uint16_t* dst) {
+  int64_t i;
+  for (i = 0; i < n; ++i)
+    dst[i] = (dtype == OR_BF16) ? or_f32_to_bf16(src[i]) : or_f32_to_f16(src[i]);
+}
+
+void or_widen_array(int32_t dtype, int64_t n, const uint16_t* src, float* dst) {
+  int64_t i;
+  for (i = 0; i < n; ++i)
+    dst[i] = (dtype == OR_BF16) ? or_bf16_to_f32(src[i]) : or_f16_to_f32(src[i]);
+}
+
+static float widen(int32_t dtype, uint16_t h) {
+  return (dtype == OR_BF16) ? or_bf16_to_f32(h) : or_f16_to_f32(h);
+}
+static uint16_t narrow(int32_t dtype, float f) {
+  return (dtype == OR_BF16) ? or_f32_to_bf16(f) : or_f32_to_f16(f);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Seeded inputs.  splitmix64 (Steele, Lea and Flood, "Fast splittable
+ * pseudorandom number generators", OOPSLA 2014) used as a counter-based
+ * generator: output j of a generator whose state starts at s is
+ * mix(s + (j+1)*gamma).  A stream's starting state is output number `stream`
+ * of the generator seeded with `seed`.  Element i of a stream consumes outputs
+ * 3i, 3i+1, 3i+2: twelve 16-bit words k, and z = (sum k - 393210) / 65536 is
+ * an Irwin-Hall(12) approximation of N(0,1), exact in binary32.            */
+
+#define OR_GAMMA 0x9E3779B97F4A7C15ull
+
+static uint64_t or_mix64(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+uint64_t or_splitmix64_next(uint64_t* state) {
+  *state += OR_GAMMA;
+  return or_mix64(*state);
+}
+
+uint64_t or_stream_state(uint64_t seed, uint64_t stream) {
+  return or_mix64(seed + (stream + 1ull) * OR_GAMMA);
+}
+
+float or_normal_z(uint64_t st, int64_t logical_index) {
+  int64_t sum = 0;
+  int c, h;
+  for (c = 0; c < 3; ++c) {
+    uint64_t w = or_mix64(st + ((uint64_t)logical_index * 3ull + (uint64_t)c + 1ull) * OR_GAMMA);
+    for (h = 0; h < 4; ++h) sum += (int64_t)((w >> (16 * h)) & 0xFFFFull);
+  }
+  return (float)(sum - 393210) / 65536.0f;
+}
+
+void or_gen16(uint16_t* dst, int64_t n, int32_t dtype, uint64_t seed, uint64_t stream,
+              int64_t logical_base, double sigma, double scale) {
+  uint64_t st = or_stream_state(seed, stream);
+  float sf = (float)sigma, kf = (float)scale;
+  int64_t i;
+  for (i = 0; i < n; ++i) {
+    float x = or_normal_z(st, logical_base + i) * sf;
+    x = x * kf;
+    dst[i] = narrow(dtype, x);
+  }
+}
+
+void or_gen32(float* dst, int64_t n, uint64_t seed, uint64_t stream, int64_t logical_base,
+              double sigma) {
+  uint64_t st = or_stream_state(seed, stream);
+  float sf = (float)sigma;
+  int64_t i;
+  for (i = 0; i < n; ++i) dst[i] = or_normal_z(st, logical_base + i) * sf;
+}
+
+/* Gradient stream of (step, replica); steps count from 1. */
+static uint64_t grad_stream(int64_t step, int64_t replica) {
+  return ((uint64_t)step << 20) | (uint64_t)replica;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Layout.  [L13] 5.2: the tensors of a unit are flattened end to end into
+ * one 1-D FlatParameter, right-padded with zeros to a multiple of the shard
+ * count and split into equal shards; shard d belongs to rank d, so the pad
+ * (at most N-1 elements) sits in the last shard.  [L13] 0.4 builds one such
+ * unit per Linear layer (W then b).  [F6]: ZeRO-1/2 may instead treat all
+ * parameters as one giant 1-D vector (the global-flat layout).            */
+
+int or_layout(const int64_t* seg_numel, const int32_t* seg_unit, int64_t nseg, int32_t n_ranks,
+              int32_t layout, or_unit* units_out, int64_t max_units, int64_t* n_units_out,
+              int64_t* psi_out, int64_t* psi_pad_out) {
+  int64_t s, nu = 0, O = 0, lam = 0, M = 0;
+  int32_t cur = -1;
+  if (n_ranks < 1 || nseg < 1 || !seg_numel || !units_out) return -1;
+  if (layout != OR_GLOBAL_FLAT && layout != OR_PER_UNIT) return -1;
+  if (layout == OR_PER_UNIT && !seg_unit) return -1;
+  for (s = 0; s < nseg; ++s) {
+    int32_t uid = (layout == OR_GLOBAL_FLAT) ? 0 : seg_unit[s];
+    if (seg_numel[s] < 1) return -1;
+    if (uid != cur) {
+      if (uid != cur + 1) return -1;  /* unit ids must run 0,0,..,1,1,..,2 */
+      if (nu >= max_units) return -1;
+      units_out[nu].L = 0;
+      units_out[nu].lam = lam;
+      nu += 1;
+      cur = uid;
+    }
+    units_out[nu - 1].L += seg_numel[s];
+    lam += seg_numel[s];
+  }
+  for (s = 0; s < nu; ++s) {
+    or_unit* u = &units_out[s];
+    u->P = ((u->L + n_ranks - 1) / n_ranks) * n_ranks;
+    u->S = u->P / n_ranks;
+    u->O = O;
+    u->M = M;
+    O += u->P;
+    M += u->S;
+  }
+  *n_units_out = nu;
+  *psi_out = lam;
+  *psi_pad_out = O;
+  return 0;
+}
+
+/* Bytes of model state one rank holds once backward has finished ([L13] 2.3
+ * and 3.5, and its summary): stage 0 (plain DP) 2+2+12 bytes per parameter;
+ * stage 1 full 16-bit params and grads plus its 1/N of the fp32
+ * master/m/v; stage 2 also keeps only its 1/N of the grads; stage 3 keeps
+ * only its 1/N of everything.  With padding, the sharded stages count the
+ * padded Psi' ([L13] 3.6).  The stage-3 peak follows exercise 5 of the
+ * notes: while backward runs unit b (units run last to first), a rank holds
+ * its resident shards, the already reduce-scattered grad shards of units
+ * after b, and the full 16-bit params and full grads of unit b.  For stages
+ * 0-2 the peak reported is the after-backward figure (the transient fp32
+ * gradient of one unit at update time is not modelled).                 */
+int or_ledger(const or_unit* units, int64_t n_units, int32_t n_ranks, int32_t stage,
+              int64_t* after_backward_bytes, int64_t* peak_bytes) {
+  int64_t psi = 0, psi_pad = 0, s_tot = 0, u, b;
+  if (!units || n_units < 1 || n_ranks < 1 || stage < 0 || stage > 3) return -1;
+  for (u = 0; u < n_units; ++u) {
+    psi += units[u].L;
+    psi_pad += units[u].P;
+    s_tot += units[u].S;
+  }
+  switch (stage) {
+    case 0: *after_backward_bytes = 2 * psi + 2 * psi + 12 * psi; break;
+    case 1: *after_backward_bytes = 2 * psi_pad + 2 * psi_pad + 12 * s_tot; break;
+    case 2: *after_backward_bytes = 2 * psi_pad + 2 * s_tot + 12 * s_tot; break;
+    default: *after_backward_bytes = 2 * s_tot + 2 * s_tot + 12 * s_tot; break;
+  }
+  *peak_bytes = *after_backward_bytes;
+  if (stage == 3) {
+    int64_t best = 0;
+    for (b = n_units - 1; b >= 0; --b) {
+      int64_t reduced = 0, here;
+      for (u = b + 1; u < n_units; ++u) reduced += units[u].S;
+      here = 2 * s_tot + 12 * s_tot + 2 * reduced + 2 * units[b].P + 2 * units[b].P;
+      if (here > best) best = here;
+    }
+    *peak_bytes = best;
+  }
+  return 0;
+}
+
+/* Bytes one rank sends per step with ring collectives ([L13] 4.1-4.2): a
+ * ring reduce-scatter or all-gather of 2*Psi' bytes sends (N-1)/N of it.
+ * variant 0: DP all-reduce (RS + AG); 1, 2: stage 1/2 (RS of grads + AG of
+ * params); 3: stage 3 (AG in forward, AG in backward, RS); 4: the slides'
+ * stage 1 (all-reduce of grads, then AG of params).                      */
+double or_comm_bytes(int64_t psi_pad, int32_t n_ranks, int32_t variant) {
+  double passes;
+  switch (variant) {
+    case 0: case 1: case 2: passes = 2.0; break;
+    case 3: case 4: passes = 3.0; break;
+    default: return -1.0;
+  }
+  return passes * ((double)(n_ranks - 1) / (double)n_ranks) * 2.0 * (double)psi_pad;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Reduce-scatter ([L13] 3.1 step 3 and 3.2; [F7] ZeRO-2 hook): rank r
+ * receives the element-wise reduction of all N replicas over its own shard of
+ * every unit.  Reading taken: the sum is done in binary32, in the fixed rank
+ * order 0..N-1 starting from replica 0 widened to binary32; the 1/N of the
+ * average is folded into the gradient scale (see or_finish).  A ring would
+ * accumulate in a rotating order ([L13] 3.4 condition 2); this is the fixed
+ * order.  Output: rs_out[r] has the rank's shard buffer layout (unit-major,
+ * unit u at offset M_u, S_u elements, pad included).                      */
+int or_reduce_scatter(int32_t grad_dtype, int32_t n_ranks, const or_unit* units, int64_t n_units,
+                      const uint16_t* const* grads, float* const* rs_out) {
+  int64_t u, j;
+  int32_t r, q;
+  if (!units || !grads || !rs_out || n_ranks < 1) return -1;
+  for (r = 0; r < n_ranks; ++r) {
+    for (u = 0; u < n_units; ++u) {
+      const or_unit* U = &units[u];
+      for (j = 0; j < U->S; ++j) {
+        int64_t p = U->O + (int64_t)r * U->S + j;
+        float acc = widen(grad_dtype, grads[0][p]);
+        for (q = 1; q < n_ranks; ++q) acc = acc + widen(grad_dtype, grads[q][p]);
+        rs_out[r][U->M + j] = acc;
+      }
+    }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Scalars of one step, from the global squared norm and overflow flag.
+ *  - [MDT] 四.3: the optimizer first checks for fp16 overflow, then clips,
+ *    then steps.  Reading: any non-finite reduced gradient skips the step;
+ *    with dynamic loss scaling the scale halves and the growth counter
+ *    resets; m, v, the master, t and the 16-bit params are left untouched.
+ *    Otherwise t advances, and after K consecutive applied steps the scale
+ *    doubles.
+ *  - Global L2 clipping on the fp32 gradient ([MDT] 五.7; Femtotron dev log
+ *    #4 and #5).  Reading: the norm is of the unscaled, averaged gradient,
+ *    norm = sqrt(sumsq) / (S*N) in double, and the coefficient is
+ *    min(1, max_norm / (norm + 1e-6)); max_norm <= 0 disables clipping.
+ *  - Unscale, average and clip are one binary32 factor gs = f32(coef/(S*N)).
+ *  - Adam's bias corrections ([L13] 2.1) use beta^t formed by t-1 successive
+ *    double multiplications; every scalar is rounded to binary32 once.    */
+int or_finish(double sumsq, int32_t overflow, int32_t n_ranks, const or_hparams* hp,
+              or_scale_state* st, or_scalars* sc, or_result* res) {
+  double S, norm, coef, B1, B2;
+  int64_t i;
+  if (!hp || !st || !sc || !res || n_ranks < 1) return -1;
+  memset(res, 0, sizeof(*res));
+  memset(sc, 0, sizeof(*sc));
+  res->overflow = overflow ? 1 : 0;
+  res->sumsq = sumsq;
+  res->scale_used = st->loss_scale;
+  if (overflow) {
+    res->skipped = 1;
+    if (st->dynamic) {
+      st->loss_scale = st->loss_scale * 0.5;
+      st->growth_ctr = 0;
+    }
+    res->scale_next = st->loss_scale;
+    res->t = st->t;
+    return 0;
+  }
+  S = st->loss_scale;
+  st->t += 1;
+  st->growth_ctr += 1;
+  if (st->dynamic && st->growth_interval > 0 && st->growth_ctr >= st->growth_interval) {
+    st->loss_scale = S * 2.0;
+    st->growth_ctr = 0;
+  }
+  norm = sqrt(sumsq) / (S * (double)n_ranks);
+  coef = 1.0;
+  if (hp->max_norm > 0.0) {
+    coef = hp->max_norm / (norm + 1e-6);
+    if (coef > 1.0) coef = 1.0;
+  }
+  B1 = hp->beta1;
+  B2 = hp->beta2;
+  for (i = 1; i < st->t; ++i) {
+    B1 = B1 * hp->beta1;
+    B2 = B2 * hp->beta2;
+  }
+  sc->gs = (float)(coef / (S * (double)n_ranks));
+  sc->dec = (float)(1.0 - hp->lr * hp->weight_decay);
+  sc->b1 = (float)hp->beta1;
+  sc->c1 = (float)(1.0 - hp->beta1);
+  sc->b2 = (float)hp->beta2;
+  sc->c2 = (float)(1.0 - hp->beta2);
+  sc->bc1 = (float)(1.0 - B1);
+  sc->bc2 = (float)(1.0 - B2);
+  sc->lrf = (float)hp->lr;
+  sc->ef = (float)hp->eps;
+  res->norm = norm;
+  res->coef = coef;
+  res->gs = sc->gs;
+  res->scale_next = st->loss_scale;
+  res->t = st->t;
+  return 0;
+}
+
+/* AdamW on fp32 master/m/v, element by element ([L13] 2.1 for Adam, 2.2 for
+ * the fp32 master; 3.1: Adam is element-wise, so a shard updates exactly as
+ * the same elements of the whole array would).  Reading: decoupled weight
+ * decay applied to the parameter first, then Adam with epsilon outside the
+ * square root and bias corrections 1 - beta^t:
+ *     g = acc*gs;  p = p*dec;  m = b1*m + c1*g;  v = b2*v + c2*(g*g);
+ *     d = sqrt(v/bc2) + eps;   p = p - lr*((m/bc1)/d)                      */
+void or_adamw_array(int64_t n, const float* acc, const or_scalars* sc, float* p, float* m,
+                    float* v) {
+  int64_t i;
+  for (i = 0; i < n; ++i) {
+    float g = acc[i] * sc->gs;
+    float pp = p[i] * sc->dec;
+    float mm = sc->b1 * m[i] + sc->c1 * g;
+    float vv = sc->b2 * v[i] + sc->c2 * (g * g);
+    float d = sqrtf(vv / sc->bc2) + sc->ef;
+    float mh = mm / sc->bc1;
+    pp = pp - sc->lrf * (mh / d);
+    p[i] = pp;
+    m[i] = mm;
+    v[i] = vv;
+  }
+}
+
+/* One emulated ZeRO step for all N ranks ([L13] 3.1 steps 3-6, 3.2, 3.3;
+ * [MDT] 四.3 step order).
+ *   1. reduce-scatter: each rank gets the fixed-order sum over its shard;
+ *   2. overflow: any non-finite reduced value, padding included;
+ *   3. squared norm: sum of (double)acc^2 over the real elements in logical
+ *      order (unit by unit, ranks in order), so the value does not depend on
+ *      the layout; the padding is zero by contract and would add nothing;
+ *   4-6. scalars (or_finish); a skipped step stops here;
+ *   7. each rank runs AdamW on its shard (padding included: zero stays zero);
+ *   8. each rank casts its shard to 16 bits; stages 0-2 place it in the full
+ *      padded buffer (the post-update all-gather, [L13] 3.1 step 6), stage 3
+ *      keeps it as the rank's resident shard ([L13] exercise 4).
+ * master/exp_avg/exp_avg_sq/param_shards[r] are rank r's shard buffers:
+ * sum_u S_u elements, unit u at offset M_u.                               */
+int or_zero_step(int32_t grad_dtype, int32_t param_dtype, int32_t n_ranks, const or_unit* units,
+                 int64_t n_units, int32_t stage, const uint16_t* const* grads,
+                 float* const* master, float* const* exp_avg, float* const* exp_avg_sq,
+                 uint16_t* params_full, uint16_t* const* param_shards, const or_hparams* hp,
+                 or_scale_state* st, or_result* res) {
+  int64_t s_tot = 0, u, j, k;
+  int32_t r, overflow = 0;
+  double ss = 0.0;
+  float** acc;
+  or_scalars sc;
+  int rc = 0;
+  if (!units || n_units < 1 || !grads || !master || !exp_avg || !exp_avg_sq || !hp || !st || !res)
+    return -1;
+  if (stage < 3 && !params_full) return -1;
+  if (stage == 3 && !param_shards) return -1;
+  for (u = 0; u < n_units; ++u) s_tot += units[u].S;
+  acc = (float**)calloc((size_t)n_ranks, sizeof(float*));
+  if (!acc) return -2;
+  for (r = 0; r < n_ranks; ++r) {
+    acc[r] = (float*)malloc((size_t)(s_tot > 0 ? s_tot : 1) * sizeof(float));
+    if (!acc[r]) { rc = -2; goto done; }
+  }
+  or_reduce_scatter(grad_dtype, n_ranks, units, n_units, grads, acc);
+
+  for (r = 0; r < n_ranks; ++r)
+    for (k = 0; k < s_tot; ++k)
+      if (!isfinite(acc[r][k])) overflow = 1;
+
+  for (u = 0; u < n_units; ++u) {
+    const or_unit* U = &units[u];
+    for (r = 0; r < n_ranks; ++r)
+      for (j = 0; j < U->S; ++j) {
+        if ((int64_t)r * U->S + j >= U->L) continue;  /* padding */
+        ss += (double)acc[r][U->M + j] * (double)acc[r][U->M + j];
+      }
+  }
+
+  or_finish(ss, overflow, n_ranks, hp, st, &sc, res);
+  if (res->skipped) goto done;
+
+  for (r = 0; r < n_ranks; ++r)
+    or_adamw_array(s_tot, acc[r], &sc, master[r], exp_avg[r], exp_avg_sq[r]);
+
+  for (r = 0; r < n_ranks; ++r) {
+    for (u = 0; u < n_units; ++u) {
+      const or_unit* U = &units[u];
+      for (j = 0; j < U->S; ++j) {
+        uint16_t q = narrow(param_dtype, master[r][U->M + j]);
+        if (stage < 3)
+          params_full[U->O + (int64_t)r * U->S + j] = q;
+        else
+          param_shards[r][U->M + j] = q;
+      }
+    }
+  }
+done:
+  for (r = 0; r < n_ranks; ++r) free(acc[r]);
+  free(acc);
+  return rc;
+}
+
+/* ZeRO-3 / FSDP gather of one unit before it is used ([L13] 3.3 and 5.1
+ * step 3; [F9] unshard): the N ranks' shards of unit u, in rank order, form
+ * the unit's padded FlatParameter: unit_buf[r*S_u + j] = shard_r[u][j].    */
+int or_gather_unit(const or_unit* units, int64_t n_units, int32_t n_ranks, int64_t u,
+                   const uint16_t* const* param_shards, uint16_t* unit_buf) {
+  int64_t j;
+  int32_t r;
+  if (!units || u < 0 || u >= n_units || !param_shards || !unit_buf) return -1;
+  for (r = 0; r < n_ranks; ++r)
+    for (j = 0; j < units[u].S; ++j)
+      unit_buf[(int64_t)r * units[u].S + j] = param_shards[r][units[u].M + j];
+  return 0;
+}
+
+/* Plain data-parallel reference on one unpadded buffer of Psi elements: the
+ * same N replicas are summed in the same rank order, and the whole array is
+ * updated at once.  ZeRO-1/2 must reproduce it bit for bit ([L13] 3.4: the
+ * same summation order and an element-wise Adam make the results identical).
+ * grads[q] is replica q's unpadded gradient, logical order.               */
+int or_dp_step(int32_t grad_dtype, int32_t param_dtype, int32_t n_ranks, int64_t psi,
+               const uint16_t* const* grads, float* master, float* exp_avg, float* exp_avg_sq,
+               uint16_t* params, const or_hparams* hp, or_scale_state* st, or_result* res) {
+  float* acc;
+  int64_t i;
+  int32_t q, overflow = 0;
+  double ss = 0.0;
+  or_scalars sc;
+  if (!grads || !master || !exp_avg || !exp_avg_sq || !params || !hp || !st || !res) return -1;
+  acc = (float*)malloc((size_t)(psi > 0 ? psi : 1) * sizeof(float));
+  if (!acc) return -2;
+  for (i = 0; i < psi; ++i) {
+    float a = widen(grad_dtype, grads[0][i]);
+    for (q = 1; q < n_ranks; ++q) a = a + widen(grad_dtype, grads[q][i]);
+    acc[i] = a;
+    if (!isfinite(a)) overflow = 1;
+    ss += (double)a * (double)a;
+  }
+  or_finish(ss, overflow, n_ranks, hp, st, &sc, res);
+  if (!res->skipped) {
+    or_adamw_array(psi, acc, &sc, master, exp_avg, exp_avg_sq);
+    for (i = 0; i < psi; ++i) params[i] = narrow(param_dtype, master[i]);
+  }
+  free(acc);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Full-size checks by regeneration: the reduced gradient of a logical index
+ * is recomputed from the seeded generator, so a sample of elements (and the
+ * exact global squared norm, range by range) can be checked at any model
+ * size without holding the replicas in host memory.  An optional injection
+ * overrides one (step, replica, index) with given 16-bit bits.           */
+
+static float regen_acc_one(int32_t dtype, int32_t n_ranks, uint64_t seed, int64_t step,
+                           float sf, float kf, int64_t i, const or_inject* inj) {
+  float acc = 0.0f;
+  int32_t q;
+  for (q = 0; q < n_ranks; ++q) {
+    uint16_t h;
+    if (inj && inj->step == step && inj->replica == q && inj->index == i) {
+      h = inj->bits;
+    } else {
+      uint64_t st = or_stream_state(seed, grad_stream(step, q));
+      float x = or_normal_z(st, i) * sf;
+      x = x * kf;
+      h = narrow(dtype, x);
+    }
+    acc = (q == 0) ? widen(dtype, h) : acc + widen(dtype, h);
+  }
+  return acc;
+}
+
+int or_regen_sumsq(int32_t grad_dtype, int32_t n_ranks, uint64_t seed, int64_t step, double sigma,
+                   double scale, int64_t i0, int64_t i1, const or_inject* inj, double* sumsq,
+                   int32_t* nonfinite) {
+  int64_t i;
+  double ss = 0.0;
+  int32_t nf = 0;
+  float sf = (float)sigma, kf = (float)scale;
+  if (!sumsq || !nonfinite || n_ranks < 1 || i1 < i0) return -1;
+  for (i = i0; i < i1; ++i) {
+    float a = regen_acc_one(grad_dtype, n_ranks, seed, step, sf, kf, i, inj);
+    if (!isfinite(a)) nf = 1;
+    ss += (double)a * (double)a;
+  }
+  *sumsq = ss;
+  *nonfinite = nf;
+  return 0;
+}
+
+int or_regen_acc(int32_t grad_dtype, int32_t n_ranks, uint64_t seed, int64_t step, double sigma,
+                 double scale, int64_t n, const int64_t* logical_idx, const or_inject* inj,
+                 float* acc_out) {
+  int64_t k;
+  float sf = (float)sigma, kf = (float)scale;
+  if (!logical_idx || !acc_out || n_ranks < 1) return -1;
+  for (k = 0; k < n; ++k)
+    acc_out[k] = regen_acc_one(grad_dtype, n_ranks, seed, step, sf, kf, logical_idx[k], inj);
+  return 0;
+}
