@@ -1,0 +1,195 @@
+#!/usr/bin/env python
+"""Throughput of the sharded mixed-precision AdamW step on one MI355X.
+
+A step is one zf_shard_step over one batch of N resident replica gradients
+(reduce-scatter sums, overflow/norm/clip, fused AdamW + cast + gather), plus
+the per-unit gathers for a ZeRO-3 workload.  Inputs are seeded synthetic
+data generated on the device before the timed region; every step reuses the
+same batch (the state evolves).
+
+Prints one JSON line:
+  value        algorithmic GB/s = (2N + 26) B per parameter (+ 4 for the
+               ZeRO-3 unit gathers) x Psi / step time
+  roofline     the dominant kernel (the fused update pass): its algorithmic
+               bytes per launch / its mean duration from HIP events recorded
+               around it on its stream, against 8 TB/s
+  cpu_baseline the single-threaded CPU oracle on a bounded slice of the
+               same workload (rank 0, one GPU only)
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, vendor figure
+DEFAULT_WORKLOAD = "llama-73m-n8"
+
+
+def algorithmic_bytes_per_param(w):
+    """Bytes the method itself moves per real parameter per applied step:
+    read N 16-bit replicas, read and write fp32 master/m/v, write the 16-bit
+    param; ZeRO-3 adds the unit gather (read 2 + write 2)."""
+    b = 2 * w.n_ranks + 12 + 12 + 2
+    if w.stage == 3:
+        b += 4
+    return b
+
+
+def update_kernel_bytes_per_elem(w, materialized):
+    """The fused update pass per (padded) element: the reduced gradient (fp32
+    sums, or the N replicas again), fp32 master/m/v in and out, 16-bit out."""
+    return (4 if materialized else 2 * w.n_ranks) + 12 + 12 + 2
+
+
+def traffic_factor():
+    """HBM traffic from rocprofv3 counters, if a summary has been committed:
+    profiles/<workload>_traffic.json holds per-launch FETCH/WRITE bytes of the
+    update kernel, already scaled by the copy-kernel calibration."""
+    return None
+
+
+def cpu_baseline(w, min_seconds=10.0, max_steps=40):
+    """The CPU oracle as it stands, single thread, on a slice of the workload:
+    its first segments up to ~19M parameters (for the Llama workloads: the
+    embedding and the first two decoder layers), same N, dtypes and
+    hyperparameters, one resident batch, steps until min_seconds."""
+    import numpy as np  # noqa: F401
+    import oracle as O
+    from fsdp_sharded_mixed_amd import workloads as W
+    from tests import oracle_inputs as OI
+
+    segs, tot = [], 0
+    for s in w.segments:
+        segs.append(s)
+        tot += s.numel
+        if tot >= 18_000_000:
+            break
+    ws = W.Workload(**{**w.__dict__, "segments": segs})
+    units, psi, psi_pad = OI.plan(ws)
+    run = OI.OracleRun(ws, units, psi, psi_pad)
+    grads = OI.replicas(ws, units, psi_pad, 1, ws.loss_scale)
+    steps, t0 = 0, time.perf_counter()
+    while steps < max_steps and (time.perf_counter() - t0) < min_seconds:
+        O.zero_step(ws.grad_dtype, ws.param_dtype, ws.n_ranks, units, ws.stage, grads,
+                    run.master, run.m, run.v, run.full, run.shards, run.hp, run.st)
+        steps += 1
+    dt = time.perf_counter() - t0
+    gbs = algorithmic_bytes_per_param(ws) * psi * steps / dt / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "params_per_s": round(psi * steps / dt, 1),
+            "sample": f"first {len(segs)} parameter tensors ({psi:,} params) of {w.name}, "
+                      f"N={ws.n_ranks}, {steps} steps over one batch, {dt:.1f} s, "
+                      f"single-threaded C oracle"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(N data-parallel ranks are emulated on a single device)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from fsdp_sharded_mixed_amd import runner, workloads as W
+
+    w = W.get(args.workload)
+    torch.cuda.set_device(0)
+    print(f"bench: {w.name} Psi={w.psi:,} N={w.n_ranks} stage={w.stage}", file=sys.stderr,
+          flush=True)
+    dev = runner.DeviceRun(w, device="cuda:0")
+    dev.init_state()
+    dev.fill_grads(1, w.loss_scale)
+    torch.cuda.synchronize()
+    n_units = len(dev.plan.units)
+
+    def one_step(phase_events=None):
+        dev.step(phase_events=phase_events)
+        if w.stage == 3:
+            for u in range(n_units):
+                dev.gather(u)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    res = dev.result()
+    assert res.skipped == 0, "warm-up step skipped"
+
+    # timed region: exactly K steps
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        one_step()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end) / args.steps
+    res = dev.result()
+    assert res.skipped == 0
+
+    # per-kernel durations: a second run of K steps with HIP events recorded
+    # by the library between its kernels, on the step's stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for row in evs:
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+    for row in evs:
+        one_step(phase_events=[e.cuda_event for e in row])
+    torch.cuda.synchronize()
+    p1 = sum(r[0].elapsed_time(r[1]) for r in evs) / args.steps
+    fin = sum(r[1].elapsed_time(r[2]) for r in evs) / args.steps
+    p2 = sum(r[2].elapsed_time(r[3]) for r in evs) / args.steps
+
+    s = dev.plan.summary
+    materialized = s.policy == 1
+    alg = algorithmic_bytes_per_param(w) * w.psi
+    gbs = alg / (ms * 1e-3) / 1e9
+    upd_bytes = update_kernel_bytes_per_elem(w, materialized) * s.psi_pad
+    upd_gbs = upd_bytes / (p2 * 1e-3) / 1e9
+    line = {
+        "metric": "ZeRO step GB/s (algorithmic bytes) and % of HBM peak; params updated/s",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 state, " + ("bf16" if w.grad_dtype == W.BF16 else "f16") + " grads",
+        "data": "synthetic (seeded splitmix64/Irwin-Hall normal grads and master init, "
+                "random-init weights)",
+        "config": {"workload": w.name, "psi": w.psi, "psi_padded": s.psi_pad,
+                   "virtual_ranks": w.n_ranks, "zero_stage": w.stage,
+                   "layout": "global flat" if w.layout == W.GLOBAL_FLAT else "per-unit",
+                   "rs_policy": "materialize" if materialized else "recompute"},
+        "params_updated_per_s": round(w.psi / (ms * 1e-3), 1),
+        "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+        "wall_ms_per_step": round(1e3 * wall / args.steps, 5),
+        "kernels_ms": {"pass1_rs_norm": round(p1, 5), "finish": round(fin, 5),
+                       "pass2_update": round(p2, 5)},
+        "roofline": {"bound": "hbm", "achieved": round(upd_gbs, 2), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(upd_gbs / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_factor(), "kernel": "zf_pass2 (fused AdamW+cast+gather)",
+                     "bytes_per_launch": upd_bytes},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

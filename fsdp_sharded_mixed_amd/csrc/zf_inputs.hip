@@ -1,0 +1,95 @@
+// zf_inputs.hip -- seeded synthetic inputs (splitmix64 + Irwin-Hall(12)).
+// The definition is stated in zf_inputs.h.  Input generation only: nothing
+// here belongs to the step.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "zf_inputs.h"
+
+namespace {
+
+constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ull;
+
+__host__ __device__ __forceinline__ uint64_t mix64(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+__host__ __device__ __forceinline__ uint64_t stream_state(uint64_t seed, uint64_t stream) {
+  return mix64(seed + (stream + 1ull) * kGamma);
+}
+
+__device__ __forceinline__ float irwin_hall(uint64_t st, int64_t i) {
+  const uint64_t base = st + (uint64_t)i * 3ull * kGamma;
+  uint32_t sum = 0;
+#pragma unroll
+  for (int c = 1; c <= 3; ++c) {
+    const uint64_t w = mix64(base + (uint64_t)c * kGamma);
+    sum += (uint32_t)(w & 0xFFFFu) + (uint32_t)((w >> 16) & 0xFFFFu) +
+           (uint32_t)((w >> 32) & 0xFFFFu) + (uint32_t)(w >> 48);
+  }
+  // |sum - 393210| < 2^24: the conversion and the power-of-two scaling are exact
+  return (float)((int32_t)sum - 393210) * (1.0f / 65536.0f);
+}
+
+template <int DT>
+__global__ void fill16(uint16_t* dst, int64_t n, uint64_t st, int64_t base, float sf, float kf) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < n; k += stride) {
+    float x = irwin_hall(st, base + k) * sf;
+    x = x * kf;
+    if constexpr (DT == 2) dst[k] = __builtin_bit_cast(uint16_t, (__bf16)x);
+    else dst[k] = __builtin_bit_cast(uint16_t, (_Float16)x);
+  }
+}
+
+__global__ void fill32(float* dst, int64_t n, uint64_t st, int64_t base, float sf) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < n; k += stride)
+    dst[k] = irwin_hall(st, base + k) * sf;
+}
+
+dim3 grid_for(int64_t n) {
+  int64_t b = (n + 255) / 256;
+  if (b < 1) b = 1;
+  if (b > 16384) b = 16384;
+  return dim3((uint32_t)b);
+}
+
+}  // namespace
+
+extern "C" int zfi_fill_normal16(void* dst, int64_t n, int32_t dtype, uint64_t seed,
+                                 uint64_t stream, int64_t logical_base, double sigma,
+                                 double scale, void* stream_handle) {
+  if (!dst || n < 0 || logical_base < 0 || (dtype != 1 && dtype != 2)) return -1;
+  if ((reinterpret_cast<uintptr_t>(dst) & 1u) != 0) return -1;
+  if (n == 0) return 0;
+  const uint64_t st = stream_state(seed, stream);
+  hipStream_t s = static_cast<hipStream_t>(stream_handle);
+  (void)hipGetLastError();
+  if (dtype == 2)
+    hipLaunchKernelGGL(fill16<2>, grid_for(n), dim3(256), 0, s, static_cast<uint16_t*>(dst), n,
+                       st, logical_base, (float)sigma, (float)scale);
+  else
+    hipLaunchKernelGGL(fill16<1>, grid_for(n), dim3(256), 0, s, static_cast<uint16_t*>(dst), n,
+                       st, logical_base, (float)sigma, (float)scale);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+extern "C" int zfi_fill_normal32(float* dst, int64_t n, uint64_t seed, uint64_t stream,
+                                 int64_t logical_base, double sigma, void* stream_handle) {
+  if (!dst || n < 0 || logical_base < 0) return -1;
+  if ((reinterpret_cast<uintptr_t>(dst) & 3u) != 0) return -1;
+  if (n == 0) return 0;
+  const uint64_t st = stream_state(seed, stream);
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(fill32, grid_for(n), dim3(256), 0, static_cast<hipStream_t>(stream_handle),
+                     dst, n, st, logical_base, (float)sigma);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+extern "C" uint64_t zfi_stream_output(uint64_t seed, uint64_t stream, uint64_t j) {
+  return mix64(stream_state(seed, stream) + (j + 1ull) * kGamma);
+}

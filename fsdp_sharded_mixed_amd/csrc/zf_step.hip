@@ -1,0 +1,680 @@
+// zf_step.hip -- gfx950 kernels and C entry points of the sharded AdamW step.
+//
+// The step is a stream over the padded flat index p with under one flop per
+// byte, so it is bound by HBM bandwidth and uses no matrix cores.  Every
+// kernel reads and writes 16 bytes per lane per access (eight 16-bit values
+// or four fp32 values), wave64-coalesced, from 16-byte aligned bases.
+//
+// Pages followed (by title and section):
+//   CMU 15-779 Lecture 13 notes, "Zero Redundancy and PyTorch FSDP": 2.1
+//   (Adam), 2.2 (update in fp32 master weights, then cast down), 3.1-3.3 (the
+//   stages: reduce-scatter, update of the own shard, all-gather of 16-bit
+//   params, or per-unit gather under stage 3), 3.4 (same summation order =>
+//   same bits), 5.2 (FlatParameter padding).
+//   Megatron / DeepSpeed / torchtitan architecture and source guide, ch. 四.3
+//   (check fp16 overflow, clip, Adam per fp32 partition, copy to the 16-bit
+//   partition) and 五.7 (clipping by the global gradient norm).
+//
+// Arithmetic contract (shared with nothing; checked against the CPU oracle):
+//   acc  = f32(g_0) + f32(g_1) + ... + f32(g_{N-1})          in rank order
+//   skip = any acc is inf or NaN (padding included)
+//   ss   = sum of (double)acc^2; norm = sqrt(ss)/(S*N); coef = min(1,
+//          max_norm/(norm+1e-6)); gs = f32(coef/(S*N))
+//   g = acc*gs; p = p*dec; m = b1*m + c1*g; v = b2*v + c2*(g*g);
+//   p = p - lr*((m/bc1) / (sqrt(v/bc2) + eps)); out = RNE16(p)
+// Each operator is one IEEE binary32 operation: built with
+// -ffp-contract=off and correctly rounded division and square root.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "zf_internal.h"
+
+namespace {
+
+using zf::kThreads;
+using zf::kVec;
+
+// ---------------------------------------------------------------------------
+// Device state block (the caller's zf_state_bytes() buffer).
+struct __align__(16) DevState {
+  double loss_scale;     // S for the next step
+  double beta1_pow;      // beta1^t after t applied steps (1 at t = 0)
+  double beta2_pow;
+  int64_t t;
+  int32_t growth_ctr, growth_interval, dynamic, pad0;
+  // result of the last step
+  int32_t overflow, skipped;
+  double sumsq, norm, coef, scale_used;
+  float gs, bc1, bc2, pad1;
+};
+static_assert(sizeof(DevState) <= 256, "state block");
+constexpr int64_t kStateBytes = 256;
+
+struct __align__(16) Partial {
+  double ss;
+  uint32_t bad;
+  uint32_t pad;
+};
+
+struct GradPtrs {
+  const uint16_t* p[ZF_MAX_RANKS];
+};
+
+// ---------------------------------------------------------------------------
+// 16-bit <-> binary32.  Widening is exact; narrowing uses the hardware
+// round-to-nearest-even conversions (v_cvt_pk_bf16_f32, v_cvt_f16_f32).
+
+template <int DT>
+__device__ __forceinline__ float lo16(uint32_t w) {
+  if constexpr (DT == ZF_BF16) return __uint_as_float(w << 16);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+}
+template <int DT>
+__device__ __forceinline__ float hi16(uint32_t w) {
+  if constexpr (DT == ZF_BF16) return __uint_as_float(w & 0xFFFF0000u);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+template <int DT>
+__device__ __forceinline__ float widen1(uint16_t h) {
+  return lo16<DT>((uint32_t)h);
+}
+template <int DT>
+__device__ __forceinline__ uint16_t narrow1(float x) {
+  if constexpr (DT == ZF_BF16) return __builtin_bit_cast(uint16_t, (__bf16)x);
+  else return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  return (uint32_t)narrow1<DT>(a) | ((uint32_t)narrow1<DT>(b) << 16);
+}
+
+template <int DT>
+__device__ __forceinline__ void widen8(const uint4& w, float (&x)[8]) {
+  x[0] = lo16<DT>(w.x); x[1] = hi16<DT>(w.x);
+  x[2] = lo16<DT>(w.y); x[3] = hi16<DT>(w.y);
+  x[4] = lo16<DT>(w.z); x[5] = hi16<DT>(w.z);
+  x[6] = lo16<DT>(w.w); x[7] = hi16<DT>(w.w);
+}
+
+__device__ __forceinline__ bool nonfinite(float x) {
+  return (__float_as_uint(x) & 0x7F800000u) == 0x7F800000u;
+}
+
+// Fixed-order sum of the N replicas at vector v (elements 8v .. 8v+7).
+// NR > 0: N known at compile time, all N loads issued before the adds.
+// NR == 0: N at run time, in groups of four replicas.
+template <int NR, int DT>
+__device__ __forceinline__ void sum8(const GradPtrs& g, int nr, int64_t v, float (&acc)[8]) {
+  if constexpr (NR > 0) {
+    uint4 w[NR];
+#pragma unroll
+    for (int q = 0; q < NR; ++q) w[q] = reinterpret_cast<const uint4*>(g.p[q])[v];
+    widen8<DT>(w[0], acc);
+#pragma unroll
+    for (int q = 1; q < NR; ++q) {
+      float x[8];
+      widen8<DT>(w[q], x);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] = acc[k] + x[k];
+    }
+  } else {
+    widen8<DT>(reinterpret_cast<const uint4*>(g.p[0])[v], acc);
+    int q = 1;
+    for (; q + 4 <= nr; q += 4) {
+      uint4 w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[j] = reinterpret_cast<const uint4*>(g.p[q + j])[v];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float x[8];
+        widen8<DT>(w[j], x);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[k] = acc[k] + x[k];
+      }
+    }
+    for (; q < nr; ++q) {
+      float x[8];
+      widen8<DT>(reinterpret_cast<const uint4*>(g.p[q])[v], x);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] = acc[k] + x[k];
+    }
+  }
+}
+
+// Scalar element p (the ragged tail).
+template <int DT>
+__device__ __forceinline__ float sum1(const GradPtrs& g, int nr, int64_t p) {
+  float acc = widen1<DT>(g.p[0][p]);
+  for (int q = 1; q < nr; ++q) acc = acc + widen1<DT>(g.p[q][p]);
+  return acc;
+}
+
+// Block-wide reduction of (sum, or): wave64 xor-butterfly (every lane ends
+// with the same bits: each level only swaps the operands of an addition),
+// then the four waves in order.  The result is valid in thread 0.
+__device__ __forceinline__ void block_reduce(double& ss, uint32_t& bad) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    ss = ss + __shfl_xor(ss, off, 64);
+    bad = bad | __shfl_xor(bad, off, 64);
+  }
+  __shared__ double s_ss[kThreads / 64];
+  __shared__ uint32_t s_bad[kThreads / 64];
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    s_ss[wave] = ss;
+    s_bad[wave] = bad;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t = s_ss[0];
+    uint32_t b = s_bad[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) {
+      t = t + s_ss[w];
+      b = b | s_bad[w];
+    }
+    ss = t;
+    bad = b;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pass 1: reduce-scatter sums, overflow flag and squared-norm partials.
+struct Pass1Args {
+  GradPtrs g;
+  int64_t n;          // Psi'
+  float* rs;          // fp32 sums (MAT) or unused
+  Partial* partials;  // one per block (NORM) or unused
+  int32_t nr;
+};
+
+template <int NR, int DT, bool MAT, bool NORM>
+__global__ __launch_bounds__(kThreads) void zf_pass1(Pass1Args a) {
+  const int nr = NR > 0 ? NR : a.nr;
+  const int64_t nvec = a.n / kVec;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  double ss = 0.0;
+  uint32_t bad = 0;
+  for (int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x; v < nvec; v += stride) {
+    float acc[8];
+    sum8<NR, DT>(a.g, nr, v, acc);
+    if constexpr (MAT) {
+      float4* o = reinterpret_cast<float4*>(a.rs) + 2 * v;
+      o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      o[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
+    if constexpr (NORM) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        bad |= nonfinite(acc[k]) ? 1u : 0u;
+        ss = ss + (double)acc[k] * (double)acc[k];
+      }
+    }
+  }
+  // ragged tail (< 8 elements), taken by the last block
+  const int64_t tail0 = nvec * kVec;
+  if (blockIdx.x == gridDim.x - 1 && (int64_t)threadIdx.x < a.n - tail0) {
+    const int64_t p = tail0 + threadIdx.x;
+    const float acc = sum1<DT>(a.g, nr, p);
+    if constexpr (MAT) a.rs[p] = acc;
+    if constexpr (NORM) {
+      bad |= nonfinite(acc) ? 1u : 0u;
+      ss = ss + (double)acc * (double)acc;
+    }
+  }
+  if constexpr (NORM) {
+    block_reduce(ss, bad);
+    if (threadIdx.x == 0) {
+      a.partials[blockIdx.x].ss = ss;
+      a.partials[blockIdx.x].bad = bad;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Finish: one block turns the partials into the step's scalars.
+struct FinishArgs {
+  const Partial* partials;
+  DevState* st;
+  double beta1, beta2, max_norm;
+  int32_t np, n_ranks;
+};
+
+__global__ __launch_bounds__(kThreads) void zf_finish(FinishArgs a) {
+  double ss = 0.0;
+  uint32_t bad = 0;
+  for (int i = threadIdx.x; i < a.np; i += kThreads) {
+    ss = ss + a.partials[i].ss;
+    bad = bad | a.partials[i].bad;
+  }
+  block_reduce(ss, bad);
+  if (threadIdx.x != 0) return;
+  DevState* s = a.st;
+  s->overflow = bad ? 1 : 0;
+  s->sumsq = ss;
+  s->scale_used = s->loss_scale;
+  if (bad) {
+    // overflow: skip; a dynamic loss scale halves and its counter restarts
+    s->skipped = 1;
+    if (s->dynamic) {
+      s->loss_scale = s->loss_scale * 0.5;
+      s->growth_ctr = 0;
+    }
+    s->norm = 0.0;
+    s->coef = 0.0;
+    s->gs = 0.0f;
+    return;
+  }
+  s->skipped = 0;
+  const double S = s->loss_scale;
+  s->t = s->t + 1;
+  s->growth_ctr = s->growth_ctr + 1;
+  if (s->dynamic && s->growth_interval > 0 && s->growth_ctr >= s->growth_interval) {
+    s->loss_scale = S * 2.0;
+    s->growth_ctr = 0;
+  }
+  const double sn = S * (double)a.n_ranks;
+  const double norm = sqrt(ss) / sn;
+  double coef = 1.0;
+  if (a.max_norm > 0.0) {
+    coef = a.max_norm / (norm + 1e-6);
+    if (coef > 1.0) coef = 1.0;
+  }
+  s->beta1_pow = s->beta1_pow * a.beta1;
+  s->beta2_pow = s->beta2_pow * a.beta2;
+  s->norm = norm;
+  s->coef = coef;
+  s->gs = (float)(coef / sn);
+  s->bc1 = (float)(1.0 - s->beta1_pow);
+  s->bc2 = (float)(1.0 - s->beta2_pow);
+}
+
+// ---------------------------------------------------------------------------
+// Pass 2: fused unscale/clip + AdamW + RNE cast + gathered write.
+struct Pass2Args {
+  GradPtrs g;
+  const float* rs;
+  float* master;
+  float* m;
+  float* v;
+  void* out;
+  const DevState* st;
+  int64_t n;
+  float dec, b1, c1, b2, c2, lrf, ef;
+  int32_t nr;
+};
+
+struct Coef {
+  float gs, dec, b1, c1, b2, c2, bc1, bc2, lrf, ef;
+};
+
+__device__ __forceinline__ void adamw1(const Coef& c, float acc, float& p, float& m, float& v) {
+  const float g = acc * c.gs;
+  float pp = p * c.dec;
+  const float mm = c.b1 * m + c.c1 * g;
+  const float vv = c.b2 * v + c.c2 * (g * g);
+  const float d = sqrtf(vv / c.bc2) + c.ef;
+  const float mh = mm / c.bc1;
+  pp = pp - c.lrf * (mh / d);
+  p = pp;
+  m = mm;
+  v = vv;
+}
+
+template <int NR, int GDT, int PDT, bool MAT>
+__global__ __launch_bounds__(kThreads) void zf_pass2(Pass2Args a) {
+  if (a.st->skipped) return;  // the whole grid leaves at once
+  Coef c;
+  c.gs = a.st->gs;
+  c.bc1 = a.st->bc1;
+  c.bc2 = a.st->bc2;
+  c.dec = a.dec; c.b1 = a.b1; c.c1 = a.c1; c.b2 = a.b2; c.c2 = a.c2;
+  c.lrf = a.lrf; c.ef = a.ef;
+  const int nr = NR > 0 ? NR : a.nr;
+  const int64_t nvec = a.n / kVec;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  float4* P4 = reinterpret_cast<float4*>(a.master);
+  float4* M4 = reinterpret_cast<float4*>(a.m);
+  float4* V4 = reinterpret_cast<float4*>(a.v);
+  uint4* O4 = reinterpret_cast<uint4*>(a.out);
+  for (int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x; v < nvec; v += stride) {
+    float acc[8];
+    if constexpr (MAT) {
+      const float4 r0 = reinterpret_cast<const float4*>(a.rs)[2 * v];
+      const float4 r1 = reinterpret_cast<const float4*>(a.rs)[2 * v + 1];
+      acc[0] = r0.x; acc[1] = r0.y; acc[2] = r0.z; acc[3] = r0.w;
+      acc[4] = r1.x; acc[5] = r1.y; acc[6] = r1.z; acc[7] = r1.w;
+    } else {
+      sum8<NR, GDT>(a.g, nr, v, acc);
+    }
+    const float4 p0 = P4[2 * v], p1 = P4[2 * v + 1];
+    const float4 m0 = M4[2 * v], m1 = M4[2 * v + 1];
+    const float4 v0 = V4[2 * v], v1 = V4[2 * v + 1];
+    float p[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+    float m[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+    float w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) adamw1(c, acc[k], p[k], m[k], w[k]);
+    P4[2 * v] = make_float4(p[0], p[1], p[2], p[3]);
+    P4[2 * v + 1] = make_float4(p[4], p[5], p[6], p[7]);
+    M4[2 * v] = make_float4(m[0], m[1], m[2], m[3]);
+    M4[2 * v + 1] = make_float4(m[4], m[5], m[6], m[7]);
+    V4[2 * v] = make_float4(w[0], w[1], w[2], w[3]);
+    V4[2 * v + 1] = make_float4(w[4], w[5], w[6], w[7]);
+    O4[v] = make_uint4(pack2<PDT>(p[0], p[1]), pack2<PDT>(p[2], p[3]),
+                       pack2<PDT>(p[4], p[5]), pack2<PDT>(p[6], p[7]));
+  }
+  const int64_t tail0 = nvec * kVec;
+  if (blockIdx.x == gridDim.x - 1 && (int64_t)threadIdx.x < a.n - tail0) {
+    const int64_t q = tail0 + threadIdx.x;
+    const float acc = MAT ? a.rs[q] : sum1<GDT>(a.g, nr, q);
+    float p = a.master[q], m = a.m[q], w = a.v[q];
+    adamw1(c, acc, p, m, w);
+    a.master[q] = p;
+    a.m[q] = m;
+    a.v[q] = w;
+    reinterpret_cast<uint16_t*>(a.out)[q] = narrow1<PDT>(p);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Unit gather: blockIdx.y = rank; unit_buf[r*S + j] = src_r[j].
+struct GatherArgs {
+  const uint16_t* src[ZF_MAX_RANKS];
+  uint16_t* dst;
+  int64_t S;
+};
+
+__global__ __launch_bounds__(kThreads) void zf_gather_kernel(GatherArgs a) {
+  const int r = blockIdx.y;
+  const uint16_t* s = a.src[r];
+  uint16_t* d = a.dst + (int64_t)r * a.S;
+  const int64_t S = a.S;
+  const int64_t tid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  const uintptr_t ms = reinterpret_cast<uintptr_t>(s) & 15u;
+  const uintptr_t md = reinterpret_cast<uintptr_t>(d) & 15u;
+  if (ms == md) {
+    // same misalignment: a scalar head up to the 16-byte boundary, 16-byte
+    // copies, then a scalar tail
+    int64_t head = (int64_t)(((16u - ms) & 15u) >> 1);
+    if (head > S) head = S;
+    const int64_t nvec = (S - head) / 8;
+    const uint4* s4 = reinterpret_cast<const uint4*>(s + head);
+    uint4* d4 = reinterpret_cast<uint4*>(d + head);
+    for (int64_t v = tid; v < nvec; v += stride) d4[v] = s4[v];
+    const int64_t tail0 = head + nvec * 8;
+    if (tid < head) d[tid] = s[tid];
+    if (tid < S - tail0) d[tail0 + tid] = s[tail0 + tid];
+  } else {
+    for (int64_t j = tid; j < S; j += stride) d[j] = s[j];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// State initialisation.
+__global__ void zf_state_init_kernel(DevState* s, double S, int32_t dynamic, int32_t growth) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  s->loss_scale = S;
+  s->beta1_pow = 1.0;
+  s->beta2_pow = 1.0;
+  s->t = 0;
+  s->growth_ctr = 0;
+  s->growth_interval = growth;
+  s->dynamic = dynamic ? 1 : 0;
+  s->pad0 = 0;
+  s->overflow = 0;
+  s->skipped = 0;
+  s->sumsq = 0.0;
+  s->norm = 0.0;
+  s->coef = 0.0;
+  s->scale_used = S;
+  s->gs = 0.0f;
+  s->bc1 = 0.0f;
+  s->bc2 = 0.0f;
+  s->pad1 = 0.0f;
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool valid_dtype(int32_t d) { return d == ZF_F16 || d == ZF_BF16; }
+bool valid_plan(const zf_plan* p) { return p && p->magic == zf::kPlanMagic; }
+
+int grads_ok(const zf_plan* plan, const void* const* grads, GradPtrs& out) {
+  if (!grads) return ZF_EINVAL;
+  for (int q = 0; q < plan->summary.n_ranks; ++q) {
+    if (!grads[q]) return ZF_EINVAL;
+    if (!aligned16(grads[q])) return ZF_EALIGN;
+    out.p[q] = static_cast<const uint16_t*>(grads[q]);
+  }
+  for (int q = plan->summary.n_ranks; q < ZF_MAX_RANKS; ++q) out.p[q] = nullptr;
+  return ZF_OK;
+}
+
+int64_t pass2_blocks(int64_t n) {
+  const int64_t nvec = n / kVec;
+  int64_t b = (nvec + kThreads - 1) / kThreads;
+  if (b < 1) b = 1;
+  if (b > 8192) b = 8192;
+  return b;
+}
+
+template <bool MAT, bool NORM>
+int launch_pass1(int nr, int32_t dt, dim3 grid, hipStream_t s, const Pass1Args& a) {
+#define ZF_P1(NRV, DTV) hipLaunchKernelGGL((zf_pass1<NRV, DTV, MAT, NORM>), grid, dim3(kThreads), 0, s, a)
+#define ZF_P1_DT(NRV) \
+  do { if (dt == ZF_BF16) ZF_P1(NRV, ZF_BF16); else ZF_P1(NRV, ZF_F16); } while (0)
+  switch (nr) {
+    case 1: ZF_P1_DT(1); break;
+    case 2: ZF_P1_DT(2); break;
+    case 3: ZF_P1_DT(3); break;
+    case 4: ZF_P1_DT(4); break;
+    case 5: ZF_P1_DT(5); break;
+    case 6: ZF_P1_DT(6); break;
+    case 7: ZF_P1_DT(7); break;
+    case 8: ZF_P1_DT(8); break;
+    default: ZF_P1_DT(0); break;
+  }
+#undef ZF_P1_DT
+#undef ZF_P1
+  return hipGetLastError() == hipSuccess ? ZF_OK : ZF_EHIP;
+}
+
+template <int GDT, int PDT>
+void launch_pass2_nr(int nr, bool mat, dim3 grid, hipStream_t s, const Pass2Args& a) {
+  if (mat) {
+    hipLaunchKernelGGL((zf_pass2<0, GDT, PDT, true>), grid, dim3(kThreads), 0, s, a);
+    return;
+  }
+#define ZF_P2(NRV) hipLaunchKernelGGL((zf_pass2<NRV, GDT, PDT, false>), grid, dim3(kThreads), 0, s, a)
+  switch (nr) {
+    case 1: ZF_P2(1); break;
+    case 2: ZF_P2(2); break;
+    case 3: ZF_P2(3); break;
+    case 4: ZF_P2(4); break;
+    case 5: ZF_P2(5); break;
+    case 6: ZF_P2(6); break;
+    case 7: ZF_P2(7); break;
+    case 8: ZF_P2(8); break;
+    default: ZF_P2(0); break;
+  }
+#undef ZF_P2
+}
+
+int launch_pass2(int nr, int32_t gdt, int32_t pdt, bool mat, dim3 grid, hipStream_t s,
+                 const Pass2Args& a) {
+  if (gdt == ZF_BF16) {
+    if (pdt == ZF_BF16) launch_pass2_nr<ZF_BF16, ZF_BF16>(nr, mat, grid, s, a);
+    else launch_pass2_nr<ZF_BF16, ZF_F16>(nr, mat, grid, s, a);
+  } else {
+    if (pdt == ZF_BF16) launch_pass2_nr<ZF_F16, ZF_BF16>(nr, mat, grid, s, a);
+    else launch_pass2_nr<ZF_F16, ZF_F16>(nr, mat, grid, s, a);
+  }
+  return hipGetLastError() == hipSuccess ? ZF_OK : ZF_EHIP;
+}
+
+int record(void* const* ev, int i, hipStream_t s) {
+  if (!ev || !ev[i]) return ZF_OK;
+  return hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) == hipSuccess ? ZF_OK : ZF_EHIP;
+}
+
+}  // namespace
+
+extern "C" int64_t zf_state_bytes(void) { return kStateBytes; }
+
+extern "C" int zf_state_init(void* d_state, double loss_scale, int32_t dynamic,
+                             int32_t growth_interval, void* stream) {
+  if (!d_state || !(loss_scale > 0.0) || loss_scale > 1e300) return ZF_EINVAL;
+  if (!aligned16(d_state)) return ZF_EALIGN;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(zf_state_init_kernel, dim3(1), dim3(64), 0,
+                     static_cast<hipStream_t>(stream), static_cast<DevState*>(d_state),
+                     loss_scale, dynamic, growth_interval);
+  return hipGetLastError() == hipSuccess ? ZF_OK : ZF_EHIP;
+}
+
+extern "C" int zf_shard_step(const zf_plan* plan, const zf_hparams* hp,
+                             const zf_step_args* args, void* stream) {
+  if (!valid_plan(plan) || !hp || !args) return ZF_EINVAL;
+  const zf_plan_summary& sm = plan->summary;
+  if (!valid_dtype(args->grad_dtype) || !valid_dtype(args->param_dtype)) return ZF_EDTYPE;
+  if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0) || !(hp->beta2 >= 0.0 && hp->beta2 < 1.0))
+    return ZF_EINVAL;
+  GradPtrs gp;
+  int rc = grads_ok(plan, args->grads, gp);
+  if (rc != ZF_OK) return rc;
+  void* const bufs[] = {args->master, args->exp_avg, args->exp_avg_sq, args->params,
+                        args->state};
+  for (void* b : bufs) {
+    if (!b) return ZF_EINVAL;
+    if (!aligned16(b)) return ZF_EALIGN;
+  }
+  if (sm.workspace_bytes > 0) {
+    if (!args->workspace) return ZF_EINVAL;
+    if (!aligned16(args->workspace)) return ZF_EALIGN;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(args->workspace);
+  Partial* partials = reinterpret_cast<Partial*>(ws + plan->ws_partials_offset);
+  const bool mat = plan->ws_rs_offset >= 0;
+  float* rs = mat ? reinterpret_cast<float*>(ws + plan->ws_rs_offset) : nullptr;
+  const int nr = sm.n_ranks;
+
+  (void)hipGetLastError();
+  if ((rc = record(args->phase_events, 0, s)) != ZF_OK) return rc;
+
+  Pass1Args a1;
+  a1.g = gp;
+  a1.n = sm.psi_pad;
+  a1.rs = rs;
+  a1.partials = partials;
+  a1.nr = nr;
+  const dim3 g1(plan->pass1_blocks);
+  rc = mat ? launch_pass1<true, true>(nr, args->grad_dtype, g1, s, a1)
+           : launch_pass1<false, true>(nr, args->grad_dtype, g1, s, a1);
+  if (rc != ZF_OK) return rc;
+  if ((rc = record(args->phase_events, 1, s)) != ZF_OK) return rc;
+
+  FinishArgs af;
+  af.partials = partials;
+  af.st = static_cast<DevState*>(args->state);
+  af.beta1 = hp->beta1;
+  af.beta2 = hp->beta2;
+  af.max_norm = hp->max_norm;
+  af.np = plan->pass1_blocks;
+  af.n_ranks = nr;
+  hipLaunchKernelGGL(zf_finish, dim3(1), dim3(kThreads), 0, s, af);
+  if (hipGetLastError() != hipSuccess) return ZF_EHIP;
+  if ((rc = record(args->phase_events, 2, s)) != ZF_OK) return rc;
+
+  // binary32 hyperparameters, each rounded once from its double value
+  Pass2Args a2;
+  a2.g = gp;
+  a2.rs = rs;
+  a2.master = args->master;
+  a2.m = args->exp_avg;
+  a2.v = args->exp_avg_sq;
+  a2.out = args->params;
+  a2.st = static_cast<const DevState*>(args->state);
+  a2.n = sm.psi_pad;
+  a2.dec = (float)(1.0 - hp->lr * hp->weight_decay);
+  a2.b1 = (float)hp->beta1;
+  a2.c1 = (float)(1.0 - hp->beta1);
+  a2.b2 = (float)hp->beta2;
+  a2.c2 = (float)(1.0 - hp->beta2);
+  a2.lrf = (float)hp->lr;
+  a2.ef = (float)hp->eps;
+  a2.nr = nr;
+  rc = launch_pass2(nr, args->grad_dtype, args->param_dtype, mat, dim3(pass2_blocks(sm.psi_pad)),
+                    s, a2);
+  if (rc != ZF_OK) return rc;
+  return record(args->phase_events, 3, s);
+}
+
+extern "C" int zf_reduce_scatter(const zf_plan* plan, int32_t grad_dtype,
+                                 const void* const* grads, float* rs_out, void* stream) {
+  if (!valid_plan(plan) || !rs_out) return ZF_EINVAL;
+  if (!valid_dtype(grad_dtype)) return ZF_EDTYPE;
+  if (!aligned16(rs_out)) return ZF_EALIGN;
+  GradPtrs gp;
+  int rc = grads_ok(plan, grads, gp);
+  if (rc != ZF_OK) return rc;
+  Pass1Args a1;
+  a1.g = gp;
+  a1.n = plan->summary.psi_pad;
+  a1.rs = rs_out;
+  a1.partials = nullptr;
+  a1.nr = plan->summary.n_ranks;
+  (void)hipGetLastError();
+  return launch_pass1<true, false>(a1.nr, grad_dtype, dim3(plan->pass1_blocks),
+                                   static_cast<hipStream_t>(stream), a1);
+}
+
+extern "C" int zf_gather(const zf_plan* plan, int64_t unit, int32_t dtype,
+                         const void* const* shards, void* unit_buf, void* stream) {
+  if (!valid_plan(plan) || !shards || !unit_buf) return ZF_EINVAL;
+  if (!valid_dtype(dtype)) return ZF_EDTYPE;
+  if (unit < 0 || unit >= plan->summary.n_units) return ZF_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(unit_buf) & 1u) != 0) return ZF_EALIGN;
+  const int nr = plan->summary.n_ranks;
+  GatherArgs a;
+  for (int r = 0; r < ZF_MAX_RANKS; ++r) a.src[r] = nullptr;
+  for (int r = 0; r < nr; ++r) {
+    if (!shards[r]) return ZF_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(shards[r]) & 1u) != 0) return ZF_EALIGN;
+    a.src[r] = static_cast<const uint16_t*>(shards[r]);
+  }
+  a.dst = static_cast<uint16_t*>(unit_buf);
+  a.S = plan->units[unit].S;
+  int64_t bx = (a.S / 8 + kThreads - 1) / kThreads;
+  if (bx < 1) bx = 1;
+  if (bx > 4096) bx = 4096;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(zf_gather_kernel, dim3((uint32_t)bx, (uint32_t)nr), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), a);
+  return hipGetLastError() == hipSuccess ? ZF_OK : ZF_EHIP;
+}
+
+extern "C" int zf_read_result(const void* d_state, zf_step_result* out, void* stream) {
+  if (!d_state || !out) return ZF_EINVAL;
+  DevState h;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(&h, d_state, sizeof(h), hipMemcpyDeviceToHost, s) != hipSuccess)
+    return ZF_EHIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return ZF_EHIP;
+  out->overflow = h.overflow;
+  out->skipped = h.skipped;
+  out->t = h.t;
+  out->sumsq = h.sumsq;
+  out->norm = h.norm;
+  out->coef = h.coef;
+  out->scale_used = h.scale_used;
+  out->scale_next = h.loss_scale;
+  out->gs = h.gs;
+  out->growth_ctr = h.growth_ctr;
+  return ZF_OK;
+}

@@ -1,0 +1,66 @@
+"""Binding of include/zf_inputs.h: seeded synthetic inputs filled on the GPU.
+
+Input generation only (no step arithmetic).  The values follow the
+splitmix64 + Irwin-Hall(12) definition in zf_inputs.h and depend only on
+(seed, stream, logical index).
+"""
+import ctypes as C
+import os
+
+from . import workloads as W
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libzf_inputs.so")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run fsdp_sharded_mixed_amd/build.py")
+    lib = C.CDLL(LIB_PATH)
+    lib.zfi_fill_normal16.restype = C.c_int
+    lib.zfi_fill_normal16.argtypes = [C.c_void_p, C.c_int64, C.c_int32, C.c_uint64, C.c_uint64,
+                                      C.c_int64, C.c_double, C.c_double, C.c_void_p]
+    lib.zfi_fill_normal32.restype = C.c_int
+    lib.zfi_fill_normal32.argtypes = [C.c_void_p, C.c_int64, C.c_uint64, C.c_uint64, C.c_int64,
+                                      C.c_double, C.c_void_p]
+    lib.zfi_stream_output.restype = C.c_uint64
+    lib.zfi_stream_output.argtypes = [C.c_uint64, C.c_uint64, C.c_uint64]
+    return lib
+
+
+lib = _load()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def fill_normal16(dst, n, dtype, seed, stream_id, logical_base, sigma, scale=1.0,
+                  offset=0, stream=None):
+    """Fill n 16-bit values of tensor `dst` starting at element `offset`."""
+    addr = dst.data_ptr() + 2 * int(offset)
+    rc = lib.zfi_fill_normal16(addr, int(n), int(dtype), int(seed), int(stream_id),
+                               int(logical_base), float(sigma), float(scale), _stream(stream))
+    if rc != 0:
+        raise RuntimeError(f"zfi_fill_normal16 failed ({rc})")
+
+
+def fill_normal32(dst, n, seed, stream_id, logical_base, sigma, offset=0, stream=None):
+    addr = dst.data_ptr() + 4 * int(offset)
+    rc = lib.zfi_fill_normal32(addr, int(n), int(seed), int(stream_id), int(logical_base),
+                               float(sigma), _stream(stream))
+    if rc != 0:
+        raise RuntimeError(f"zfi_fill_normal32 failed ({rc})")
+
+
+def stream_output(seed, stream_id, j):
+    return lib.zfi_stream_output(int(seed), int(stream_id), int(j))
+
+
+def inject_index(w, psi):
+    """Logical index that receives a workload's injected +inf: output 0 of
+    the inject stream, modulo Psi."""
+    return stream_output(w.seed, W.STREAM_INJECT, 0) % psi

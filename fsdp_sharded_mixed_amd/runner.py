@@ -1,0 +1,117 @@
+"""Device buffers and the step sequence for one workload on one GPU.
+
+torch supplies device memory and the stream; libzf_inputs fills the seeded
+inputs; every step runs through the libzf C ABI (fsdp_sharded_mixed_amd.zf).
+
+All per-element arrays use the padded flat index p of include/zf.h: the N
+ranks' shards of unit u sit side by side at [O_u, O_u + P_u).
+"""
+import torch
+
+from . import inputs as I
+from . import workloads as W
+from . import zf
+
+TORCH_16 = {W.F16: torch.float16, W.BF16: torch.bfloat16}
+
+
+class DeviceRun:
+    """A workload's device state: N replicas, fp32 master/m/v, 16-bit params,
+    workspace and state block, plus a reused unit buffer for stage 3."""
+
+    def __init__(self, w, device="cuda:0", grads=True):
+        self.w = w
+        self.device = torch.device(device)
+        self.plan = zf.plan_flat(w.segments, w.n_ranks, w.layout, w.stage)
+        s = self.plan.summary
+        self.psi, self.psi_pad = s.psi, s.psi_pad
+        n, dev = s.psi_pad, self.device
+        gdt, pdt = TORCH_16[w.grad_dtype], TORCH_16[w.param_dtype]
+        self.grads = [torch.zeros(n, dtype=gdt, device=dev) for _ in range(w.n_ranks)] \
+            if grads else []
+        self.master = torch.zeros(n, dtype=torch.float32, device=dev)
+        self.exp_avg = torch.zeros(n, dtype=torch.float32, device=dev)
+        self.exp_avg_sq = torch.zeros(n, dtype=torch.float32, device=dev)
+        self.params = torch.zeros(n, dtype=pdt, device=dev)
+        self.workspace = torch.empty(max(1, s.workspace_bytes), dtype=torch.uint8, device=dev)
+        self.state = torch.empty(zf.state_bytes(), dtype=torch.uint8, device=dev)
+        self.unit_buf = (torch.empty(s.max_unit_pad, dtype=pdt, device=dev)
+                         if w.stage == 3 else None)
+        self.hp = zf.hparams(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, w.max_norm)
+        self.step_no = 0
+        self.loss_scale = w.loss_scale
+
+    # ---- inputs ------------------------------------------------------------
+    def logical_to_padded(self, i):
+        for u in self.plan.units:
+            if u.lam <= i < u.lam + u.L:
+                return u.O + (i - u.lam)
+        raise IndexError(i)
+
+    def init_state(self):
+        """fp32 master from the seeded stream (norm weights 1.0 where the
+        workload says so), m = v = 0, 16-bit params = RNE(master), t = 0."""
+        w = self.w
+        self.master.zero_()
+        for u in self.plan.units:
+            I.fill_normal32(self.master, u.L, w.seed, W.STREAM_MASTER, u.lam, w.master_sigma,
+                            offset=u.O)
+        if w.norm_weights_one:
+            for a, b in w.norm_ranges():
+                pa = self.logical_to_padded(a)
+                self.master[pa:pa + (b - a)] = 1.0
+        self.exp_avg.zero_()
+        self.exp_avg_sq.zero_()
+        self.params.copy_(self.master.to(self.params.dtype))
+        zf.state_init(self.state, w.loss_scale, w.dynamic, w.growth_interval)
+        self.step_no = 0
+        self.loss_scale = w.loss_scale
+
+    def fill_grads(self, step, scale, sigma=None):
+        """Replica q's gradient for `step`, keyed by logical index (pads stay 0)."""
+        w = self.w
+        sigma = w.sigma if sigma is None else sigma
+        for q, g in enumerate(self.grads):
+            for u in self.plan.units:
+                I.fill_normal16(g, u.L, w.grad_dtype, w.seed, W.grad_stream(step, q), u.lam,
+                                sigma, scale, offset=u.O)
+
+    def inject_inf(self):
+        """+inf into the workload's inject replica at its inject index."""
+        i = I.inject_index(self.w, self.psi)
+        p = self.logical_to_padded(i)
+        self.grads[self.w.inject_replica][p] = float("inf")
+        return i
+
+    # ---- the step ------------------------------------------------------------
+    def step(self, stream=None, phase_events=None):
+        self.step_no += 1
+        zf.shard_step(self.plan, self.hp, self.w.grad_dtype, self.w.param_dtype, self.grads,
+                      self.master, self.exp_avg, self.exp_avg_sq, self.params, self.workspace,
+                      self.state, stream=stream, phase_events=phase_events)
+
+    def result(self):
+        return zf.read_result(self.state)
+
+    def unit_shards(self, u):
+        """Rank r's 16-bit shard of unit u: params[O_u + r*S_u : +S_u]."""
+        info = self.plan.units[u]
+        base = self.params.data_ptr()
+        return [base + 2 * (info.O + r * info.S) for r in range(self.w.n_ranks)]
+
+    def gather(self, u, stream=None):
+        zf.gather(self.plan, u, self.w.param_dtype, self.unit_shards(u), self.unit_buf,
+                  stream=stream)
+        return self.unit_buf[:self.plan.units[u].P]
+
+    def run_workload_step(self):
+        """One step of the workload's own sequence: fresh grads for step k at
+        the current loss scale, the injection if due, then the step."""
+        k = self.step_no + 1
+        self.fill_grads(k, self.loss_scale)
+        if self.w.inject_step == k:
+            self.inject_inf()
+        self.step()
+        res = self.result()
+        self.loss_scale = res.scale_next
+        return res

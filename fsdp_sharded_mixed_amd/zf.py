@@ -1,0 +1,233 @@
+"""Thin Python binding of include/zf.h (argument marshalling only).
+
+Every step of the path runs in libzf.so; this module converts Python values
+and torch tensors (device pointers via data_ptr(), the HIP stream via
+torch.cuda.current_stream()) into the C ABI's arguments and raises ZfError
+on a non-zero status.  If libzf.so is missing it raises at import: there is
+no fallback.
+"""
+import ctypes as C
+import os
+from dataclasses import dataclass
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libzf.so")
+
+F16, BF16 = 1, 2
+GLOBAL_FLAT, PER_UNIT = 0, 1
+MAX_RANKS = 64
+STATUS = {0: "ZF_OK", -1: "ZF_EINVAL", -2: "ZF_EALIGN", -3: "ZF_EDTYPE", -4: "ZF_ESIZE",
+          -5: "ZF_EHIP", -6: "ZF_ENOMEM"}
+
+
+class ZfError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({strerror(status)})")
+
+
+class Segment(C.Structure):
+    _fields_ = [("numel", C.c_int64), ("unit", C.c_int32), ("kind", C.c_int32)]
+
+
+class PlanSummary(C.Structure):
+    _fields_ = [("psi", C.c_int64), ("psi_pad", C.c_int64), ("n_units", C.c_int64),
+                ("max_unit_pad", C.c_int64), ("n_ranks", C.c_int32), ("layout", C.c_int32),
+                ("stage", C.c_int32), ("policy", C.c_int32), ("workspace_bytes", C.c_int64),
+                ("state_bytes", C.c_int64 * 4), ("stage3_peak_bytes", C.c_int64),
+                ("comm_bytes", C.c_double * 5)]
+
+
+class UnitInfo(C.Structure):
+    _fields_ = [("L", C.c_int64), ("P", C.c_int64), ("S", C.c_int64), ("O", C.c_int64),
+                ("lam", C.c_int64)]
+
+
+class Hparams(C.Structure):
+    _fields_ = [("lr", C.c_double), ("beta1", C.c_double), ("beta2", C.c_double),
+                ("eps", C.c_double), ("weight_decay", C.c_double), ("max_norm", C.c_double)]
+
+
+class StepArgs(C.Structure):
+    _fields_ = [("grad_dtype", C.c_int32), ("param_dtype", C.c_int32),
+                ("grads", C.POINTER(C.c_void_p)), ("master", C.c_void_p),
+                ("exp_avg", C.c_void_p), ("exp_avg_sq", C.c_void_p), ("params", C.c_void_p),
+                ("workspace", C.c_void_p), ("state", C.c_void_p),
+                ("phase_events", C.POINTER(C.c_void_p))]
+
+
+class StepResult(C.Structure):
+    _fields_ = [("overflow", C.c_int32), ("skipped", C.c_int32), ("t", C.c_int64),
+                ("sumsq", C.c_double), ("norm", C.c_double), ("coef", C.c_double),
+                ("scale_used", C.c_double), ("scale_next", C.c_double), ("gs", C.c_float),
+                ("growth_ctr", C.c_int32)]
+
+
+# Every function declared in include/zf.h, with its ctypes signature.
+_SIGNATURES = {
+    "zf_plan_flat": (C.c_int, [C.POINTER(Segment), C.c_int64, C.c_int32, C.c_int32, C.c_int32,
+                               C.POINTER(C.c_void_p)]),
+    "zf_plan_info": (C.c_int, [C.c_void_p, C.POINTER(PlanSummary)]),
+    "zf_plan_unit": (C.c_int, [C.c_void_p, C.c_int64, C.POINTER(UnitInfo)]),
+    "zf_plan_free": (None, [C.c_void_p]),
+    "zf_workspace_bytes": (C.c_int64, [C.c_void_p]),
+    "zf_state_bytes": (C.c_int64, []),
+    "zf_state_init": (C.c_int, [C.c_void_p, C.c_double, C.c_int32, C.c_int32, C.c_void_p]),
+    "zf_shard_step": (C.c_int, [C.c_void_p, C.POINTER(Hparams), C.POINTER(StepArgs),
+                                C.c_void_p]),
+    "zf_reduce_scatter": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(C.c_void_p), C.c_void_p,
+                                    C.c_void_p]),
+    "zf_gather": (C.c_int, [C.c_void_p, C.c_int64, C.c_int32, C.POINTER(C.c_void_p),
+                            C.c_void_p, C.c_void_p]),
+    "zf_read_result": (C.c_int, [C.c_void_p, C.POINTER(StepResult), C.c_void_p]),
+    "zf_strerror": (C.c_char_p, [C.c_int]),
+}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run fsdp_sharded_mixed_amd/build.py "
+                          "(or __graft_entry__.build())")
+    lib = C.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def strerror(status):
+    return lib.zf_strerror(int(status)).decode()
+
+
+def _check(status, where):
+    if status != 0:
+        raise ZfError(status, where)
+
+
+def _ptr(x):
+    """Device pointer of a torch tensor, or an int address, or None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ptr_array(items):
+    return (C.c_void_p * len(items))(*[_ptr(t) for t in items])
+
+
+@dataclass
+class Plan:
+    """An immutable layout plan (owns the C zf_plan)."""
+    handle: int
+    summary: PlanSummary
+    units: list
+
+    def __del__(self, _free=lib.zf_plan_free):
+        h, self.handle = self.handle, None
+        if h:
+            _free(h)
+
+    @property
+    def n_ranks(self):
+        return self.summary.n_ranks
+
+    @property
+    def psi_pad(self):
+        return self.summary.psi_pad
+
+
+def plan_flat(segments, n_ranks, layout, stage):
+    """zf_plan_flat.  segments: sequence of (numel, unit[, kind]) or objects
+    with .numel/.unit/.kind attributes."""
+    arr = (Segment * len(segments))()
+    for i, s in enumerate(segments):
+        if isinstance(s, (tuple, list)):
+            numel, unit, kind = (list(s) + [0])[:3]
+        else:
+            numel, unit, kind = s.numel, s.unit, getattr(s, "kind", 0)
+        arr[i] = Segment(int(numel), int(unit), int(kind))
+    h = C.c_void_p()
+    _check(lib.zf_plan_flat(arr, len(segments), int(n_ranks), int(layout), int(stage),
+                            C.byref(h)), "zf_plan_flat")
+    summary = plan_info(h.value)
+    units = [plan_unit(h.value, u) for u in range(summary.n_units)]
+    return Plan(h.value, summary, units)
+
+
+def _handle(plan):
+    return plan.handle if isinstance(plan, Plan) else plan
+
+
+def plan_info(plan):
+    out = PlanSummary()
+    _check(lib.zf_plan_info(_handle(plan), C.byref(out)), "zf_plan_info")
+    return out
+
+
+def plan_unit(plan, u):
+    out = UnitInfo()
+    _check(lib.zf_plan_unit(_handle(plan), int(u), C.byref(out)), "zf_plan_unit")
+    return out
+
+
+def workspace_bytes(plan):
+    n = lib.zf_workspace_bytes(_handle(plan))
+    if n < 0:
+        raise ZfError(n, "zf_workspace_bytes")
+    return n
+
+
+def state_bytes():
+    return lib.zf_state_bytes()
+
+
+def state_init(state, loss_scale, dynamic, growth_interval=2000, stream=None):
+    _check(lib.zf_state_init(_ptr(state), float(loss_scale), int(bool(dynamic)),
+                             int(growth_interval), _stream(stream)), "zf_state_init")
+
+
+def hparams(lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, max_norm=1.0):
+    return Hparams(lr, beta1, beta2, eps, weight_decay, max_norm)
+
+
+def shard_step(plan, hp, grad_dtype, param_dtype, grads, master, exp_avg, exp_avg_sq, params,
+               workspace, state, stream=None, phase_events=None):
+    """zf_shard_step.  grads: N tensors (or addresses); phase_events: None or
+    4 raw hipEvent_t handles."""
+    gp = _ptr_array(grads)
+    ev = (C.c_void_p * 4)(*phase_events) if phase_events is not None else None
+    args = StepArgs(int(grad_dtype), int(param_dtype), gp, _ptr(master), _ptr(exp_avg),
+                    _ptr(exp_avg_sq), _ptr(params), _ptr(workspace), _ptr(state), ev)
+    _check(lib.zf_shard_step(_handle(plan), C.byref(hp), C.byref(args), _stream(stream)),
+           "zf_shard_step")
+
+
+def reduce_scatter(plan, grad_dtype, grads, rs_out, stream=None):
+    _check(lib.zf_reduce_scatter(_handle(plan), int(grad_dtype), _ptr_array(grads),
+                                 _ptr(rs_out), _stream(stream)), "zf_reduce_scatter")
+
+
+def gather(plan, unit, dtype, shards, unit_buf, stream=None):
+    _check(lib.zf_gather(_handle(plan), int(unit), int(dtype), _ptr_array(shards),
+                         _ptr(unit_buf), _stream(stream)), "zf_gather")
+
+
+def read_result(state, stream=None):
+    out = StepResult()
+    _check(lib.zf_read_result(_ptr(state), C.byref(out), _stream(stream)), "zf_read_result")
+    return out

@@ -1,0 +1,46 @@
+/*
+ * zf_inputs.h -- seeded synthetic inputs on the GPU (a library of its own).
+ *
+ * Not part of the step: it only fills device buffers with reproducible
+ * pseudo-random values, so that the step can be driven at full model size
+ * without host traffic.  It holds no arithmetic of the step.
+ *
+ * Definition (implemented here and, independently, by the CPU oracle):
+ *   splitmix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number
+ *   generators", OOPSLA 2014) is used as a counter-based generator: output j
+ *   of a generator whose state starts at s is mix64(s + (j+1)*0x9E3779B97F4A7C15).
+ *   A stream's starting state is output number `stream` of the generator
+ *   seeded with `seed`.  Element i of a stream takes outputs 3i, 3i+1, 3i+2,
+ *   splits them into twelve 16-bit words k_0..k_11, and
+ *       z = (k_0 + ... + k_11 - 393210) / 65536      (Irwin-Hall(12), exact)
+ *   is a standard-normal stand-in bounded by +-6.  A 16-bit draw is
+ *   RNE16((z * f32(sigma)) * f32(scale)), each product one binary32
+ *   rounding; an fp32 draw is z * f32(sigma).
+ * Element k of a fill has logical index logical_base + k, so a value depends
+ * only on (seed, stream, logical index), never on where the buffer sits.
+ */
+#ifndef ZF_INPUTS_H
+#define ZF_INPUTS_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Fill dst[0..n) (device, 16-bit, 2-byte aligned) with draws of `stream`.
+ * dtype: 1 = fp16, 2 = bf16.  Enqueued on the hipStream_t `stream_handle`.
+ * Returns 0, or -1 (bad argument) / -5 (HIP error). */
+int zfi_fill_normal16(void* dst, int64_t n, int32_t dtype, uint64_t seed, uint64_t stream,
+                      int64_t logical_base, double sigma, double scale, void* stream_handle);
+
+/* Fill dst[0..n) (device fp32, 4-byte aligned) with z * f32(sigma). */
+int zfi_fill_normal32(float* dst, int64_t n, uint64_t seed, uint64_t stream,
+                      int64_t logical_base, double sigma, void* stream_handle);
+
+/* Output j of `stream`'s splitmix64 generator (host computation). */
+uint64_t zfi_stream_output(uint64_t seed, uint64_t stream, uint64_t j);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

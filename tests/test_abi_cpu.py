@@ -1,0 +1,188 @@
+"""Host-side checks of the C-ABI libraries (no GPU needed).
+
+The libraries load, export every function their headers declare, and their
+host logic (layout plan, ledger, would-be traffic, argument validation)
+agrees with the CPU oracle.  No call here reaches a kernel launch: every
+invalid-argument call returns before the HIP runtime is touched.
+"""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+from fsdp_sharded_mixed_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+INCLUDE = os.path.join(ROOT, "include")
+
+
+def _declared(header):
+    text = open(os.path.join(INCLUDE, header)).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:zf|zfi)_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def zf():
+    from fsdp_sharded_mixed_amd import zf as Z
+    return Z
+
+
+def test_headers_declare_the_calls():
+    names = _declared("zf.h")
+    for required in ("zf_plan_flat", "zf_shard_step", "zf_gather"):
+        assert required in names
+    assert len(_declared("zf_inputs.h")) == 3
+
+
+@pytest.mark.parametrize("header,lib", [("zf.h", "libzf.so"), ("zf_inputs.h", "libzf_inputs.so")])
+def test_library_exports_every_declared_symbol(header, lib):
+    path = os.path.join(ROOT, "fsdp_sharded_mixed_amd", lib)
+    L = C.CDLL(path)
+    for name in _declared(header):
+        assert hasattr(L, name), f"{lib} does not export {name}"
+
+
+def test_binding_covers_every_declared_call(zf):
+    assert set(_declared("zf.h")) == set(zf._SIGNATURES)
+
+
+def _oracle_units(w):
+    numel, unit = w.seg_arrays()
+    return O.layout(numel, unit, w.n_ranks, w.layout)
+
+
+@pytest.mark.parametrize("name", list(W.ALL))
+def test_plan_matches_oracle_layout(zf, name):
+    w = W.get(name)
+    plan = zf.plan_flat(w.segments, w.n_ranks, w.layout, w.stage)
+    units, psi, psi_pad = _oracle_units(w)
+    s = plan.summary
+    assert (s.psi, s.psi_pad, s.n_units) == (psi, psi_pad, len(units))
+    for mine, ref in zip(plan.units, units):
+        assert (mine.L, mine.P, mine.S, mine.O, mine.lam) == (ref["L"], ref["P"], ref["S"],
+                                                                ref["O"], ref["lam"])
+    assert s.max_unit_pad == units["P"].max()
+    for stage in range(4):
+        ab, peak = O.ledger(units, w.n_ranks, stage)
+        assert s.state_bytes[stage] == ab
+        if stage == 3:
+            assert s.stage3_peak_bytes == peak
+    for v in range(5):
+        assert s.comm_bytes[v] == pytest.approx(O.comm_bytes(psi_pad, w.n_ranks, v), rel=1e-15)
+
+
+def test_plan_bruteforce_small(zf):
+    rng = np.random.default_rng(3)
+    for _ in range(300):
+        n = int(rng.integers(1, 17))
+        k = int(rng.integers(1, 6))
+        lens = [int(x) for x in rng.integers(1, 40, k)]
+        layout = int(rng.integers(0, 2))
+        uid = sorted(int(x) for x in rng.integers(0, k, k)) if layout else [0] * k
+        # make unit ids run 0,0,..,1,..
+        remap, nxt = {}, 0
+        for u in uid:
+            if u not in remap:
+                remap[u] = nxt
+                nxt += 1
+        uid = [remap[u] for u in uid]
+        plan = zf.plan_flat(list(zip(lens, uid)), n, layout, 2)
+        units, psi, psi_pad = O.layout(lens, uid, n, layout)
+        assert plan.summary.psi_pad == psi_pad
+        assert [(u.P, u.S, u.O) for u in plan.units] == [(u["P"], u["S"], u["O"]) for u in units]
+
+
+def test_policy_and_workspace(zf):
+    for n, pol in ((1, 0), (2, 0), (4, 0), (5, 1), (8, 1)):
+        plan = zf.plan_flat([(1000, 0)], n, W.GLOBAL_FLAT, 2)
+        assert plan.summary.policy == pol
+        ws = zf.workspace_bytes(plan)
+        if pol:
+            assert ws >= plan.summary.psi_pad * 4
+        assert ws % 256 == 0
+
+
+def test_plan_errors(zf):
+    Z = zf
+    with pytest.raises(Z.ZfError) as e:
+        Z.plan_flat([(10, 0)], 0, W.GLOBAL_FLAT, 2)
+    assert e.value.status == -4
+    with pytest.raises(Z.ZfError) as e:
+        Z.plan_flat([(10, 0)], Z.MAX_RANKS + 1, W.GLOBAL_FLAT, 2)
+    assert e.value.status == -4
+    for bad in ([(0, 0)], [(5, 0), (5, 2)], [(5, 1)]):
+        with pytest.raises(Z.ZfError) as e:
+            Z.plan_flat(bad, 2, W.PER_UNIT, 2)
+        assert e.value.status == -1
+    with pytest.raises(Z.ZfError):
+        Z.plan_flat([(10, 0)], 2, 7, 2)
+    with pytest.raises(Z.ZfError):
+        Z.plan_flat([(10, 0)], 2, W.GLOBAL_FLAT, 4)
+    assert Z.lib.zf_plan_info(None, C.byref(Z.PlanSummary())) == -1
+    assert Z.lib.zf_plan_unit(None, 0, C.byref(Z.UnitInfo())) == -1
+    plan = Z.plan_flat([(10, 0)], 2, W.GLOBAL_FLAT, 2)
+    assert Z.lib.zf_plan_unit(plan.handle, 1, C.byref(Z.UnitInfo())) == -1
+    Z.lib.zf_plan_free(None)  # NULL is allowed
+    assert Z.strerror(-2) and Z.strerror(12345) == "unknown status"
+
+
+def test_step_argument_errors_enqueue_nothing(zf):
+    """Invalid arguments are rejected before any HIP call (so this runs on a
+    machine without a GPU): NULLs, bad dtypes, misaligned pointers."""
+    Z = zf
+    plan = Z.plan_flat([(100, 0)], 2, W.GLOBAL_FLAT, 2)
+    hp = Z.hparams(1e-3)
+    ok = 0x10000
+    grads = (C.c_void_p * 2)(ok, ok)
+
+    def args(**kw):
+        d = dict(grad_dtype=1, param_dtype=1, grads=grads, master=ok, exp_avg=ok, exp_avg_sq=ok,
+                 params=ok, workspace=ok, state=ok, phase_events=None)
+        d.update(kw)
+        return Z.StepArgs(d["grad_dtype"], d["param_dtype"], d["grads"], d["master"],
+                          d["exp_avg"], d["exp_avg_sq"], d["params"], d["workspace"],
+                          d["state"], d["phase_events"])
+
+    step = lambda a, p=plan.handle, h=hp: Z.lib.zf_shard_step(p, C.byref(h), C.byref(a), None)
+    assert step(args(), p=None) == -1
+    assert step(args(grad_dtype=3)) == -3
+    assert step(args(param_dtype=0)) == -3
+    assert step(args(master=None)) == -1
+    assert step(args(master=ok + 4)) == -2
+    assert step(args(params=ok + 8)) == -2
+    assert step(args(grads=(C.c_void_p * 2)(ok, None))) == -1
+    assert step(args(grads=(C.c_void_p * 2)(ok, ok + 2))) == -2
+    assert step(args(state=None)) == -1
+    assert step(args(workspace=None)) == -1
+    assert step(args(), h=Z.hparams(1e-3, beta1=1.0)) == -1
+    assert Z.lib.zf_shard_step(plan.handle, None, C.byref(args()), None) == -1
+    assert Z.lib.zf_reduce_scatter(plan.handle, 9, grads, ok, None) == -3
+    assert Z.lib.zf_reduce_scatter(plan.handle, 1, grads, ok + 4, None) == -2
+    assert Z.lib.zf_reduce_scatter(plan.handle, 1, None, ok, None) == -1
+    shards = (C.c_void_p * 2)(ok, ok)
+    assert Z.lib.zf_gather(plan.handle, 1, 1, shards, ok, None) == -1
+    assert Z.lib.zf_gather(plan.handle, 0, 5, shards, ok, None) == -3
+    assert Z.lib.zf_gather(plan.handle, 0, 1, (C.c_void_p * 2)(ok, ok + 1), ok, None) == -2
+    assert Z.lib.zf_gather(plan.handle, 0, 1, shards, None, None) == -1
+    assert Z.lib.zf_state_init(None, 1.0, 0, 10, None) == -1
+    assert Z.lib.zf_state_init(ok, 0.0, 0, 10, None) == -1
+    assert Z.lib.zf_state_init(ok + 4, 1.0, 0, 10, None) == -2
+    assert Z.lib.zf_read_result(None, C.byref(Z.StepResult()), None) == -1
+    assert Z.state_bytes() == 256
+
+
+def test_input_library_stream_output_matches_oracle():
+    """The host half of the GPU input generator (stream starting state and
+    splitmix64 outputs) agrees with the oracle's own implementation."""
+    from fsdp_sharded_mixed_amd import inputs as I
+    for seed in (0, 1, 5, 2**63 + 7):
+        for stream in (0, 1, W.STREAM_MASTER, W.STREAM_INJECT, W.grad_stream(3, 1)):
+            st = O.lib().or_stream_state(seed, stream)
+            state = C.c_uint64(st)
+            for j in range(3):
+                assert I.stream_output(seed, stream, j) == O.lib().or_splitmix64_next(
+                    C.byref(state))

@@ -1,0 +1,154 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+bench times (the library's own grids over the whole padded flat).
+
+The oracle cannot hold these models, so it checks them by regeneration:
+the exact global squared norm and overflow flag of every step come from
+re-deriving every reduced gradient on the host (a thread pool over index
+ranges, partials added in order), and a sample of elements -- random
+indices, every rank's shard edges, norm weights, the injected index and
+its neighbours -- is carried through the oracle's element update and
+compared with the device every step.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from fsdp_sharded_mixed_amd import workloads as W
+from tests import gpu_common as G
+from tests import oracle_inputs as OI
+
+pytestmark = pytest.mark.gpu
+
+
+def sample_indices(w, plan, k=4096, extra=()):
+    rng = np.random.default_rng(w.seed)
+    idx = set(int(i) for i in rng.integers(0, w.psi, k))
+    for u in plan.units:
+        for r in range(w.n_ranks):
+            for j in (u.lam + r * u.S, u.lam + r * u.S + u.S - 1):
+                if u.lam <= j < u.lam + u.L:
+                    idx.add(int(j))
+    for a, b in w.norm_ranges()[:4]:
+        idx.update({a, a + 1, b - 1})
+    idx.update({0, w.psi - 1})
+    idx.update(int(e) for e in extra if 0 <= e < w.psi)
+    return np.array(sorted(idx), np.int64)
+
+
+def padded_of(plan, idx):
+    lam = np.array([u.lam for u in plan.units], np.int64)
+    off = np.array([u.O for u in plan.units], np.int64)
+    k = np.searchsorted(lam, idx, side="right") - 1
+    return off[k] + (idx - lam[k])
+
+
+def take(t, pidx):
+    return t[torch.from_numpy(pidx).to(t.device)].cpu()
+
+
+def check_samples(dev, so, pidx, what):
+    m = take(dev.master, pidx).numpy()
+    ea = take(dev.exp_avg, pidx).numpy()
+    eas = take(dev.exp_avg_sq, pidx).numpy()
+    G.assert_state_close(f"{what} master", m, so.p)
+    G.assert_state_close(f"{what} exp_avg", ea, so.m)
+    G.assert_state_close(f"{what} exp_avg_sq", eas, so.v)
+    prm = take(dev.params.view(torch.int16), pidx).numpy().view(np.uint16)
+    ref = O.narrow(dev.w.param_dtype, so.p)
+    assert G.ulp16_distance(prm, ref).max() <= 1, f"{what} params"
+    return float((m.view(np.uint32) == so.p.view(np.uint32)).mean())
+
+
+def run_workload(R, name, rs_check_step=1):
+    w = W.get(name)
+    G.say(f"workload {w.name}: Psi={w.psi:,} N={w.n_ranks} stage={w.stage} steps={w.steps}")
+    dev = R.DeviceRun(w)
+    dev.init_state()
+    from fsdp_sharded_mixed_amd import inputs as I
+    inj = I.inject_index(w, w.psi) if w.inject_step else None
+    extra = [] if inj is None else [inj - 1, inj, inj + 1]
+    idx = sample_indices(w, dev.plan, extra=extra)
+    pidx = padded_of(dev.plan, idx)
+    so = G.SampledOracle(w, w.psi, idx)
+    assert np.array_equal(take(dev.master, pidx).numpy().view(np.uint32), so.p.view(np.uint32))
+    trace = []
+    for k in range(1, w.steps + 1):
+        scale = dev.loss_scale
+        dev.fill_grads(k, scale)
+        if w.inject_step == k:
+            dev.inject_inf()
+        if k == rs_check_step:
+            from fsdp_sharded_mixed_amd import zf
+            rs = torch.empty(dev.psi_pad, dtype=torch.float32, device=dev.device)
+            zf.reduce_scatter(dev.plan, w.grad_dtype, dev.grads, rs)
+            ref = O.regen_acc(w.grad_dtype, w.n_ranks, w.seed, k, w.sigma, scale, idx)
+            got = take(rs, pidx).numpy()
+            assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), "RS sums"
+            del rs
+        dev.step()
+        res_d = dev.result()
+        dev.loss_scale = res_d.scale_next
+        res_o = so.step(inject_index=inj if w.inject_step == k else None)
+        G.assert_result_matches(res_d, res_o, f"{w.name} step {k}")
+        share = check_samples(dev, so, pidx, f"{w.name} step {k}")
+        trace.append((k, res_d.skipped, res_d.t, res_d.scale_used, res_d.scale_next,
+                      round(res_d.norm, 6), round(res_d.coef, 6), share))
+        G.say(f"  step {k}: skipped={res_d.skipped} t={res_d.t} S={res_d.scale_used}->"
+              f"{res_d.scale_next} norm={res_d.norm:.6f} (oracle {res_o.norm:.6f}) "
+              f"coef={res_d.coef:.6f} exact-share={share:.4f}")
+        if w.stage == 3:
+            check_unit_gathers(dev, so, idx, w)
+    return dev, trace
+
+
+def check_unit_gathers(dev, so, idx, w):
+    """ZeRO-3: gather every unit into the reused buffer (forward order) and
+    check the sampled elements and the unit's padding."""
+    ref16 = O.narrow(w.param_dtype, so.p)
+    for u, info in enumerate(dev.plan.units):
+        buf = dev.gather(u)
+        sel = (idx >= info.lam) & (idx < info.lam + info.L)
+        if sel.any():
+            k = torch.from_numpy(idx[sel] - info.lam).to(buf.device)
+            got = buf.view(torch.int16)[k].cpu().numpy().view(np.uint16)
+            assert G.ulp16_distance(got, ref16[sel]).max() <= 1, f"unit {u}"
+        if info.P > info.L:
+            assert torch.all(buf[info.L:info.P].view(torch.int16) == 0)
+
+
+@pytest.fixture(scope="module")
+def R():
+    from fsdp_sharded_mixed_amd import runner
+    assert torch.cuda.is_available()
+    return runner
+
+
+def test_llama73m_n8(R):
+    """73M decoder, N = 8 (materialised sums), ten steps, clipped each step."""
+    dev, trace = run_workload(R, "llama-73m-n8")
+    assert all(t[1] == 0 for t in trace)
+    assert all(abs(t[5] - 3.03) < 0.1 and t[6] < 1.0 for t in trace)
+
+
+def test_llama654m_n2(R):
+    """654M decoder, N = 2 (recomputed sums), gradients scaled so the global
+    norm is about 3: clipping is active."""
+    dev, trace = run_workload(R, "llama-654m-n2")
+    assert all(abs(t[5] - 3.0) < 0.1 and t[6] < 1.0 for t in trace)
+
+
+def test_llama2b_zero3(R):
+    """2.1B decoder as 34 FSDP units, N = 2, stage 3: resident 16-bit shards
+    and per-unit gathers into one reused buffer."""
+    dev, trace = run_workload(R, "llama-2.1b-n2-zero3")
+    assert len(dev.plan.units) == 34
+
+
+def test_llama4b_n2_injected_overflow(R):
+    """4.06B decoder, N = 2, fp16 under dynamic loss scaling with +inf in
+    replica 1 at step 2: step 2 is skipped and S halves 32768 -> 16384."""
+    dev, trace = run_workload(R, "llama-4.06b-n2")
+    assert [(t[1], t[2]) for t in trace] == [(0, 1), (1, 1), (0, 2), (0, 3)]
+    assert trace[1][3] == 32768.0 and trace[1][4] == 16384.0
+    assert trace[2][3] == 16384.0
