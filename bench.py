@@ -45,11 +45,99 @@ def update_kernel_bytes_per_elem(w, materialized):
     return (4 if materialized else 2 * w.n_ranks) + 12 + 12 + 2
 
 
-def traffic_factor():
-    """HBM traffic from rocprofv3 counters, if a summary has been committed:
-    profiles/<workload>_traffic.json holds per-launch FETCH/WRITE bytes of the
-    update kernel, already scaled by the copy-kernel calibration."""
-    return None
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCE = os.path.join(ROOT, "fsdp_sharded_mixed_amd", "csrc", "zf_step.hip")
+COPY_BYTES = 1 << 30  # calibration copy: 1 GiB read + 1 GiB written
+
+
+def kernel_source_hash():
+    import hashlib
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(workload):
+    """Measured HBM bytes per launch of the update kernel from the committed
+    rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, each scaled by the
+    same counter's reading for a 1 GiB copy), or None if there is none or the
+    kernel source has changed since it was taken."""
+    path = os.path.join(PROFILES, f"zf_pass2_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return d["zf_pass2"]["hbm_bytes_per_launch"]
+
+
+def _csv_rows(directory, suffix):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(directory, "**", "*" + suffix), recursive=True))
+    if not files:
+        raise SystemExit(f"no *{suffix} under {directory}")
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_trace(directory, out, command):
+    """Text summary of a rocprofv3 --kernel-trace --stats run."""
+    rows = _csv_rows(directory, "kernel_stats.csv")
+    lines = [f"command: {command}", "",
+             f"{'kernel':<70} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}"]
+    for r in rows:
+        name = r["Name"].replace("(anonymous namespace)::", "")
+        name = name if len(name) <= 70 else name[:67] + "..."
+        lines.append(f"{name:<70} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>10.2f} "
+                     f"{float(r['MinNs']) / 1e3:>10.2f} {float(r['MaxNs']) / 1e3:>10.2f} "
+                     f"{float(r['Percentage']):>6.2f}")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_pmc(fetch_dir, write_dir, workload, out, commands):
+    """Per-launch HBM traffic of the step's kernels from two counter runs,
+    scaled by the counters' reading for the 1 GiB calibration copy."""
+    from fsdp_sharded_mixed_amd import workloads as W
+
+    def per_kernel(directory, counter):
+        rows = _csv_rows(directory, "counter_collection.csv")
+        vals = {}
+        for r in rows:
+            if r.get("Counter_Name") != counter:
+                continue
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    def pick(vals, key):
+        hits = [v for k, v in vals.items() if key in k]
+        if not hits:
+            raise SystemExit(f"no dispatch of {key}")
+        xs = sorted(hits[0])
+        return xs[len(xs) // 2]  # median over dispatches (KiB)
+
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    copy_key = next(k for k in fetch if "copy" in k.lower() and "zf_" not in k)
+    f_scale = COPY_BYTES / (pick(fetch, copy_key) * 1024.0)
+    w_scale = COPY_BYTES / (pick(write, copy_key) * 1024.0)
+    w = W.get(workload)
+    res = {"workload": workload, "kernel_source_sha256_16": kernel_source_hash(),
+           "calibration": {"kernel": copy_key, "bytes_each_way": COPY_BYTES,
+                           "fetch_scale": f_scale, "write_scale": w_scale},
+           "commands": commands}
+    for key in ("zf_pass1", "zf_pass2", "zf_gather"):
+        try:
+            fb = pick(fetch, key) * 1024.0 * f_scale
+            wb = pick(write, key) * 1024.0 * w_scale
+        except SystemExit:
+            continue
+        res[key] = {"fetch_bytes": fb, "write_bytes": wb, "hbm_bytes_per_launch": fb + wb,
+                    "per_param": (fb + wb) / w.psi}
+    with open(out, "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps(res, indent=1))
 
 
 def cpu_baseline(w, min_seconds=10.0, max_steps=40):
@@ -93,7 +181,19 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("DIR", "OUT"))
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"))
+    ap.add_argument("--command", default="", help="command text recorded in a summary")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace, args.command)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload,
+                      args.summarize_pmc[2], args.command)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(N data-parallel ranks are emulated on a single device)", file=sys.stderr)
@@ -106,6 +206,13 @@ def main():
     torch.cuda.set_device(0)
     print(f"bench: {w.name} Psi={w.psi:,} N={w.n_ranks} stage={w.stage}", file=sys.stderr,
           flush=True)
+    if args.calibrate_copy:
+        src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     dev = runner.DeviceRun(w, device="cuda:0")
     dev.init_state()
     dev.fill_grads(1, w.loss_scale)
@@ -183,7 +290,8 @@ def main():
                        "pass2_update": round(p2, 5)},
         "roofline": {"bound": "hbm", "achieved": round(upd_gbs, 2), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(upd_gbs / PEAK_HBM_GBS, 4),
-                     "traffic": traffic_factor(), "kernel": "zf_pass2 (fused AdamW+cast+gather)",
+                     "traffic": traffic_for(w.name),
+                     "kernel": "zf_pass2 (fused AdamW+cast+gather)",
                      "bytes_per_launch": upd_bytes},
     }
     if not args.no_cpu_baseline:

@@ -108,13 +108,20 @@ extern "C" int zf_plan_flat(const zf_segment* segs, int64_t nseg, int32_t n_rank
   // unless writing and re-reading an fp32 copy (8 bytes) is cheaper.
   s.policy = (2 * n_ranks > 8) ? 1 : 0;
 
-  const int64_t vecs = (s.psi_pad + zf::kVec - 1) / zf::kVec;
-  int64_t blocks = (vecs + zf::kThreads - 1) / zf::kThreads;
-  if (blocks < 1) blocks = 1;
-  if (blocks > zf::kMaxPass1Blocks) blocks = zf::kMaxPass1Blocks;
-  p->pass1_blocks = (int32_t)blocks;
+  const int64_t nvec = s.psi_pad / zf::kVec;  // the ragged tail rides on the last tile
+  p->unr1 = zf::unr_pass1(n_ranks);
+  p->unr2 = zf::unr_pass2(n_ranks, s.psi_pad, s.policy == 1);
+  const int64_t t1 = (nvec + zf::kThreads * p->unr1 - 1) / (zf::kThreads * p->unr1);
+  const int64_t t2 = (nvec + zf::kThreads * p->unr2 - 1) / (zf::kThreads * p->unr2);
+  p->pass1_tiles = t1 < 1 ? 1 : t1;
+  p->pass2_tiles = t2 < 1 ? 1 : t2;
+  int64_t l2 = (p->pass1_tiles + zf::kThreads - 1) / zf::kThreads;
+  if (l2 > zf::kMaxLevel2Blocks) l2 = zf::kMaxLevel2Blocks;
+  p->level2_blocks = (int32_t)l2;
   p->ws_partials_offset = 0;
-  int64_t ws = round_up(blocks * 16, 256);
+  int64_t ws = round_up(p->pass1_tiles * 16, 256);
+  p->ws_partials2_offset = ws;
+  ws += round_up(l2 * 16, 256);
   p->ws_rs_offset = -1;
   if (s.policy == 1) {
     p->ws_rs_offset = ws;

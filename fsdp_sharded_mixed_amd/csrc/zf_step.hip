@@ -61,6 +61,27 @@ struct GradPtrs {
   const uint16_t* p[ZF_MAX_RANKS];
 };
 
+// 16-byte vectors.  Streams that are not read again within the step are
+// stored with the non-temporal hint (global_store ... nt).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <bool NT>
+__device__ __forceinline__ u32x4 ld16(const uint16_t* base, int64_t v) {
+  const u32x4* p = reinterpret_cast<const u32x4*>(base) + v;
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+__device__ __forceinline__ f32x4 ldf(const float* base, int64_t v) {
+  return reinterpret_cast<const f32x4*>(base)[v];
+}
+__device__ __forceinline__ void stf_nt(float* base, int64_t v, f32x4 x) {
+  __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(base) + v);
+}
+__device__ __forceinline__ void st16_nt(void* base, int64_t v, u32x4 x) {
+  __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(base) + v);
+}
+
 // ---------------------------------------------------------------------------
 // 16-bit <-> binary32.  Widening is exact; narrowing uses the hardware
 // round-to-nearest-even conversions (v_cvt_pk_bf16_f32, v_cvt_f16_f32).
@@ -90,7 +111,7 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 }
 
 template <int DT>
-__device__ __forceinline__ void widen8(const uint4& w, float (&x)[8]) {
+__device__ __forceinline__ void widen8(const u32x4& w, float (&x)[8]) {
   x[0] = lo16<DT>(w.x); x[1] = hi16<DT>(w.x);
   x[2] = lo16<DT>(w.y); x[3] = hi16<DT>(w.y);
   x[4] = lo16<DT>(w.z); x[5] = hi16<DT>(w.z);
@@ -104,12 +125,12 @@ __device__ __forceinline__ bool nonfinite(float x) {
 // Fixed-order sum of the N replicas at vector v (elements 8v .. 8v+7).
 // NR > 0: N known at compile time, all N loads issued before the adds.
 // NR == 0: N at run time, in groups of four replicas.
-template <int NR, int DT>
+template <int NR, int DT, bool NT>
 __device__ __forceinline__ void sum8(const GradPtrs& g, int nr, int64_t v, float (&acc)[8]) {
   if constexpr (NR > 0) {
-    uint4 w[NR];
+    u32x4 w[NR];
 #pragma unroll
-    for (int q = 0; q < NR; ++q) w[q] = reinterpret_cast<const uint4*>(g.p[q])[v];
+    for (int q = 0; q < NR; ++q) w[q] = ld16<NT>(g.p[q], v);
     widen8<DT>(w[0], acc);
 #pragma unroll
     for (int q = 1; q < NR; ++q) {
@@ -119,12 +140,12 @@ __device__ __forceinline__ void sum8(const GradPtrs& g, int nr, int64_t v, float
       for (int k = 0; k < 8; ++k) acc[k] = acc[k] + x[k];
     }
   } else {
-    widen8<DT>(reinterpret_cast<const uint4*>(g.p[0])[v], acc);
+    widen8<DT>(ld16<NT>(g.p[0], v), acc);
     int q = 1;
     for (; q + 4 <= nr; q += 4) {
-      uint4 w[4];
+      u32x4 w[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) w[j] = reinterpret_cast<const uint4*>(g.p[q + j])[v];
+      for (int j = 0; j < 4; ++j) w[j] = ld16<NT>(g.p[q + j], v);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float x[8];
@@ -135,7 +156,7 @@ __device__ __forceinline__ void sum8(const GradPtrs& g, int nr, int64_t v, float
     }
     for (; q < nr; ++q) {
       float x[8];
-      widen8<DT>(reinterpret_cast<const uint4*>(g.p[q])[v], x);
+      widen8<DT>(ld16<NT>(g.p[q], v), x);
 #pragma unroll
       for (int k = 0; k < 8; ++k) acc[k] = acc[k] + x[k];
     }
@@ -182,38 +203,44 @@ __device__ __forceinline__ void block_reduce(double& ss, uint32_t& bad) {
 
 // ---------------------------------------------------------------------------
 // Pass 1: reduce-scatter sums, overflow flag and squared-norm partials.
+// Block b owns tile b: vectors [b*256*U, (b+1)*256*U), thread t the
+// vectors b*256*U + u*256 + t (u < U), so each wave reads 1 KiB
+// contiguous from every replica per vector.  The last block also takes the
+// ragged tail (< 8 elements).
 struct Pass1Args {
   GradPtrs g;
   int64_t n;          // Psi'
   float* rs;          // fp32 sums (MAT) or unused
-  Partial* partials;  // one per block (NORM) or unused
+  Partial* partials;  // one per tile (NORM) or unused
   int32_t nr;
 };
 
-template <int NR, int DT, bool MAT, bool NORM>
+template <int NR, int DT, bool MAT, bool NORM, int U>
 __global__ __launch_bounds__(kThreads) void zf_pass1(Pass1Args a) {
   const int nr = NR > 0 ? NR : a.nr;
   const int64_t nvec = a.n / kVec;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  const int64_t v0 = (int64_t)blockIdx.x * kThreads * U + threadIdx.x;
   double ss = 0.0;
   uint32_t bad = 0;
-  for (int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x; v < nvec; v += stride) {
-    float acc[8];
-    sum8<NR, DT>(a.g, nr, v, acc);
-    if constexpr (MAT) {
-      float4* o = reinterpret_cast<float4*>(a.rs) + 2 * v;
-      o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-      o[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
-    }
-    if constexpr (NORM) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        bad |= nonfinite(acc[k]) ? 1u : 0u;
-        ss = ss + (double)acc[k] * (double)acc[k];
+  for (int u = 0; u < U; ++u) {
+    const int64_t v = v0 + (int64_t)u * kThreads;
+    if (v < nvec) {
+      float acc[8];
+      sum8<NR, DT, true>(a.g, nr, v, acc);
+      if constexpr (MAT) {
+        stf_nt(a.rs, 2 * v, (f32x4){acc[0], acc[1], acc[2], acc[3]});
+        stf_nt(a.rs, 2 * v + 1, (f32x4){acc[4], acc[5], acc[6], acc[7]});
+      }
+      if constexpr (NORM) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          bad |= nonfinite(acc[k]) ? 1u : 0u;
+          ss = ss + (double)acc[k] * (double)acc[k];
+        }
       }
     }
   }
-  // ragged tail (< 8 elements), taken by the last block
   const int64_t tail0 = nvec * kVec;
   if (blockIdx.x == gridDim.x - 1 && (int64_t)threadIdx.x < a.n - tail0) {
     const int64_t p = tail0 + threadIdx.x;
@@ -230,6 +257,30 @@ __global__ __launch_bounds__(kThreads) void zf_pass1(Pass1Args a) {
       a.partials[blockIdx.x].ss = ss;
       a.partials[blockIdx.x].bad = bad;
     }
+  }
+}
+
+// Level 2: block b reduces the tile partials [b*T/G, (b+1)*T/G) in order.
+struct Level2Args {
+  const Partial* in;
+  Partial* out;
+  int64_t n_in;
+};
+
+__global__ __launch_bounds__(kThreads) void zf_level2(Level2Args a) {
+  const int64_t G = gridDim.x;
+  const int64_t lo = a.n_in * (int64_t)blockIdx.x / G;
+  const int64_t hi = a.n_in * ((int64_t)blockIdx.x + 1) / G;
+  double ss = 0.0;
+  uint32_t bad = 0;
+  for (int64_t i = lo + threadIdx.x; i < hi; i += kThreads) {
+    ss = ss + a.in[i].ss;
+    bad = bad | a.in[i].bad;
+  }
+  block_reduce(ss, bad);
+  if (threadIdx.x == 0) {
+    a.out[blockIdx.x].ss = ss;
+    a.out[blockIdx.x].bad = bad;
   }
 }
 
@@ -323,7 +374,7 @@ __device__ __forceinline__ void adamw1(const Coef& c, float acc, float& p, float
   v = vv;
 }
 
-template <int NR, int GDT, int PDT, bool MAT>
+template <int NR, int GDT, int PDT, bool MAT, int U>
 __global__ __launch_bounds__(kThreads) void zf_pass2(Pass2Args a) {
   if (a.st->skipped) return;  // the whole grid leaves at once
   Coef c;
@@ -334,37 +385,35 @@ __global__ __launch_bounds__(kThreads) void zf_pass2(Pass2Args a) {
   c.lrf = a.lrf; c.ef = a.ef;
   const int nr = NR > 0 ? NR : a.nr;
   const int64_t nvec = a.n / kVec;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  float4* P4 = reinterpret_cast<float4*>(a.master);
-  float4* M4 = reinterpret_cast<float4*>(a.m);
-  float4* V4 = reinterpret_cast<float4*>(a.v);
-  uint4* O4 = reinterpret_cast<uint4*>(a.out);
-  for (int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x; v < nvec; v += stride) {
+  const int64_t v0 = (int64_t)blockIdx.x * kThreads * U + threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t v = v0 + (int64_t)u * kThreads;
+    if (v >= nvec) break;
     float acc[8];
     if constexpr (MAT) {
-      const float4 r0 = reinterpret_cast<const float4*>(a.rs)[2 * v];
-      const float4 r1 = reinterpret_cast<const float4*>(a.rs)[2 * v + 1];
+      const f32x4 r0 = ldf(a.rs, 2 * v), r1 = ldf(a.rs, 2 * v + 1);
       acc[0] = r0.x; acc[1] = r0.y; acc[2] = r0.z; acc[3] = r0.w;
       acc[4] = r1.x; acc[5] = r1.y; acc[6] = r1.z; acc[7] = r1.w;
     } else {
-      sum8<NR, GDT>(a.g, nr, v, acc);
+      sum8<NR, GDT, false>(a.g, nr, v, acc);
     }
-    const float4 p0 = P4[2 * v], p1 = P4[2 * v + 1];
-    const float4 m0 = M4[2 * v], m1 = M4[2 * v + 1];
-    const float4 v0 = V4[2 * v], v1 = V4[2 * v + 1];
+    const f32x4 p0 = ldf(a.master, 2 * v), p1 = ldf(a.master, 2 * v + 1);
+    const f32x4 m0 = ldf(a.m, 2 * v), m1 = ldf(a.m, 2 * v + 1);
+    const f32x4 w0 = ldf(a.v, 2 * v), w1 = ldf(a.v, 2 * v + 1);
     float p[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
     float m[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-    float w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
     for (int k = 0; k < 8; ++k) adamw1(c, acc[k], p[k], m[k], w[k]);
-    P4[2 * v] = make_float4(p[0], p[1], p[2], p[3]);
-    P4[2 * v + 1] = make_float4(p[4], p[5], p[6], p[7]);
-    M4[2 * v] = make_float4(m[0], m[1], m[2], m[3]);
-    M4[2 * v + 1] = make_float4(m[4], m[5], m[6], m[7]);
-    V4[2 * v] = make_float4(w[0], w[1], w[2], w[3]);
-    V4[2 * v + 1] = make_float4(w[4], w[5], w[6], w[7]);
-    O4[v] = make_uint4(pack2<PDT>(p[0], p[1]), pack2<PDT>(p[2], p[3]),
-                       pack2<PDT>(p[4], p[5]), pack2<PDT>(p[6], p[7]));
+    stf_nt(a.master, 2 * v, (f32x4){p[0], p[1], p[2], p[3]});
+    stf_nt(a.master, 2 * v + 1, (f32x4){p[4], p[5], p[6], p[7]});
+    stf_nt(a.m, 2 * v, (f32x4){m[0], m[1], m[2], m[3]});
+    stf_nt(a.m, 2 * v + 1, (f32x4){m[4], m[5], m[6], m[7]});
+    stf_nt(a.v, 2 * v, (f32x4){w[0], w[1], w[2], w[3]});
+    stf_nt(a.v, 2 * v + 1, (f32x4){w[4], w[5], w[6], w[7]});
+    st16_nt(a.out, v, (u32x4){pack2<PDT>(p[0], p[1]), pack2<PDT>(p[2], p[3]),
+                              pack2<PDT>(p[4], p[5]), pack2<PDT>(p[6], p[7])});
   }
   const int64_t tail0 = nvec * kVec;
   if (blockIdx.x == gridDim.x - 1 && (int64_t)threadIdx.x < a.n - tail0) {
@@ -455,17 +504,10 @@ int grads_ok(const zf_plan* plan, const void* const* grads, GradPtrs& out) {
   return ZF_OK;
 }
 
-int64_t pass2_blocks(int64_t n) {
-  const int64_t nvec = n / kVec;
-  int64_t b = (nvec + kThreads - 1) / kThreads;
-  if (b < 1) b = 1;
-  if (b > 8192) b = 8192;
-  return b;
-}
-
-template <bool MAT, bool NORM>
-int launch_pass1(int nr, int32_t dt, dim3 grid, hipStream_t s, const Pass1Args& a) {
-#define ZF_P1(NRV, DTV) hipLaunchKernelGGL((zf_pass1<NRV, DTV, MAT, NORM>), grid, dim3(kThreads), 0, s, a)
+template <bool MAT, bool NORM, int U>
+void launch_pass1_u(int nr, int32_t dt, dim3 grid, hipStream_t s, const Pass1Args& a) {
+#define ZF_P1(NRV, DTV) \
+  hipLaunchKernelGGL((zf_pass1<NRV, DTV, MAT, NORM, U>), grid, dim3(kThreads), 0, s, a)
 #define ZF_P1_DT(NRV) \
   do { if (dt == ZF_BF16) ZF_P1(NRV, ZF_BF16); else ZF_P1(NRV, ZF_F16); } while (0)
   switch (nr) {
@@ -481,16 +523,25 @@ int launch_pass1(int nr, int32_t dt, dim3 grid, hipStream_t s, const Pass1Args& 
   }
 #undef ZF_P1_DT
 #undef ZF_P1
+}
+
+template <bool MAT, bool NORM>
+int launch_pass1(const zf_plan* plan, int32_t dt, hipStream_t s, const Pass1Args& a) {
+  const dim3 grid((uint32_t)plan->pass1_tiles);
+  const int nr = plan->summary.n_ranks;
+  if (plan->unr1 == 2) launch_pass1_u<MAT, NORM, 2>(nr, dt, grid, s, a);
+  else launch_pass1_u<MAT, NORM, 1>(nr, dt, grid, s, a);
   return hipGetLastError() == hipSuccess ? ZF_OK : ZF_EHIP;
 }
 
-template <int GDT, int PDT>
+template <int GDT, int PDT, int U>
 void launch_pass2_nr(int nr, bool mat, dim3 grid, hipStream_t s, const Pass2Args& a) {
   if (mat) {
-    hipLaunchKernelGGL((zf_pass2<0, GDT, PDT, true>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((zf_pass2<0, GDT, PDT, true, U>), grid, dim3(kThreads), 0, s, a);
     return;
   }
-#define ZF_P2(NRV) hipLaunchKernelGGL((zf_pass2<NRV, GDT, PDT, false>), grid, dim3(kThreads), 0, s, a)
+#define ZF_P2(NRV) \
+  hipLaunchKernelGGL((zf_pass2<NRV, GDT, PDT, false, U>), grid, dim3(kThreads), 0, s, a)
   switch (nr) {
     case 1: ZF_P2(1); break;
     case 2: ZF_P2(2); break;
@@ -505,15 +556,25 @@ void launch_pass2_nr(int nr, bool mat, dim3 grid, hipStream_t s, const Pass2Args
 #undef ZF_P2
 }
 
-int launch_pass2(int nr, int32_t gdt, int32_t pdt, bool mat, dim3 grid, hipStream_t s,
-                 const Pass2Args& a) {
+template <int U>
+void launch_pass2_u(int nr, int32_t gdt, int32_t pdt, bool mat, dim3 grid, hipStream_t s,
+                    const Pass2Args& a) {
   if (gdt == ZF_BF16) {
-    if (pdt == ZF_BF16) launch_pass2_nr<ZF_BF16, ZF_BF16>(nr, mat, grid, s, a);
-    else launch_pass2_nr<ZF_BF16, ZF_F16>(nr, mat, grid, s, a);
+    if (pdt == ZF_BF16) launch_pass2_nr<ZF_BF16, ZF_BF16, U>(nr, mat, grid, s, a);
+    else launch_pass2_nr<ZF_BF16, ZF_F16, U>(nr, mat, grid, s, a);
   } else {
-    if (pdt == ZF_BF16) launch_pass2_nr<ZF_F16, ZF_BF16>(nr, mat, grid, s, a);
-    else launch_pass2_nr<ZF_F16, ZF_F16>(nr, mat, grid, s, a);
+    if (pdt == ZF_BF16) launch_pass2_nr<ZF_F16, ZF_BF16, U>(nr, mat, grid, s, a);
+    else launch_pass2_nr<ZF_F16, ZF_F16, U>(nr, mat, grid, s, a);
   }
+}
+
+int launch_pass2(const zf_plan* plan, int32_t gdt, int32_t pdt, hipStream_t s,
+                 const Pass2Args& a) {
+  const dim3 grid((uint32_t)plan->pass2_tiles);
+  const int nr = plan->summary.n_ranks;
+  const bool mat = plan->ws_rs_offset >= 0;
+  if (plan->unr2 == 2) launch_pass2_u<2>(nr, gdt, pdt, mat, grid, s, a);
+  else launch_pass2_u<1>(nr, gdt, pdt, mat, grid, s, a);
   return hipGetLastError() == hipSuccess ? ZF_OK : ZF_EHIP;
 }
 
@@ -573,19 +634,26 @@ extern "C" int zf_shard_step(const zf_plan* plan, const zf_hparams* hp,
   a1.rs = rs;
   a1.partials = partials;
   a1.nr = nr;
-  const dim3 g1(plan->pass1_blocks);
-  rc = mat ? launch_pass1<true, true>(nr, args->grad_dtype, g1, s, a1)
-           : launch_pass1<false, true>(nr, args->grad_dtype, g1, s, a1);
+  rc = mat ? launch_pass1<true, true>(plan, args->grad_dtype, s, a1)
+           : launch_pass1<false, true>(plan, args->grad_dtype, s, a1);
   if (rc != ZF_OK) return rc;
   if ((rc = record(args->phase_events, 1, s)) != ZF_OK) return rc;
 
+  Partial* partials2 = reinterpret_cast<Partial*>(ws + plan->ws_partials2_offset);
+  Level2Args a2l;
+  a2l.in = partials;
+  a2l.out = partials2;
+  a2l.n_in = plan->pass1_tiles;
+  hipLaunchKernelGGL(zf_level2, dim3((uint32_t)plan->level2_blocks), dim3(kThreads), 0, s, a2l);
+  if (hipGetLastError() != hipSuccess) return ZF_EHIP;
+
   FinishArgs af;
-  af.partials = partials;
+  af.partials = partials2;
   af.st = static_cast<DevState*>(args->state);
   af.beta1 = hp->beta1;
   af.beta2 = hp->beta2;
   af.max_norm = hp->max_norm;
-  af.np = plan->pass1_blocks;
+  af.np = plan->level2_blocks;
   af.n_ranks = nr;
   hipLaunchKernelGGL(zf_finish, dim3(1), dim3(kThreads), 0, s, af);
   if (hipGetLastError() != hipSuccess) return ZF_EHIP;
@@ -609,8 +677,7 @@ extern "C" int zf_shard_step(const zf_plan* plan, const zf_hparams* hp,
   a2.lrf = (float)hp->lr;
   a2.ef = (float)hp->eps;
   a2.nr = nr;
-  rc = launch_pass2(nr, args->grad_dtype, args->param_dtype, mat, dim3(pass2_blocks(sm.psi_pad)),
-                    s, a2);
+  rc = launch_pass2(plan, args->grad_dtype, args->param_dtype, s, a2);
   if (rc != ZF_OK) return rc;
   return record(args->phase_events, 3, s);
 }
@@ -630,8 +697,7 @@ extern "C" int zf_reduce_scatter(const zf_plan* plan, int32_t grad_dtype,
   a1.partials = nullptr;
   a1.nr = plan->summary.n_ranks;
   (void)hipGetLastError();
-  return launch_pass1<true, false>(a1.nr, grad_dtype, dim3(plan->pass1_blocks),
-                                   static_cast<hipStream_t>(stream), a1);
+  return launch_pass1<true, false>(plan, grad_dtype, static_cast<hipStream_t>(stream), a1);
 }
 
 extern "C" int zf_gather(const zf_plan* plan, int64_t unit, int32_t dtype,

@@ -75,6 +75,8 @@ class DeviceRun:
             for u in self.plan.units:
                 I.fill_normal16(g, u.L, w.grad_dtype, w.seed, W.grad_stream(step, q), u.lam,
                                 sigma, scale, offset=u.O)
+                if u.P > u.L:  # the padding must be zero (a test may have poisoned it)
+                    g[u.O + u.L:u.O + u.P].zero_()
 
     def inject_inf(self):
         """+inf into the workload's inject replica at its inject index."""

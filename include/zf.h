@@ -175,15 +175,16 @@ typedef struct {
                                  if that is 0) */
   void* state;                /* a state block set up by zf_state_init */
   void* const* phase_events;  /* NULL, or 4 hipEvent_t recorded on `stream`:
-                                 before pass 1, after pass 1, after the
-                                 finishing block, after the update pass */
+                                 before pass 1, after pass 1, after the norm
+                                 reduction and finish, after the update pass */
 } zf_step_args;
 
 /* One emulated step for all N ranks ([L13] 3.1 steps 3-6, 3.2, 3.3; [F6]
- * reduce_grads + step + gather_weights; [MDT] 四.3 order).  Enqueues three
+ * reduce_grads + step + gather_weights; [MDT] 四.3 order).  Enqueues four
  * kernels on `stream` and returns without synchronising:
- *   pass 1  reduce-scatter sums, overflow flag, per-block squared-norm
+ *   pass 1  reduce-scatter sums, overflow flag, per-tile squared-norm
  *           partials (fp64), and the fp32 sums when the plan materialises;
+ *   reduce  fixed contiguous ranges of the partials, in order;
  *   finish  one block: fixed-order total, skip decision, clip coefficient,
  *           bias corrections, next loss scale -> state block;
  *   pass 2  unless skipped: g = sum * f32(coef/(S*N)); AdamW; RNE cast to

@@ -508,7 +508,17 @@ int or_dp_step(int32_t grad_dtype, int32_t param_dtype, int32_t n_ranks, int64_t
  * size without holding the replicas in host memory.  An optional injection
  * overrides one (step, replica, index) with given 16-bit bits.           */
 
-static float regen_acc_one(int32_t dtype, int32_t n_ranks, uint64_t seed, int64_t step,
+#define OR_MAX_REPLICAS 64
+
+/* Starting states of the N gradient streams of `step`. */
+static int grad_states(uint64_t seed, int64_t step, int32_t n_ranks, uint64_t* st) {
+  int32_t q;
+  if (n_ranks < 1 || n_ranks > OR_MAX_REPLICAS) return -1;
+  for (q = 0; q < n_ranks; ++q) st[q] = or_stream_state(seed, grad_stream(step, q));
+  return 0;
+}
+
+static float regen_acc_one(int32_t dtype, int32_t n_ranks, const uint64_t* st, int64_t step,
                            float sf, float kf, int64_t i, const or_inject* inj) {
   float acc = 0.0f;
   int32_t q;
@@ -517,8 +527,7 @@ static float regen_acc_one(int32_t dtype, int32_t n_ranks, uint64_t seed, int64_
     if (inj && inj->step == step && inj->replica == q && inj->index == i) {
       h = inj->bits;
     } else {
-      uint64_t st = or_stream_state(seed, grad_stream(step, q));
-      float x = or_normal_z(st, i) * sf;
+      float x = or_normal_z(st[q], i) * sf;
       x = x * kf;
       h = narrow(dtype, x);
     }
@@ -534,9 +543,11 @@ int or_regen_sumsq(int32_t grad_dtype, int32_t n_ranks, uint64_t seed, int64_t s
   double ss = 0.0;
   int32_t nf = 0;
   float sf = (float)sigma, kf = (float)scale;
-  if (!sumsq || !nonfinite || n_ranks < 1 || i1 < i0) return -1;
+  uint64_t st[OR_MAX_REPLICAS];
+  if (!sumsq || !nonfinite || i1 < i0) return -1;
+  if (grad_states(seed, step, n_ranks, st) != 0) return -1;
   for (i = i0; i < i1; ++i) {
-    float a = regen_acc_one(grad_dtype, n_ranks, seed, step, sf, kf, i, inj);
+    float a = regen_acc_one(grad_dtype, n_ranks, st, step, sf, kf, i, inj);
     if (!isfinite(a)) nf = 1;
     ss += (double)a * (double)a;
   }
@@ -550,8 +561,10 @@ int or_regen_acc(int32_t grad_dtype, int32_t n_ranks, uint64_t seed, int64_t ste
                  float* acc_out) {
   int64_t k;
   float sf = (float)sigma, kf = (float)scale;
-  if (!logical_idx || !acc_out || n_ranks < 1) return -1;
+  uint64_t st[OR_MAX_REPLICAS];
+  if (!logical_idx || !acc_out) return -1;
+  if (grad_states(seed, step, n_ranks, st) != 0) return -1;
   for (k = 0; k < n; ++k)
-    acc_out[k] = regen_acc_one(grad_dtype, n_ranks, seed, step, sf, kf, logical_idx[k], inj);
+    acc_out[k] = regen_acc_one(grad_dtype, n_ranks, st, step, sf, kf, logical_idx[k], inj);
   return 0;
 }
