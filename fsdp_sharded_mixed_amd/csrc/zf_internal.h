@@ -14,17 +14,46 @@ constexpr uint64_t kPlanMagic = 0x7a665f706c616e31ull;  // "zf_plan1"
 // kLevel2Blocks blocks reduces fixed, contiguous ranges of them; a single
 // block finishes.  The tiling depends only on the plan, so the norm's
 // rounding does not depend on the device or the run.
-// Tiling (measured on MI355X): pass 1 streams the N replicas with the
-// non-temporal load hint; two vectors per thread pay off once N >= 4.  The
-// update pass uses plain loads; two vectors per thread pay off on large
-// recomputing plans, one on materialising ones (more, smaller tiles).
+// Tiling (measured on MI355X, in-process A/B over builds):
+//  - pass 1 streams the N replicas with the non-temporal load hint, 2 x 2
+//    quads per thread; with few replicas (N <= 2) it walks the tiles
+//    XCD-contiguously (-9..-13% time), with many it keeps one shared window
+//    (the XCD-contiguous walk costs +5% at N = 8);
+//  - the update pass uses plain loads; 2 x 2 quads per thread on large
+//    recomputing plans, 2 quads otherwise (within 1% either way).
+// Builds may pin a choice for measurement: ZF_FORCE_UNR1, ZF_FORCE_UNR2 (1|2),
+// ZF_FORCE_MAP1 (0|1), ZF_PASS1_NT_LOADS (0|1).
+#ifndef ZF_PASS1_NT_LOADS
+#define ZF_PASS1_NT_LOADS 1
+#endif
 constexpr int kThreads = 256;        // 4 wave64 per block
-constexpr int kVec = 8;              // elements per thread per vector
+constexpr int kQuadsPerUnr = 2;      // quads (4 elements) per thread per tile step
 constexpr int64_t kBigPlan = int64_t(1) << 27;  // padded elements
-inline int unr_pass1(int n_ranks) { return n_ranks >= 4 ? 2 : 1; }
+inline int unr_pass1(int n_ranks) {
+  (void)n_ranks;
+#ifdef ZF_FORCE_UNR1
+  return ZF_FORCE_UNR1;
+#else
+  return 2;
+#endif
+}
+inline int map_pass1(int n_ranks) {
+#ifdef ZF_FORCE_MAP1
+  (void)n_ranks;
+  return ZF_FORCE_MAP1;
+#else
+  return n_ranks <= 2 ? 1 : 0;
+#endif
+}
 inline int unr_pass2(int n_ranks, int64_t psi_pad, bool materialize) {
   (void)n_ranks;
+#ifdef ZF_FORCE_UNR2
+  (void)psi_pad;
+  (void)materialize;
+  return ZF_FORCE_UNR2;
+#else
   return (!materialize && psi_pad >= kBigPlan) ? 2 : 1;
+#endif
 }
 constexpr int kMaxLevel2Blocks = 1024;
 
@@ -34,7 +63,8 @@ struct zf_plan {
   uint64_t magic;
   zf_plan_summary summary;
   std::vector<zf_unit_info> units;
-  int32_t unr1, unr2;           // vectors per thread in pass 1 / pass 2
+  int32_t unr1, unr2;           // tile depth of pass 1 / pass 2 (x2 quads per thread)
+  int32_t pass1_map;            // pass-1 tile walk (0 shared window, 1 XCD-contiguous)
   int64_t pass1_tiles;          // pass-1 blocks = squared-norm partials
   int32_t level2_blocks;        // blocks reducing the partials
   int64_t pass2_tiles;          // update-pass blocks

@@ -108,11 +108,14 @@ extern "C" int zf_plan_flat(const zf_segment* segs, int64_t nseg, int32_t n_rank
   // unless writing and re-reading an fp32 copy (8 bytes) is cheaper.
   s.policy = (2 * n_ranks > 8) ? 1 : 0;
 
-  const int64_t nvec = s.psi_pad / zf::kVec;  // the ragged tail rides on the last tile
+  const int64_t nq = s.psi_pad / 4;  // quads; the ragged tail rides on the last tile
   p->unr1 = zf::unr_pass1(n_ranks);
+  p->pass1_map = zf::map_pass1(n_ranks);
   p->unr2 = zf::unr_pass2(n_ranks, s.psi_pad, s.policy == 1);
-  const int64_t t1 = (nvec + zf::kThreads * p->unr1 - 1) / (zf::kThreads * p->unr1);
-  const int64_t t2 = (nvec + zf::kThreads * p->unr2 - 1) / (zf::kThreads * p->unr2);
+  const int64_t q1 = (int64_t)zf::kThreads * zf::kQuadsPerUnr * p->unr1;
+  const int64_t q2 = (int64_t)zf::kThreads * zf::kQuadsPerUnr * p->unr2;
+  const int64_t t1 = (nq + q1 - 1) / q1;
+  const int64_t t2 = (nq + q2 - 1) / q2;
   p->pass1_tiles = t1 < 1 ? 1 : t1;
   p->pass2_tiles = t2 < 1 ? 1 : t2;
   int64_t l2 = (p->pass1_tiles + zf::kThreads - 1) / zf::kThreads;

@@ -33,7 +33,6 @@
 namespace {
 
 using zf::kThreads;
-using zf::kVec;
 
 // ---------------------------------------------------------------------------
 // Device state block (the caller's zf_state_bytes() buffer).
@@ -61,25 +60,30 @@ struct GradPtrs {
   const uint16_t* p[ZF_MAX_RANKS];
 };
 
-// 16-byte vectors.  Streams that are not read again within the step are
-// stored with the non-temporal hint (global_store ... nt).
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// Element ownership.  A "quad" is 4 consecutive elements: 16 bytes of an
+// fp32 stream, 8 bytes of a 16-bit stream.  A block's tile is 256*Q quads and
+// lane t owns quads tile*256*Q + h*256 + t (h < Q): every load or store
+// instruction of a wave covers one contiguous span (1 KiB of fp32, 512 B of
+// 16-bit values), which keeps whole cache lines per instruction and lets the
+// non-temporal stores go out as full lines.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+constexpr int kQuad = 4;
 
 template <bool NT>
-__device__ __forceinline__ u32x4 ld16(const uint16_t* base, int64_t v) {
-  const u32x4* p = reinterpret_cast<const u32x4*>(base) + v;
+__device__ __forceinline__ u32x2 ldq16(const uint16_t* base, int64_t q) {
+  const u32x2* p = reinterpret_cast<const u32x2*>(base) + q;
   if constexpr (NT) return __builtin_nontemporal_load(p);
   else return *p;
 }
-__device__ __forceinline__ f32x4 ldf(const float* base, int64_t v) {
-  return reinterpret_cast<const f32x4*>(base)[v];
+__device__ __forceinline__ f32x4 ldq32(const float* base, int64_t q) {
+  return reinterpret_cast<const f32x4*>(base)[q];
 }
-__device__ __forceinline__ void stf_nt(float* base, int64_t v, f32x4 x) {
-  __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(base) + v);
+__device__ __forceinline__ void stq32_nt(float* base, int64_t q, f32x4 x) {
+  __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(base) + q);
 }
-__device__ __forceinline__ void st16_nt(void* base, int64_t v, u32x4 x) {
-  __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(base) + v);
+__device__ __forceinline__ void stq16_nt(void* base, int64_t q, u32x2 x) {
+  __builtin_nontemporal_store(x, reinterpret_cast<u32x2*>(base) + q);
 }
 
 // ---------------------------------------------------------------------------
@@ -109,61 +113,72 @@ template <int DT>
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
   return (uint32_t)narrow1<DT>(a) | ((uint32_t)narrow1<DT>(b) << 16);
 }
-
 template <int DT>
-__device__ __forceinline__ void widen8(const u32x4& w, float (&x)[8]) {
-  x[0] = lo16<DT>(w.x); x[1] = hi16<DT>(w.x);
-  x[2] = lo16<DT>(w.y); x[3] = hi16<DT>(w.y);
-  x[4] = lo16<DT>(w.z); x[5] = hi16<DT>(w.z);
-  x[6] = lo16<DT>(w.w); x[7] = hi16<DT>(w.w);
+__device__ __forceinline__ f32x4 widen4(const u32x2& w) {
+  return (f32x4){lo16<DT>(w.x), hi16<DT>(w.x), lo16<DT>(w.y), hi16<DT>(w.y)};
 }
 
 __device__ __forceinline__ bool nonfinite(float x) {
   return (__float_as_uint(x) & 0x7F800000u) == 0x7F800000u;
 }
 
-// Fixed-order sum of the N replicas at vector v (elements 8v .. 8v+7).
-// NR > 0: N known at compile time, all N loads issued before the adds.
+// Tile of this block.  Blocks are dispatched to the 8 XCDs round-robin
+// (block b on XCD b % 8).  map == 0: tile b, so all XCDs share one moving
+// window; map == 1: XCD x walks its own contiguous eighth of the tiles in
+// order (faster for pass 1 with few replicas, slower with many).  Partials
+// are indexed by tile, so the reduction order does not depend on the map.
+__device__ __forceinline__ int64_t tile_of_block(int map) {
+  const int64_t b = blockIdx.x;
+  if (map == 1) {
+    const int64_t G = gridDim.x, m = G / 8, r = G % 8, x = b % 8, k = b / 8;
+    return x * m + (x < r ? x : r) + k;
+  }
+  return b;
+}
+
+// Fixed-order sums of the N replicas over a thread's Q quads.
+// NR > 0: N known at compile time, all N*Q loads issued before the adds.
 // NR == 0: N at run time, in groups of four replicas.
-template <int NR, int DT, bool NT>
-__device__ __forceinline__ void sum8(const GradPtrs& g, int nr, int64_t v, float (&acc)[8]) {
+template <int NR, int DT, bool NT, int Q>
+__device__ __forceinline__ void sum_quads(const GradPtrs& g, int nr, const int64_t (&qi)[Q],
+                                          const bool (&ok)[Q], f32x4 (&acc)[Q]) {
   if constexpr (NR > 0) {
-    u32x4 w[NR];
+    u32x2 w[NR][Q];
 #pragma unroll
-    for (int q = 0; q < NR; ++q) w[q] = ld16<NT>(g.p[q], v);
-    widen8<DT>(w[0], acc);
+    for (int h = 0; h < Q; ++h)
 #pragma unroll
-    for (int q = 1; q < NR; ++q) {
-      float x[8];
-      widen8<DT>(w[q], x);
+      for (int r = 0; r < NR; ++r) w[r][h] = ok[h] ? ldq16<NT>(g.p[r], qi[h]) : (u32x2){0, 0};
 #pragma unroll
-      for (int k = 0; k < 8; ++k) acc[k] = acc[k] + x[k];
+    for (int h = 0; h < Q; ++h) {
+      f32x4 a = widen4<DT>(w[0][h]);
+#pragma unroll
+      for (int r = 1; r < NR; ++r) a = a + widen4<DT>(w[r][h]);
+      acc[h] = a;
     }
   } else {
-    widen8<DT>(ld16<NT>(g.p[0], v), acc);
-    int q = 1;
-    for (; q + 4 <= nr; q += 4) {
-      u32x4 w[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) w[j] = ld16<NT>(g.p[q + j], v);
+    for (int h = 0; h < Q; ++h)
+      acc[h] = widen4<DT>(ok[h] ? ldq16<NT>(g.p[0], qi[h]) : (u32x2){0, 0});
+    int r = 1;
+    for (; r + 4 <= nr; r += 4) {
+      u32x2 w[4][Q];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float x[8];
-        widen8<DT>(w[j], x);
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int k = 0; k < 8; ++k) acc[k] = acc[k] + x[k];
-      }
+        for (int h = 0; h < Q; ++h) w[j][h] = ok[h] ? ldq16<NT>(g.p[r + j], qi[h]) : (u32x2){0, 0};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int h = 0; h < Q; ++h) acc[h] = acc[h] + widen4<DT>(w[j][h]);
     }
-    for (; q < nr; ++q) {
-      float x[8];
-      widen8<DT>(ld16<NT>(g.p[q], v), x);
+    for (; r < nr; ++r)
 #pragma unroll
-      for (int k = 0; k < 8; ++k) acc[k] = acc[k] + x[k];
-    }
+      for (int h = 0; h < Q; ++h)
+        acc[h] = acc[h] + widen4<DT>(ok[h] ? ldq16<NT>(g.p[r], qi[h]) : (u32x2){0, 0});
   }
 }
 
-// Scalar element p (the ragged tail).
+// Scalar element p (the ragged tail of < 4 elements).
 template <int DT>
 __device__ __forceinline__ float sum1(const GradPtrs& g, int nr, int64_t p) {
   float acc = widen1<DT>(g.p[0][p]);
@@ -202,60 +217,61 @@ __device__ __forceinline__ void block_reduce(double& ss, uint32_t& bad) {
 }
 
 // ---------------------------------------------------------------------------
-// Pass 1: reduce-scatter sums, overflow flag and squared-norm partials.
-// Block b owns tile b: vectors [b*256*U, (b+1)*256*U), thread t the
-// vectors b*256*U + u*256 + t (u < U), so each wave reads 1 KiB
-// contiguous from every replica per vector.  The last block also takes the
-// ragged tail (< 8 elements).
+// Pass 1: reduce-scatter sums, overflow flag and squared-norm partials, one
+// tile per block.  The last block also takes the ragged tail (< 4 elements).
 struct Pass1Args {
   GradPtrs g;
   int64_t n;          // Psi'
   float* rs;          // fp32 sums (MAT) or unused
   Partial* partials;  // one per tile (NORM) or unused
   int32_t nr;
+  int32_t tile_map;   // see tile_of_block
 };
 
-template <int NR, int DT, bool MAT, bool NORM, int U>
+template <int NR, int DT, bool MAT, bool NORM, int Q>
 __global__ __launch_bounds__(kThreads) void zf_pass1(Pass1Args a) {
   const int nr = NR > 0 ? NR : a.nr;
-  const int64_t nvec = a.n / kVec;
-  const int64_t v0 = (int64_t)blockIdx.x * kThreads * U + threadIdx.x;
+  const int64_t nq = a.n / kQuad;
+  const int64_t tile = tile_of_block(a.tile_map);
+  const int64_t q0 = tile * kThreads * Q + threadIdx.x;
+  int64_t qi[Q];
+  bool ok[Q];
+#pragma unroll
+  for (int h = 0; h < Q; ++h) {
+    qi[h] = q0 + (int64_t)h * kThreads;
+    ok[h] = qi[h] < nq;
+  }
+  f32x4 acc[Q];
+  sum_quads<NR, DT, ZF_PASS1_NT_LOADS != 0, Q>(a.g, nr, qi, ok, acc);
   double ss = 0.0;
   uint32_t bad = 0;
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int64_t v = v0 + (int64_t)u * kThreads;
-    if (v < nvec) {
-      float acc[8];
-      sum8<NR, DT, true>(a.g, nr, v, acc);
-      if constexpr (MAT) {
-        stf_nt(a.rs, 2 * v, (f32x4){acc[0], acc[1], acc[2], acc[3]});
-        stf_nt(a.rs, 2 * v + 1, (f32x4){acc[4], acc[5], acc[6], acc[7]});
-      }
-      if constexpr (NORM) {
+  for (int h = 0; h < Q; ++h) {
+    if (!ok[h]) continue;
+    if constexpr (MAT) stq32_nt(a.rs, qi[h], acc[h]);
+    if constexpr (NORM) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          bad |= nonfinite(acc[k]) ? 1u : 0u;
-          ss = ss + (double)acc[k] * (double)acc[k];
-        }
+      for (int k = 0; k < 4; ++k) {
+        bad |= nonfinite(acc[h][k]) ? 1u : 0u;
+        ss = ss + (double)acc[h][k] * (double)acc[h][k];
       }
     }
   }
-  const int64_t tail0 = nvec * kVec;
-  if (blockIdx.x == gridDim.x - 1 && (int64_t)threadIdx.x < a.n - tail0) {
+  const int64_t tail0 = nq * kQuad;
+  if (tile == gridDim.x - 1 && (int64_t)threadIdx.x < a.n - tail0) {
     const int64_t p = tail0 + threadIdx.x;
-    const float acc = sum1<DT>(a.g, nr, p);
-    if constexpr (MAT) a.rs[p] = acc;
+    const float t = sum1<DT>(a.g, nr, p);
+    if constexpr (MAT) a.rs[p] = t;
     if constexpr (NORM) {
-      bad |= nonfinite(acc) ? 1u : 0u;
-      ss = ss + (double)acc * (double)acc;
+      bad |= nonfinite(t) ? 1u : 0u;
+      ss = ss + (double)t * (double)t;
     }
   }
   if constexpr (NORM) {
     block_reduce(ss, bad);
     if (threadIdx.x == 0) {
-      a.partials[blockIdx.x].ss = ss;
-      a.partials[blockIdx.x].bad = bad;
+      a.partials[tile].ss = ss;
+      a.partials[tile].bad = bad;
     }
   }
 }
@@ -374,7 +390,7 @@ __device__ __forceinline__ void adamw1(const Coef& c, float acc, float& p, float
   v = vv;
 }
 
-template <int NR, int GDT, int PDT, bool MAT, int U>
+template <int NR, int GDT, int PDT, bool MAT, int Q>
 __global__ __launch_bounds__(kThreads) void zf_pass2(Pass2Args a) {
   if (a.st->skipped) return;  // the whole grid leaves at once
   Coef c;
@@ -384,47 +400,54 @@ __global__ __launch_bounds__(kThreads) void zf_pass2(Pass2Args a) {
   c.dec = a.dec; c.b1 = a.b1; c.c1 = a.c1; c.b2 = a.b2; c.c2 = a.c2;
   c.lrf = a.lrf; c.ef = a.ef;
   const int nr = NR > 0 ? NR : a.nr;
-  const int64_t nvec = a.n / kVec;
-  const int64_t v0 = (int64_t)blockIdx.x * kThreads * U + threadIdx.x;
+  const int64_t nq = a.n / kQuad;
+  const int64_t tile = blockIdx.x;
+  const int64_t q0 = tile * kThreads * Q + threadIdx.x;
+  int64_t qi[Q];
+  bool ok[Q];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int64_t v = v0 + (int64_t)u * kThreads;
-    if (v >= nvec) break;
-    float acc[8];
-    if constexpr (MAT) {
-      const f32x4 r0 = ldf(a.rs, 2 * v), r1 = ldf(a.rs, 2 * v + 1);
-      acc[0] = r0.x; acc[1] = r0.y; acc[2] = r0.z; acc[3] = r0.w;
-      acc[4] = r1.x; acc[5] = r1.y; acc[6] = r1.z; acc[7] = r1.w;
-    } else {
-      sum8<NR, GDT, false>(a.g, nr, v, acc);
-    }
-    const f32x4 p0 = ldf(a.master, 2 * v), p1 = ldf(a.master, 2 * v + 1);
-    const f32x4 m0 = ldf(a.m, 2 * v), m1 = ldf(a.m, 2 * v + 1);
-    const f32x4 w0 = ldf(a.v, 2 * v), w1 = ldf(a.v, 2 * v + 1);
-    float p[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-    float m[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-    float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-    for (int k = 0; k < 8; ++k) adamw1(c, acc[k], p[k], m[k], w[k]);
-    stf_nt(a.master, 2 * v, (f32x4){p[0], p[1], p[2], p[3]});
-    stf_nt(a.master, 2 * v + 1, (f32x4){p[4], p[5], p[6], p[7]});
-    stf_nt(a.m, 2 * v, (f32x4){m[0], m[1], m[2], m[3]});
-    stf_nt(a.m, 2 * v + 1, (f32x4){m[4], m[5], m[6], m[7]});
-    stf_nt(a.v, 2 * v, (f32x4){w[0], w[1], w[2], w[3]});
-    stf_nt(a.v, 2 * v + 1, (f32x4){w[4], w[5], w[6], w[7]});
-    st16_nt(a.out, v, (u32x4){pack2<PDT>(p[0], p[1]), pack2<PDT>(p[2], p[3]),
-                              pack2<PDT>(p[4], p[5]), pack2<PDT>(p[6], p[7])});
+  for (int h = 0; h < Q; ++h) {
+    qi[h] = q0 + (int64_t)h * kThreads;
+    ok[h] = qi[h] < nq;
   }
-  const int64_t tail0 = nvec * kVec;
-  if (blockIdx.x == gridDim.x - 1 && (int64_t)threadIdx.x < a.n - tail0) {
-    const int64_t q = tail0 + threadIdx.x;
-    const float acc = MAT ? a.rs[q] : sum1<GDT>(a.g, nr, q);
-    float p = a.master[q], m = a.m[q], w = a.v[q];
-    adamw1(c, acc, p, m, w);
-    a.master[q] = p;
-    a.m[q] = m;
-    a.v[q] = w;
-    reinterpret_cast<uint16_t*>(a.out)[q] = narrow1<PDT>(p);
+  f32x4 acc[Q], p[Q], m[Q], v[Q];
+  if constexpr (MAT) {
+#pragma unroll
+    for (int h = 0; h < Q; ++h) acc[h] = ok[h] ? ldq32(a.rs, qi[h]) : (f32x4){0, 0, 0, 0};
+  } else {
+    sum_quads<NR, GDT, false, Q>(a.g, nr, qi, ok, acc);
+  }
+#pragma unroll
+  for (int h = 0; h < Q; ++h) {
+    if (ok[h]) {
+      p[h] = ldq32(a.master, qi[h]);
+      m[h] = ldq32(a.m, qi[h]);
+      v[h] = ldq32(a.v, qi[h]);
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < Q; ++h) {
+    if (!ok[h]) continue;
+    float pp[4] = {p[h].x, p[h].y, p[h].z, p[h].w};
+    float mm[4] = {m[h].x, m[h].y, m[h].z, m[h].w};
+    float vv[4] = {v[h].x, v[h].y, v[h].z, v[h].w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) adamw1(c, acc[h][k], pp[k], mm[k], vv[k]);
+    stq32_nt(a.master, qi[h], (f32x4){pp[0], pp[1], pp[2], pp[3]});
+    stq32_nt(a.m, qi[h], (f32x4){mm[0], mm[1], mm[2], mm[3]});
+    stq32_nt(a.v, qi[h], (f32x4){vv[0], vv[1], vv[2], vv[3]});
+    stq16_nt(a.out, qi[h], (u32x2){pack2<PDT>(pp[0], pp[1]), pack2<PDT>(pp[2], pp[3])});
+  }
+  const int64_t tail0 = nq * kQuad;
+  if (tile == gridDim.x - 1 && (int64_t)threadIdx.x < a.n - tail0) {
+    const int64_t e = tail0 + threadIdx.x;
+    const float t = MAT ? a.rs[e] : sum1<GDT>(a.g, nr, e);
+    float pe = a.master[e], me = a.m[e], ve = a.v[e];
+    adamw1(c, t, pe, me, ve);
+    a.master[e] = pe;
+    a.m[e] = me;
+    a.v[e] = ve;
+    reinterpret_cast<uint16_t*>(a.out)[e] = narrow1<PDT>(pe);
   }
 }
 
@@ -507,7 +530,7 @@ int grads_ok(const zf_plan* plan, const void* const* grads, GradPtrs& out) {
 template <bool MAT, bool NORM, int U>
 void launch_pass1_u(int nr, int32_t dt, dim3 grid, hipStream_t s, const Pass1Args& a) {
 #define ZF_P1(NRV, DTV) \
-  hipLaunchKernelGGL((zf_pass1<NRV, DTV, MAT, NORM, U>), grid, dim3(kThreads), 0, s, a)
+  hipLaunchKernelGGL((zf_pass1<NRV, DTV, MAT, NORM, zf::kQuadsPerUnr * U>), grid, dim3(kThreads), 0, s, a)
 #define ZF_P1_DT(NRV) \
   do { if (dt == ZF_BF16) ZF_P1(NRV, ZF_BF16); else ZF_P1(NRV, ZF_F16); } while (0)
   switch (nr) {
@@ -537,11 +560,13 @@ int launch_pass1(const zf_plan* plan, int32_t dt, hipStream_t s, const Pass1Args
 template <int GDT, int PDT, int U>
 void launch_pass2_nr(int nr, bool mat, dim3 grid, hipStream_t s, const Pass2Args& a) {
   if (mat) {
-    hipLaunchKernelGGL((zf_pass2<0, GDT, PDT, true, U>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((zf_pass2<0, GDT, PDT, true, zf::kQuadsPerUnr * U>), grid, dim3(kThreads), 0, s,
+                       a);
     return;
   }
 #define ZF_P2(NRV) \
-  hipLaunchKernelGGL((zf_pass2<NRV, GDT, PDT, false, U>), grid, dim3(kThreads), 0, s, a)
+  hipLaunchKernelGGL((zf_pass2<NRV, GDT, PDT, false, zf::kQuadsPerUnr * U>), grid, dim3(kThreads), 0, s, \
+                     a)
   switch (nr) {
     case 1: ZF_P2(1); break;
     case 2: ZF_P2(2); break;
@@ -614,9 +639,11 @@ extern "C" int zf_shard_step(const zf_plan* plan, const zf_hparams* hp,
     if (!b) return ZF_EINVAL;
     if (!aligned16(b)) return ZF_EALIGN;
   }
+  if (args->numel < sm.psi_pad) return ZF_ESIZE;
   if (sm.workspace_bytes > 0) {
     if (!args->workspace) return ZF_EINVAL;
     if (!aligned16(args->workspace)) return ZF_EALIGN;
+    if (args->workspace_size < sm.workspace_bytes) return ZF_ESIZE;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(args->workspace);
@@ -634,6 +661,7 @@ extern "C" int zf_shard_step(const zf_plan* plan, const zf_hparams* hp,
   a1.rs = rs;
   a1.partials = partials;
   a1.nr = nr;
+  a1.tile_map = plan->pass1_map;
   rc = mat ? launch_pass1<true, true>(plan, args->grad_dtype, s, a1)
            : launch_pass1<false, true>(plan, args->grad_dtype, s, a1);
   if (rc != ZF_OK) return rc;
@@ -683,10 +711,12 @@ extern "C" int zf_shard_step(const zf_plan* plan, const zf_hparams* hp,
 }
 
 extern "C" int zf_reduce_scatter(const zf_plan* plan, int32_t grad_dtype,
-                                 const void* const* grads, float* rs_out, void* stream) {
+                                 const void* const* grads, float* rs_out, int64_t numel,
+                                 void* stream) {
   if (!valid_plan(plan) || !rs_out) return ZF_EINVAL;
   if (!valid_dtype(grad_dtype)) return ZF_EDTYPE;
   if (!aligned16(rs_out)) return ZF_EALIGN;
+  if (numel < plan->summary.psi_pad) return ZF_ESIZE;
   GradPtrs gp;
   int rc = grads_ok(plan, grads, gp);
   if (rc != ZF_OK) return rc;
@@ -696,15 +726,18 @@ extern "C" int zf_reduce_scatter(const zf_plan* plan, int32_t grad_dtype,
   a1.rs = rs_out;
   a1.partials = nullptr;
   a1.nr = plan->summary.n_ranks;
+  a1.tile_map = plan->pass1_map;
   (void)hipGetLastError();
   return launch_pass1<true, false>(plan, grad_dtype, static_cast<hipStream_t>(stream), a1);
 }
 
 extern "C" int zf_gather(const zf_plan* plan, int64_t unit, int32_t dtype,
-                         const void* const* shards, void* unit_buf, void* stream) {
+                         const void* const* shards, void* unit_buf, int64_t unit_buf_numel,
+                         void* stream) {
   if (!valid_plan(plan) || !shards || !unit_buf) return ZF_EINVAL;
   if (!valid_dtype(dtype)) return ZF_EDTYPE;
   if (unit < 0 || unit >= plan->summary.n_units) return ZF_EINVAL;
+  if (unit_buf_numel < plan->units[unit].P) return ZF_ESIZE;
   if ((reinterpret_cast<uintptr_t>(unit_buf) & 1u) != 0) return ZF_EALIGN;
   const int nr = plan->summary.n_ranks;
   GatherArgs a;

@@ -52,8 +52,8 @@ class StepArgs(C.Structure):
     _fields_ = [("grad_dtype", C.c_int32), ("param_dtype", C.c_int32),
                 ("grads", C.POINTER(C.c_void_p)), ("master", C.c_void_p),
                 ("exp_avg", C.c_void_p), ("exp_avg_sq", C.c_void_p), ("params", C.c_void_p),
-                ("workspace", C.c_void_p), ("state", C.c_void_p),
-                ("phase_events", C.POINTER(C.c_void_p))]
+                ("numel", C.c_int64), ("workspace", C.c_void_p), ("workspace_size", C.c_int64),
+                ("state", C.c_void_p), ("phase_events", C.POINTER(C.c_void_p))]
 
 
 class StepResult(C.Structure):
@@ -76,9 +76,9 @@ _SIGNATURES = {
     "zf_shard_step": (C.c_int, [C.c_void_p, C.POINTER(Hparams), C.POINTER(StepArgs),
                                 C.c_void_p]),
     "zf_reduce_scatter": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(C.c_void_p), C.c_void_p,
-                                    C.c_void_p]),
+                                    C.c_int64, C.c_void_p]),
     "zf_gather": (C.c_int, [C.c_void_p, C.c_int64, C.c_int32, C.POINTER(C.c_void_p),
-                            C.c_void_p, C.c_void_p]),
+                            C.c_void_p, C.c_int64, C.c_void_p]),
     "zf_read_result": (C.c_int, [C.c_void_p, C.POINTER(StepResult), C.c_void_p]),
     "zf_strerror": (C.c_char_p, [C.c_int]),
 }
@@ -205,26 +205,42 @@ def hparams(lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, max_norm=1.
     return Hparams(lr, beta1, beta2, eps, weight_decay, max_norm)
 
 
+def _nbytes(t, nbytes):
+    if nbytes is not None:
+        return int(nbytes)
+    return t.numel() * t.element_size() if t is not None else 0
+
+
 def shard_step(plan, hp, grad_dtype, param_dtype, grads, master, exp_avg, exp_avg_sq, params,
-               workspace, state, stream=None, phase_events=None):
+               workspace, state, stream=None, phase_events=None, numel=None,
+               workspace_size=None):
     """zf_shard_step.  grads: N tensors (or addresses); phase_events: None or
-    4 raw hipEvent_t handles."""
+    4 raw hipEvent_t handles.  numel / workspace_size default to the sizes of
+    the tensors passed (the smallest per-element array)."""
     gp = _ptr_array(grads)
     ev = (C.c_void_p * 4)(*phase_events) if phase_events is not None else None
+    if numel is None:
+        numel = min(t.numel() for t in list(grads) + [master, exp_avg, exp_avg_sq, params])
     args = StepArgs(int(grad_dtype), int(param_dtype), gp, _ptr(master), _ptr(exp_avg),
-                    _ptr(exp_avg_sq), _ptr(params), _ptr(workspace), _ptr(state), ev)
+                    _ptr(exp_avg_sq), _ptr(params), int(numel), _ptr(workspace),
+                    _nbytes(workspace, workspace_size), _ptr(state), ev)
     _check(lib.zf_shard_step(_handle(plan), C.byref(hp), C.byref(args), _stream(stream)),
            "zf_shard_step")
 
 
-def reduce_scatter(plan, grad_dtype, grads, rs_out, stream=None):
+def reduce_scatter(plan, grad_dtype, grads, rs_out, stream=None, numel=None):
+    if numel is None:
+        numel = min(t.numel() for t in list(grads) + [rs_out])
     _check(lib.zf_reduce_scatter(_handle(plan), int(grad_dtype), _ptr_array(grads),
-                                 _ptr(rs_out), _stream(stream)), "zf_reduce_scatter")
+                                 _ptr(rs_out), int(numel), _stream(stream)),
+           "zf_reduce_scatter")
 
 
-def gather(plan, unit, dtype, shards, unit_buf, stream=None):
+def gather(plan, unit, dtype, shards, unit_buf, stream=None, unit_buf_numel=None):
+    """zf_gather; unit_buf is a tensor, or an address with unit_buf_numel."""
+    n = unit_buf_numel if unit_buf_numel is not None else unit_buf.numel()
     _check(lib.zf_gather(_handle(plan), int(unit), int(dtype), _ptr_array(shards),
-                         _ptr(unit_buf), _stream(stream)), "zf_gather")
+                         _ptr(unit_buf), int(n), _stream(stream)), "zf_gather")
 
 
 def read_result(state, stream=None):

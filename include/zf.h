@@ -171,8 +171,13 @@ typedef struct {
   float* exp_avg_sq;          /* Psi' fp32 */
   void* params;               /* Psi' 16-bit: stages 0-2 the gathered full
                                  buffer; stage 3 the N resident shards */
-  void* workspace;            /* zf_workspace_bytes(plan) bytes (may be NULL
-                                 if that is 0) */
+  int64_t numel;              /* elements of each per-element array above
+                                 (grads[q], master, exp_avg, exp_avg_sq,
+                                 params); must be >= Psi' */
+  void* workspace;            /* device workspace (may be NULL only if
+                                 zf_workspace_bytes(plan) is 0) */
+  int64_t workspace_size;     /* its size in bytes; must be >=
+                                 zf_workspace_bytes(plan) */
   void* state;                /* a state block set up by zf_state_init */
   void* const* phase_events;  /* NULL, or 4 hipEvent_t recorded on `stream`:
                                  before pass 1, after pass 1, after the norm
@@ -190,15 +195,17 @@ typedef struct {
  *   pass 2  unless skipped: g = sum * f32(coef/(S*N)); AdamW; RNE cast to
  *           param_dtype into params[p].
  * The skip decision and clip coefficient stay on the device.
- * Errors: ZF_EINVAL, ZF_EALIGN, ZF_EDTYPE, ZF_EHIP. */
+ * Errors: ZF_EINVAL, ZF_EALIGN, ZF_EDTYPE, ZF_ESIZE (numel < Psi' or
+ * workspace_size < zf_workspace_bytes(plan)), ZF_EHIP. */
 int zf_shard_step(const zf_plan* plan, const zf_hparams* hp, const zf_step_args* args,
                   void* stream);
 
 /* The reduce-scatter alone ([L13] 3.2; [F7] gradient hook): rs_out[p] is
  * the fixed-order binary32 sum of the N replicas at p, for every p < Psi'
- * (each rank's shard in its padded-flat place).  Errors as zf_shard_step. */
+ * (each rank's shard in its padded-flat place).  numel: elements of every
+ * grads[q] and of rs_out, >= Psi'.  Errors as zf_shard_step. */
 int zf_reduce_scatter(const zf_plan* plan, int32_t grad_dtype, const void* const* grads,
-                      float* rs_out, void* stream);
+                      float* rs_out, int64_t numel, void* stream);
 
 /* ZeRO-3 / FSDP unit gather ([L13] 3.3 and 5.1; [F9] unshard):
  * unit_buf[r*S_u + j] = shards[r][j] for every rank r < N and j < S_u, i.e.
@@ -206,9 +213,11 @@ int zf_reduce_scatter(const zf_plan* plan, int32_t grad_dtype, const void* const
  * unit's padded FlatParameter (P_u elements; the caller reuses one buffer of
  * max_unit_pad elements for every unit).  `shards` is a host array of N
  * device pointers (any 2-byte alignment; with stage-3 zf_shard_step output
- * they are params + O_u + r*S_u).  Errors: ZF_EINVAL, ZF_EDTYPE, ZF_EHIP. */
+ * they are params + O_u + r*S_u), each of S_u elements.  unit_buf_numel:
+ * elements of unit_buf, >= P_u.  Errors: ZF_EINVAL, ZF_EALIGN, ZF_EDTYPE,
+ * ZF_ESIZE, ZF_EHIP. */
 int zf_gather(const zf_plan* plan, int64_t unit, int32_t dtype, const void* const* shards,
-              void* unit_buf, void* stream);
+              void* unit_buf, int64_t unit_buf_numel, void* stream);
 
 typedef struct {
   int32_t overflow;     /* a reduced gradient was inf or NaN */

@@ -139,13 +139,16 @@ def test_step_argument_errors_enqueue_nothing(zf):
     ok = 0x10000
     grads = (C.c_void_p * 2)(ok, ok)
 
+    need = Z.workspace_bytes(plan)
+
     def args(**kw):
         d = dict(grad_dtype=1, param_dtype=1, grads=grads, master=ok, exp_avg=ok, exp_avg_sq=ok,
-                 params=ok, workspace=ok, state=ok, phase_events=None)
+                 params=ok, numel=100, workspace=ok, workspace_size=need, state=ok,
+                 phase_events=None)
         d.update(kw)
         return Z.StepArgs(d["grad_dtype"], d["param_dtype"], d["grads"], d["master"],
-                          d["exp_avg"], d["exp_avg_sq"], d["params"], d["workspace"],
-                          d["state"], d["phase_events"])
+                          d["exp_avg"], d["exp_avg_sq"], d["params"], d["numel"],
+                          d["workspace"], d["workspace_size"], d["state"], d["phase_events"])
 
     step = lambda a, p=plan.handle, h=hp: Z.lib.zf_shard_step(p, C.byref(h), C.byref(a), None)
     assert step(args(), p=None) == -1
@@ -158,16 +161,21 @@ def test_step_argument_errors_enqueue_nothing(zf):
     assert step(args(grads=(C.c_void_p * 2)(ok, ok + 2))) == -2
     assert step(args(state=None)) == -1
     assert step(args(workspace=None)) == -1
+    # sizes: a short workspace or short arrays are rejected before any launch
+    assert step(args(workspace_size=need - 1)) == -4
+    assert step(args(numel=99)) == -4
     assert step(args(), h=Z.hparams(1e-3, beta1=1.0)) == -1
     assert Z.lib.zf_shard_step(plan.handle, None, C.byref(args()), None) == -1
-    assert Z.lib.zf_reduce_scatter(plan.handle, 9, grads, ok, None) == -3
-    assert Z.lib.zf_reduce_scatter(plan.handle, 1, grads, ok + 4, None) == -2
-    assert Z.lib.zf_reduce_scatter(plan.handle, 1, None, ok, None) == -1
+    assert Z.lib.zf_reduce_scatter(plan.handle, 9, grads, ok, 100, None) == -3
+    assert Z.lib.zf_reduce_scatter(plan.handle, 1, grads, ok + 4, 100, None) == -2
+    assert Z.lib.zf_reduce_scatter(plan.handle, 1, None, ok, 100, None) == -1
+    assert Z.lib.zf_reduce_scatter(plan.handle, 1, grads, ok, 99, None) == -4
     shards = (C.c_void_p * 2)(ok, ok)
-    assert Z.lib.zf_gather(plan.handle, 1, 1, shards, ok, None) == -1
-    assert Z.lib.zf_gather(plan.handle, 0, 5, shards, ok, None) == -3
-    assert Z.lib.zf_gather(plan.handle, 0, 1, (C.c_void_p * 2)(ok, ok + 1), ok, None) == -2
-    assert Z.lib.zf_gather(plan.handle, 0, 1, shards, None, None) == -1
+    assert Z.lib.zf_gather(plan.handle, 1, 1, shards, ok, 100, None) == -1
+    assert Z.lib.zf_gather(plan.handle, 0, 5, shards, ok, 100, None) == -3
+    assert Z.lib.zf_gather(plan.handle, 0, 1, (C.c_void_p * 2)(ok, ok + 1), ok, 100, None) == -2
+    assert Z.lib.zf_gather(plan.handle, 0, 1, shards, None, 100, None) == -1
+    assert Z.lib.zf_gather(plan.handle, 0, 1, shards, ok, 99, None) == -4
     assert Z.lib.zf_state_init(None, 1.0, 0, 10, None) == -1
     assert Z.lib.zf_state_init(ok, 0.0, 0, 10, None) == -1
     assert Z.lib.zf_state_init(ok + 4, 1.0, 0, 10, None) == -2

@@ -309,7 +309,8 @@ def test_gather_misaligned_shards(R):
         base = src.data_ptr()
         ptrs = [base + 2 * (offs[r] + r * S) for r in range(n)]
         for dst_off in (0, 1):
-            zf.gather(plan, 1, W.BF16, ptrs, buf.data_ptr() + 2 * dst_off)
+            zf.gather(plan, 1, W.BF16, ptrs, buf.data_ptr() + 2 * dst_off,
+                      unit_buf_numel=buf.numel() - dst_off)
             got = buf.cpu().numpy().view(np.uint16)[dst_off:dst_off + info.P]
             want = np.concatenate([host[offs[r] + r * S:offs[r] + (r + 1) * S]
                                    for r in range(n)])
