@@ -46,14 +46,19 @@ def update_kernel_bytes_per_elem(w, materialized):
 
 
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCE = os.path.join(ROOT, "fsdp_sharded_mixed_amd", "csrc", "zf_step.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "fsdp_sharded_mixed_amd", "csrc", f)
+                  for f in ("zf_step.hip", "zf_internal.h", "zf_plan.cpp")]
 COPY_BYTES = 1 << 30  # calibration copy: 1 GiB read + 1 GiB written
 
 
 def kernel_source_hash():
+    """Fingerprint of the step library's sources (kernels, tiling, planner)."""
     import hashlib
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_for(workload):
@@ -206,13 +211,21 @@ def main():
     torch.cuda.set_device(0)
     print(f"bench: {w.name} Psi={w.psi:,} N={w.n_ranks} stage={w.stage}", file=sys.stderr,
           flush=True)
-    if args.calibrate_copy:
-        src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda:0")
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    # this box's plain device-copy bandwidth (1 GiB read + 1 GiB written),
+    # the practical ceiling the step's streams are compared against
+    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3 if args.calibrate_copy else 2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * COPY_BYTES * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
     dev = runner.DeviceRun(w, device="cuda:0")
     dev.init_state()
     dev.fill_grads(1, w.loss_scale)
@@ -286,6 +299,7 @@ def main():
         "params_updated_per_s": round(w.psi / (ms * 1e-3), 1),
         "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
         "wall_ms_per_step": round(1e3 * wall / args.steps, 5),
+        "device_copy_gbs": round(copy_gbs, 1),
         "kernels_ms": {"pass1_rs_norm": round(p1, 5), "finish": round(fin, 5),
                        "pass2_update": round(p2, 5)},
         "roofline": {"bound": "hbm", "achieved": round(upd_gbs, 2), "peak": PEAK_HBM_GBS,

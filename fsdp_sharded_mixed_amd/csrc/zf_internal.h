@@ -14,13 +14,14 @@ constexpr uint64_t kPlanMagic = 0x7a665f706c616e31ull;  // "zf_plan1"
 // kLevel2Blocks blocks reduces fixed, contiguous ranges of them; a single
 // block finishes.  The tiling depends only on the plan, so the norm's
 // rounding does not depend on the device or the run.
-// Tiling (measured on MI355X, in-process A/B over builds):
-//  - pass 1 streams the N replicas with the non-temporal load hint, 2 x 2
-//    quads per thread; with few replicas (N <= 2) it walks the tiles
-//    XCD-contiguously (-9..-13% time), with many it keeps one shared window
-//    (the XCD-contiguous walk costs +5% at N = 8);
-//  - the update pass uses plain loads; 2 x 2 quads per thread on large
-//    recomputing plans, 2 quads otherwise (within 1% either way).
+// Tiling (measured on MI355X, in-process A/B over builds on one box):
+//  - pass 1 streams the N replicas with the non-temporal load hint.  With
+//    N <= 4 it walks the tiles XCD-contiguously (N = 2: -6%, 3: -5%,
+//    4: -5%); at N = 8 that walk costs +4%, so many replicas keep one
+//    shared window.  One 2-quad step per thread for N <= 2 (-6% at 4.06B),
+//    two steps otherwise;
+//  - the update pass uses plain loads; two 2-quad steps per thread on large
+//    recomputing plans, one otherwise (within 1% either way).
 // Builds may pin a choice for measurement: ZF_FORCE_UNR1, ZF_FORCE_UNR2 (1|2),
 // ZF_FORCE_MAP1 (0|1), ZF_PASS1_NT_LOADS (0|1).
 #ifndef ZF_PASS1_NT_LOADS
@@ -30,11 +31,11 @@ constexpr int kThreads = 256;        // 4 wave64 per block
 constexpr int kQuadsPerUnr = 2;      // quads (4 elements) per thread per tile step
 constexpr int64_t kBigPlan = int64_t(1) << 27;  // padded elements
 inline int unr_pass1(int n_ranks) {
-  (void)n_ranks;
 #ifdef ZF_FORCE_UNR1
+  (void)n_ranks;
   return ZF_FORCE_UNR1;
 #else
-  return 2;
+  return n_ranks <= 2 ? 1 : 2;
 #endif
 }
 inline int map_pass1(int n_ranks) {
@@ -42,7 +43,7 @@ inline int map_pass1(int n_ranks) {
   (void)n_ranks;
   return ZF_FORCE_MAP1;
 #else
-  return n_ranks <= 2 ? 1 : 0;
+  return n_ranks <= 4 ? 1 : 0;
 #endif
 }
 inline int unr_pass2(int n_ranks, int64_t psi_pad, bool materialize) {
