@@ -1,0 +1,86 @@
+"""The oracle's pins catch plausible mistakes.
+
+Each case plants one mistake in a copy of oracle/zf_oracle.c (a dropped
+term, a wrong sign or index, a transposed operand, an off-by-one), builds
+it into a temporary library and runs the pin suite against it
+(tests/test_oracle_pins.py, via ZF_ORACLE_LIB).  The suite must fail.
+CPU only; the shipped oracle is never modified.
+"""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+from oracle import build as ob
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "zf_oracle.c")
+HDR = os.path.join(ROOT, "oracle", "zf_oracle.h")
+
+# (name, text in zf_oracle.c, replacement)
+MUTANTS = [
+    ("bf16 rounding loses ties-to-even",
+     "u += 0x7FFFu + ((u >> 16) & 1u);", "u += 0x7FFFu;"),
+    ("fp16 rounding rounds half up",
+     "if (rem > 0x1000u || (rem == 0x1000u && (q & 1u))) q += 1u;",
+     "if (rem >= 0x1000u) q += 1u;"),
+    ("fp16 subnormal shift off by one",
+     "shift = -(e + 1);", "shift = -e;"),
+    ("reduce-scatter starts from the last replica",
+     "float acc = widen(grad_dtype, grads[0][p]);\n"
+     "        for (q = 1; q < n_ranks; ++q) acc = acc + widen(grad_dtype, grads[q][p]);",
+     "float acc = widen(grad_dtype, grads[n_ranks - 1][p]);\n"
+     "        for (q = 0; q < n_ranks - 1; ++q) acc = acc + widen(grad_dtype, grads[q][p]);"),
+    ("epsilon inside the square root",
+     "float d = sqrtf(vv / sc->bc2) + sc->ef;", "float d = sqrtf(vv / sc->bc2 + sc->ef);"),
+    ("first moment not bias-corrected",
+     "float mh = mm / sc->bc1;", "float mh = mm;"),
+    ("weight decay dropped",
+     "float pp = p[i] * sc->dec;", "float pp = p[i];"),
+    ("update added instead of subtracted",
+     "pp = pp - sc->lrf * (mh / d);", "pp = pp + sc->lrf * (mh / d);"),
+    ("second moment uses g instead of g*g",
+     "float vv = sc->b2 * v[i] + sc->c2 * (g * g);", "float vv = sc->b2 * v[i] + sc->c2 * g;"),
+    ("clip coefficient without the 1e-6",
+     "coef = hp->max_norm / (norm + 1e-6);", "coef = hp->max_norm / norm;"),
+    ("norm not averaged over ranks",
+     "norm = sqrt(sumsq) / (S * (double)n_ranks);", "norm = sqrt(sumsq) / S;"),
+    ("bias-correction power off by one",
+     "for (i = 1; i < st->t; ++i) {", "for (i = 0; i < st->t; ++i) {"),
+    ("loss scale not halved on overflow",
+     "st->loss_scale = st->loss_scale * 0.5;", "st->loss_scale = st->loss_scale;"),
+    ("skipped step still counts",
+     "    res->scale_next = st->loss_scale;\n    res->t = st->t;\n    return 0;\n  }",
+     "    res->scale_next = st->loss_scale;\n    st->t += 1;\n    res->t = st->t;\n    return 0;\n  }"),
+    ("padding rounds up one shard too many",
+     "u->P = ((u->L + n_ranks - 1) / n_ranks) * n_ranks;", "u->P = (u->L / n_ranks + 1) * n_ranks;"),
+    ("stage-2 ledger keeps full gradients",
+     "case 2: *after_backward_bytes = 2 * psi_pad + 2 * s_tot + 12 * s_tot; break;",
+     "case 2: *after_backward_bytes = 2 * psi_pad + 2 * psi_pad + 12 * s_tot; break;"),
+    ("unit gather transposes rank and offset",
+     "unit_buf[(int64_t)r * units[u].S + j] = param_shards[r][units[u].M + j];",
+     "unit_buf[j * n_ranks + r] = param_shards[r][units[u].M + j];"),
+    ("Irwin-Hall centred on the wrong mean",
+     "return (float)(sum - 393210) / 65536.0f;", "return (float)(sum - 393216) / 65536.0f;"),
+    ("ring traffic without the (N-1)/N factor",
+     "return passes * ((double)(n_ranks - 1) / (double)n_ranks) * 2.0 * (double)psi_pad;",
+     "return passes * 2.0 * (double)psi_pad;"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site not found once: {name}"
+    (tmp_path / "zf_oracle.c").write_text(src.replace(old, new))
+    shutil.copy(HDR, tmp_path / "zf_oracle.h")
+    lib = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", *ob.CFLAGS, "-o", str(lib), str(tmp_path / "zf_oracle.c"), "-lm"],
+                   check=True)
+    env = dict(os.environ, ZF_ORACLE_LIB=str(lib))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"the pins did not catch: {name}\n{r.stdout[-2000:]}"

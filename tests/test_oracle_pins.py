@@ -168,6 +168,25 @@ def test_irwin_hall_normal(orc):
     assert not np.array_equal(O.gen32(100, 7, 6, 1000, 0.5), a)
 
 
+def test_generator_structure_exact(orc):
+    """Exact structure of the draws, from the published generator's outputs
+    (pinned above): a stream's starting state is output number `stream` of
+    the generator seeded with `seed`; element i uses outputs 3i, 3i+1, 3i+2
+    of the generator started there, as twelve 16-bit words, and the word sum
+    minus its exact mean 12 * 65535/2 = 393210, over 65536, is z."""
+    import ctypes as C
+    for seed in (0, 99, 2**64 - 5):
+        outs = O.splitmix64_outputs(seed, 6)
+        for k in range(6):
+            assert O.lib().or_stream_state(seed, k) == outs[k]
+        st = O.lib().or_stream_state(seed, 4)
+        state = C.c_uint64(st)
+        words = [O.lib().or_splitmix64_next(C.byref(state)) for _ in range(3 * 40)]
+        for i in range(40):
+            tot = sum((w >> (16 * h)) & 0xFFFF for w in words[3 * i:3 * i + 3] for h in range(4))
+            assert O.lib().or_normal_z(st, i) == (tot - 12 * 65535 / 2) / 65536
+
+
 def test_gen16_is_rne_of_scaled_normal(orc):
     """A 16-bit draw is the binary32 product z*sigma*scale rounded to nearest
     even: checked against numpy's float32 arithmetic and float16 cast, and
