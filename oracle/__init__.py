@@ -84,6 +84,12 @@ def lib():
             "or_layout": (C.c_int, [vp, vp, i64, i32, i32, vp, i64, C.POINTER(i64),
                                     C.POINTER(i64), C.POINTER(i64)]),
             "or_ledger": (C.c_int, [vp, i64, i32, i32, C.POINTER(i64), C.POINTER(i64)]),
+            "or_layout_dim0": (C.c_int, [vp, vp, i64, i32, vp, i64, C.POINTER(i64),
+                                         C.POINTER(i64), C.POINTER(i64)]),
+            "or_fsdp2_step": (C.c_int, [i32, i32, vp, i64, vp, vp, vp, vp, vp,
+                                        C.POINTER(Hparams), C.POINTER(ScaleState),
+                                        C.POINTER(Result)]),
+            "or_fsdp2_gather": (C.c_int, [vp, i64, i32, i64, i64, i32, vp, vp]),
             "or_comm_bytes": (dbl, [i64, i32, i32]),
             "or_reduce_scatter": (C.c_int, [i32, i32, vp, i64, vp, vp]),
             "or_finish": (C.c_int, [dbl, i32, i32, C.POINTER(Hparams), C.POINTER(ScaleState),
@@ -178,6 +184,38 @@ def layout(seg_numel, seg_unit, n_ranks, mode):
                          len(units), C.byref(nu), C.byref(psi), C.byref(psi_pad))
     _check(rc, "layout")
     return units[: nu.value].copy(), psi.value, psi_pad.value
+
+
+def layout_dim0(seg_numel, seg_rows, n_ranks):
+    """FSDP2 per-parameter dim-0 layout: (units, psi, psi_pad)."""
+    seg_numel = np.ascontiguousarray(seg_numel, np.int64)
+    seg_rows = np.ascontiguousarray(seg_rows, np.int64)
+    units = np.zeros(max(1, len(seg_numel)), UNIT_DTYPE)
+    nu, psi, psi_pad = C.c_int64(), C.c_int64(), C.c_int64()
+    rc = lib().or_layout_dim0(_p(seg_numel), _p(seg_rows), len(seg_numel), n_ranks, _p(units),
+                              len(units), C.byref(nu), C.byref(psi), C.byref(psi_pad))
+    _check(rc, "layout_dim0")
+    return units[: nu.value].copy(), psi.value, psi_pad.value
+
+
+def fsdp2_step(grad_dtype, n_ranks, units, grads, master, exp_avg, exp_avg_sq, grad_shards, hp,
+               st):
+    units = np.ascontiguousarray(units, UNIT_DTYPE)
+    grads = [np.ascontiguousarray(g, np.uint16) for g in grads]
+    res = Result()
+    _check(lib().or_fsdp2_step(grad_dtype, n_ranks, _p(units), len(units), _ptrs(grads),
+                               _ptrs(master), _ptrs(exp_avg), _ptrs(exp_avg_sq),
+                               _ptrs(grad_shards), C.byref(hp), C.byref(st), C.byref(res)),
+           "fsdp2_step")
+    return res
+
+
+def fsdp2_gather(units, n_ranks, first, count, dtype, master):
+    units = np.ascontiguousarray(units, UNIT_DTYPE)
+    out = np.empty(int(units[first:first + count]["L"].sum()), np.uint16)
+    _check(lib().or_fsdp2_gather(_p(units), len(units), n_ranks, first, count, dtype,
+                                 _ptrs(master), _p(out)), "fsdp2_gather")
+    return out
 
 
 def ledger(units, n_ranks, stage):

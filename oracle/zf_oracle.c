@@ -201,6 +201,40 @@ int or_layout(const int64_t* seg_numel, const int32_t* seg_unit, int64_t nseg, i
   return 0;
 }
 
+/* FSDP2 ([MDT] 五.4, 五.6, 六.2): every parameter is its own shard unit,
+ * cut along dim 0 into N chunks of ceil(R/N) rows (torch.chunk: the last
+ * chunks may be short or empty), each rank's chunk padded with zero rows to
+ * ceil(R/N) rows.  In the padded flat the parameter then takes
+ * P = N*ceil(R/N)*C elements (C = numel/R), rank r owning [r*S, (r+1)*S)
+ * with S = ceil(R/N)*C. */
+int or_layout_dim0(const int64_t* seg_numel, const int64_t* seg_rows, int64_t nseg,
+                   int32_t n_ranks, or_unit* units_out, int64_t max_units, int64_t* n_units_out,
+                   int64_t* psi_out, int64_t* psi_pad_out) {
+  int64_t s, O = 0, lam = 0, M = 0;
+  if (n_ranks < 1 || nseg < 1 || !seg_numel || !units_out || nseg > max_units) return -1;
+  for (s = 0; s < nseg; ++s) {
+    int64_t R = (seg_rows && seg_rows[s] > 0) ? seg_rows[s] : seg_numel[s];
+    int64_t C, c;
+    or_unit* u = &units_out[s];
+    if (seg_numel[s] < 1 || seg_numel[s] % R != 0) return -1;
+    C = seg_numel[s] / R;
+    c = (R + n_ranks - 1) / n_ranks;
+    u->L = seg_numel[s];
+    u->P = (int64_t)n_ranks * c * C;
+    u->S = c * C;
+    u->O = O;
+    u->lam = lam;
+    u->M = M;
+    O += u->P;
+    lam += u->L;
+    M += u->S;
+  }
+  *n_units_out = nseg;
+  *psi_out = lam;
+  *psi_pad_out = O;
+  return 0;
+}
+
 /* Bytes of model state one rank holds once backward has finished ([L13] 2.3
  * and 3.5, and its summary): stage 0 (plain DP) 2+2+12 bytes per parameter;
  * stage 1 full 16-bit params and grads plus its 1/N of the fp32
@@ -215,7 +249,7 @@ int or_layout(const int64_t* seg_numel, const int32_t* seg_unit, int64_t nseg, i
 int or_ledger(const or_unit* units, int64_t n_units, int32_t n_ranks, int32_t stage,
               int64_t* after_backward_bytes, int64_t* peak_bytes) {
   int64_t psi = 0, psi_pad = 0, s_tot = 0, u, b;
-  if (!units || n_units < 1 || n_ranks < 1 || stage < 0 || stage > 3) return -1;
+  if (!units || n_units < 1 || n_ranks < 1 || stage < 0 || stage > 4) return -1;
   for (u = 0; u < n_units; ++u) {
     psi += units[u].L;
     psi_pad += units[u].P;
@@ -225,7 +259,13 @@ int or_ledger(const or_unit* units, int64_t n_units, int32_t n_ranks, int32_t st
     case 0: *after_backward_bytes = 2 * psi + 2 * psi + 12 * psi; break;
     case 1: *after_backward_bytes = 2 * psi_pad + 2 * psi_pad + 12 * s_tot; break;
     case 2: *after_backward_bytes = 2 * psi_pad + 2 * s_tot + 12 * s_tot; break;
-    default: *after_backward_bytes = 2 * s_tot + 2 * s_tot + 12 * s_tot; break;
+    case 3: *after_backward_bytes = 2 * s_tot + 2 * s_tot + 12 * s_tot; break;
+    default:
+      /* FSDP2 with fp32 parameters: the fp32 shard is the parameter and the
+       * master; fp32 grad shard; m and v -- 4 + 4 + 8 bytes per element
+       * ([MDT] 五.6) */
+      *after_backward_bytes = 4 * s_tot + 4 * s_tot + 8 * s_tot;
+      break;
   }
   *peak_bytes = *after_backward_bytes;
   if (stage == 3) {
@@ -466,6 +506,64 @@ int or_gather_unit(const or_unit* units, int64_t n_units, int32_t n_ranks, int64
   for (r = 0; r < n_ranks; ++r)
     for (j = 0; j < units[u].S; ++j)
       unit_buf[(int64_t)r * units[u].S + j] = param_shards[r][units[u].M + j];
+  return 0;
+}
+
+/* One FSDP2 step for all N ranks ([MDT] 五.4 and 五.6): the reduce-scatter in
+ * fp32 writes each rank's fp32 gradient shard (kept, as the shard's .grad);
+ * overflow, norm and clip as in or_zero_step; AdamW updates the fp32 shard,
+ * which is itself the parameter, so the step writes no 16-bit copy -- the
+ * 16-bit values appear only when a unit is gathered (or_fsdp2_gather).
+ * Buffers are per-rank shard buffers (sum_u S_u elements, unit u at M_u). */
+int or_fsdp2_step(int32_t grad_dtype, int32_t n_ranks, const or_unit* units, int64_t n_units,
+                  const uint16_t* const* grads, float* const* master, float* const* exp_avg,
+                  float* const* exp_avg_sq, float* const* grad_shards, const or_hparams* hp,
+                  or_scale_state* st, or_result* res) {
+  int64_t s_tot = 0, u, j, k;
+  int32_t r, overflow = 0;
+  double ss = 0.0;
+  or_scalars sc;
+  if (!units || n_units < 1 || !grads || !master || !exp_avg || !exp_avg_sq || !grad_shards ||
+      !hp || !st || !res)
+    return -1;
+  for (u = 0; u < n_units; ++u) s_tot += units[u].S;
+  or_reduce_scatter(grad_dtype, n_ranks, units, n_units, grads, grad_shards);
+  for (r = 0; r < n_ranks; ++r)
+    for (k = 0; k < s_tot; ++k)
+      if (!isfinite(grad_shards[r][k])) overflow = 1;
+  for (u = 0; u < n_units; ++u) {
+    const or_unit* U = &units[u];
+    for (r = 0; r < n_ranks; ++r)
+      for (j = 0; j < U->S; ++j) {
+        if ((int64_t)r * U->S + j >= U->L) continue;  /* padding */
+        ss += (double)grad_shards[r][U->M + j] * (double)grad_shards[r][U->M + j];
+      }
+  }
+  or_finish(ss, overflow, n_ranks, hp, st, &sc, res);
+  if (res->skipped) return 0;
+  for (r = 0; r < n_ranks; ++r)
+    or_adamw_array(s_tot, grad_shards[r], &sc, master[r], exp_avg[r], exp_avg_sq[r]);
+  return 0;
+}
+
+/* FSDP2 unshard of one group of parameters (units first .. first+count-1)
+ * before it is used ([MDT] 五.4: each rank's fp32 shards are cast to the
+ * parameter dtype, all-gathered, then copied out into each parameter's
+ * full tensor): out holds the group's parameters end to end, unpadded, in
+ * order; element e of parameter u comes from rank e / S_u, offset e % S_u. */
+int or_fsdp2_gather(const or_unit* units, int64_t n_units, int32_t n_ranks, int64_t first,
+                    int64_t count, int32_t dtype, const float* const* master, uint16_t* out) {
+  int64_t i, e, pos = 0;
+  if (!units || !master || !out || first < 0 || count < 1 || first + count > n_units) return -1;
+  for (i = first; i < first + count; ++i) {
+    const or_unit* U = &units[i];
+    for (e = 0; e < U->L; ++e) {
+      int64_t r = e / U->S, j = e % U->S;
+      if (r >= n_ranks) return -1;
+      out[pos + e] = narrow(dtype, master[r][U->M + j]);
+    }
+    pos += U->L;
+  }
   return 0;
 }
 

@@ -22,7 +22,10 @@
  *  [F9]   Femtotron dev log #9: ZeRO-3 unshard into a padded full buffer.
  *  [MDT]  Megatron / DeepSpeed / torchtitan architecture and source guide,
  *         ch. 四.3 (DeepSpeed stage 1/2 flat partitions; "check overflow ->
- *         clip -> step") and ch. 五.7 (gradient-norm clipping in train_step).
+ *         clip -> step"), 五.4 and 五.6 (FSDP2: per-parameter dim-0 shards,
+ *         fp32 shard is the parameter, cast at all-gather time, fp32
+ *         reduce-scatter), 六.2 (Stage 3 vs FSDP1 vs FSDP2) and 五.7
+ *         (gradient-norm clipping in train_step).
  *
  * Where the pages leave a step open, the reading taken is stated at the
  * function that takes it.  Parity status: every function is pinned by a
@@ -97,6 +100,11 @@ int or_layout(const int64_t* seg_numel, const int32_t* seg_unit, int64_t nseg, i
               int64_t* psi_out, int64_t* psi_pad_out);
 int or_ledger(const or_unit* units, int64_t n_units, int32_t n_ranks, int32_t stage,
               int64_t* after_backward_bytes, int64_t* peak_bytes);
+/* FSDP2 per-parameter dim-0 sharding: one unit per parameter, padded to a
+ * multiple of N rows (rows[s] <= 0 means a 1-D parameter). */
+int or_layout_dim0(const int64_t* seg_numel, const int64_t* seg_rows, int64_t nseg,
+                   int32_t n_ranks, or_unit* units_out, int64_t max_units, int64_t* n_units_out,
+                   int64_t* psi_out, int64_t* psi_pad_out);
 double or_comm_bytes(int64_t psi_pad, int32_t n_ranks, int32_t variant);
 
 /* ---- the step ------------------------------------------------------------ */
@@ -112,6 +120,12 @@ int or_zero_step(int32_t grad_dtype, int32_t param_dtype, int32_t n_ranks, const
                  or_scale_state* st, or_result* res);
 int or_gather_unit(const or_unit* units, int64_t n_units, int32_t n_ranks, int64_t u,
                    const uint16_t* const* param_shards, uint16_t* unit_buf);
+int or_fsdp2_step(int32_t grad_dtype, int32_t n_ranks, const or_unit* units, int64_t n_units,
+                  const uint16_t* const* grads, float* const* master, float* const* exp_avg,
+                  float* const* exp_avg_sq, float* const* grad_shards, const or_hparams* hp,
+                  or_scale_state* st, or_result* res);
+int or_fsdp2_gather(const or_unit* units, int64_t n_units, int32_t n_ranks, int64_t first,
+                    int64_t count, int32_t dtype, const float* const* master, uint16_t* out);
 int or_dp_step(int32_t grad_dtype, int32_t param_dtype, int32_t n_ranks, int64_t psi,
                const uint16_t* const* grads, float* master, float* exp_avg, float* exp_avg_sq,
                uint16_t* params, const or_hparams* hp, or_scale_state* st, or_result* res);

@@ -64,6 +64,16 @@ MUTANTS = [
      "unit_buf[j * n_ranks + r] = param_shards[r][units[u].M + j];"),
     ("Irwin-Hall centred on the wrong mean",
      "return (float)(sum - 393210) / 65536.0f;", "return (float)(sum - 393216) / 65536.0f;"),
+    ("FSDP2 chunk rows rounded the wrong way",
+     "c = (R + n_ranks - 1) / n_ranks;", "c = R / n_ranks + 1;"),
+    ("FSDP2 gather transposes rank and offset",
+     "int64_t r = e / U->S, j = e % U->S;", "int64_t r = e % n_ranks, j = e / n_ranks;"),
+    ("FSDP2 update reads rank 0's gradient shard on every rank",
+     "or_adamw_array(s_tot, grad_shards[r], &sc, master[r], exp_avg[r], exp_avg_sq[r]);",
+     "or_adamw_array(s_tot, grad_shards[0], &sc, master[r], exp_avg[r], exp_avg_sq[r]);"),
+    ("FSDP2 ledger counts a 16-bit parameter copy",
+     "*after_backward_bytes = 4 * s_tot + 4 * s_tot + 8 * s_tot;",
+     "*after_backward_bytes = 2 * s_tot + 4 * s_tot + 4 * s_tot + 8 * s_tot;"),
     ("ring traffic without the (N-1)/N factor",
      "return passes * ((double)(n_ranks - 1) / (double)n_ranks) * 2.0 * (double)psi_pad;",
      "return passes * 2.0 * (double)psi_pad;"),

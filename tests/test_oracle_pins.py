@@ -564,3 +564,102 @@ def test_tiny_workload_trajectory(orc):
         assert res.skipped == 0 and res.coef == 1.0
         assert res.norm == pytest.approx(1e-3 * math.sqrt(32656 / 4), rel=0.03)
     assert run.st.t == 10 and run.st.loss_scale == 65536.0
+
+
+# ------------------------------------------------------------------ FSDP2 ----
+def test_fsdp2_chunks_match_torch_chunk(orc):
+    """[MDT] 五.4: FSDP2 cuts each parameter along dim 0 into N pieces the way
+    torch.chunk does (ceil(R/N) rows each, the last ones short or empty);
+    each rank's real rows must equal torch.chunk's sizes."""
+    import torch
+    rng = np.random.default_rng(8)
+    for _ in range(200):
+        n = int(rng.integers(1, 9))
+        R = int(rng.integers(1, 40))
+        Cc = int(rng.integers(1, 5))
+        units, _, _ = O.layout_dim0([R * Cc], [R], n)
+        u = units[0]
+        rows_per_rank = [max(0, min(u["L"], (r + 1) * u["S"]) - r * u["S"]) // Cc
+                         for r in range(n)]
+        sizes = [c.shape[0] for c in torch.chunk(torch.arange(R), n, dim=0)]
+        sizes += [0] * (n - len(sizes))
+        assert rows_per_rank == sizes
+        assert u["S"] % Cc == 0 and u["P"] == n * u["S"]
+
+
+def test_fsdp2_resident_bytes(orc):
+    """[MDT] 五.6: with fp32 parameters a rank keeps its fp32 shard (which is
+    also the master), its fp32 grad shard and m, v: 16 bytes per parameter
+    over N in total, with no separate 16-bit copy."""
+    units, psi, psi_pad = O.layout_dim0([4096 * 1024, 1024, 8 * 1024], [4096, 1024, 8], 8)
+    ab, _ = O.ledger(units, 8, 4)
+    assert ab == 16 * psi_pad // 8
+    assert psi_pad == psi  # all row counts divide by 8 here
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 5, 8])
+def test_fsdp2_equals_fsdp1_and_dp(orc, n):
+    """FSDP2 (per-parameter dim-0 shards, fp32 parameters, cast at gather)
+    does the same per-element arithmetic as the FlatParameter path and as
+    plain data parallelism ([MDT] 六.2: the three gather schemes differ in
+    layout, not in the update), so with the same replicas the fp32 state
+    and the gathered 16-bit parameters are identical bit for bit."""
+    rows = [7, 3, 16, 1, 5]
+    cols = [6, 1, 4, 9, 1]
+    numel = [r * c for r, c in zip(rows, cols)]
+    groups = [[0, 1], [2], [3, 4]]  # FSDP units over the parameters
+    w = W.Workload(name="f2", description="", n_ranks=n, layout=W.PER_UNIT, stage=3,
+                   segments=[W.Segment(f"p{i}", numel[i], g)
+                             for g, grp in enumerate(groups) for i in grp],
+                   grad_dtype=W.F16, param_dtype=W.F16, sigma=1e-2, loss_scale=1024.0,
+                   dynamic=True, lr=1e-3, steps=4, seed=12, max_norm=0.5)
+    u2, psi, pp2 = O.layout_dim0(numel, rows, n)
+    run1 = OI.OracleRun(w)  # FSDP1: one FlatParameter per group
+    m2 = OI.to_rank_shards(u2, n, OI.master_logical(w, psi))
+    e2 = [np.zeros(int(u2["S"].sum()), np.float32) for _ in range(n)]
+    v2 = [np.zeros_like(x) for x in e2]
+    g2 = [np.zeros_like(x) for x in e2]
+    st2, hp = OI.scale_state(w), OI.hparams(w)
+    p = OI.master_logical(w, psi)
+    m = np.zeros_like(p)
+    v = np.zeros_like(p)
+    prm = O.narrow(w.param_dtype, p)
+    st3 = OI.scale_state(w)
+    for step in range(1, 5):
+        r1 = OI.replicas(w, run1.units, run1.psi_pad, step, run1.st.loss_scale)
+        if step == 2:
+            r1[n - 1][run1.units[1]["O"] + 3] = 0x7C00
+        logical = [OI.padded_to_logical(run1.units, g) for g in r1]
+        r2 = []
+        for q in range(n):
+            g = np.zeros(pp2, np.uint16)
+            for i, uu in enumerate(u2):
+                g[uu["O"]:uu["O"] + uu["L"]] = logical[q][uu["lam"]:uu["lam"] + uu["L"]]
+            r2.append(g)
+        res1 = run1.step(r1)
+        res2 = O.fsdp2_step(w.grad_dtype, n, u2, r2, m2, e2, v2, g2, hp, st2)
+        res3 = O.dp_step(w.grad_dtype, w.param_dtype, n, logical, p, m, v, prm, hp, st3)
+        assert (res1.skipped, res1.t) == (res2.skipped, res2.t) == (res3.skipped, res3.t)
+        assert res1.sumsq == res2.sumsq == res3.sumsq
+        for a1, a2, ref in ((run1.master, m2, p), (run1.m, e2, m), (run1.v, v2, v)):
+            l1 = OI.rank_shards_to_logical(run1.units, a1)
+            l2 = OI.rank_shards_to_logical(u2, a2)
+            assert np.array_equal(l1.view(np.uint32), l2.view(np.uint32))
+            assert np.array_equal(l2.view(np.uint32), ref.view(np.uint32))
+        if not res2.skipped:
+            # the fp32 grad shard holds the fixed-order sums
+            acc = OI.rank_shards_to_logical(u2, g2)
+            ref_acc = O.widen(w.grad_dtype, logical[0])
+            for q in range(1, n):
+                ref_acc = ref_acc + O.widen(w.grad_dtype, logical[q])
+            assert np.array_equal(acc.view(np.uint32), ref_acc.view(np.uint32))
+        first = 0
+        for gi, grp in enumerate(groups):
+            out2 = O.fsdp2_gather(u2, n, first, len(grp), w.param_dtype, m2)
+            out1 = O.gather_unit(run1.units, n, gi, run1.shards)
+            assert np.array_equal(out2, out1[:run1.units[gi]["L"]])
+            first += len(grp)
+        assert np.array_equal(np.concatenate([
+            O.fsdp2_gather(u2, n, 0, 2, w.param_dtype, m2),
+            O.fsdp2_gather(u2, n, 2, 1, w.param_dtype, m2),
+            O.fsdp2_gather(u2, n, 3, 2, w.param_dtype, m2)]), prm)
