@@ -33,6 +33,10 @@ def algorithmic_bytes_per_param(w):
     """Bytes the method itself moves per real parameter per applied step:
     read N 16-bit replicas, read and write fp32 master/m/v, write the 16-bit
     param; ZeRO-3 adds the unit gather (read 2 + write 2)."""
+    if w.fp32_params:
+        # FSDP2: replicas in, fp32 grad shard out and back in, fp32 state in
+        # and out, then each unit gather reads fp32 and writes 16-bit
+        return 2 * w.n_ranks + 4 + 4 + 12 + 12 + 4 + 2
     b = 2 * w.n_ranks + 12 + 12 + 2
     if w.stage == 3:
         b += 4
@@ -41,8 +45,9 @@ def algorithmic_bytes_per_param(w):
 
 def update_kernel_bytes_per_elem(w, materialized):
     """The fused update pass per (padded) element: the reduced gradient (fp32
-    sums, or the N replicas again), fp32 master/m/v in and out, 16-bit out."""
-    return (4 if materialized else 2 * w.n_ranks) + 12 + 12 + 2
+    sums, or the N replicas again), fp32 master/m/v in and out, and the
+    16-bit parameter out unless the parameters are fp32 (FSDP2)."""
+    return (4 if materialized else 2 * w.n_ranks) + 12 + 12 + (0 if w.fp32_params else 2)
 
 
 PROFILES = os.path.join(ROOT, "profiles")
@@ -230,13 +235,10 @@ def main():
     dev.init_state()
     dev.fill_grads(1, w.loss_scale)
     torch.cuda.synchronize()
-    n_units = len(dev.plan.units)
 
     def one_step(phase_events=None):
         dev.step(phase_events=phase_events)
-        if w.stage == 3:
-            for u in range(n_units):
-                dev.gather(u)
+        dev.gather_all()
 
     for _ in range(args.warmup):
         one_step()
@@ -273,7 +275,7 @@ def main():
     p2 = sum(r[2].elapsed_time(r[3]) for r in evs) / args.steps
 
     s = dev.plan.summary
-    materialized = s.policy == 1
+    materialized = s.policy != 0
     alg = algorithmic_bytes_per_param(w) * w.psi
     gbs = alg / (ms * 1e-3) / 1e9
     upd_bytes = update_kernel_bytes_per_elem(w, materialized) * s.psi_pad
@@ -294,8 +296,9 @@ def main():
                 "random-init weights)",
         "config": {"workload": w.name, "psi": w.psi, "psi_padded": s.psi_pad,
                    "virtual_ranks": w.n_ranks, "zero_stage": w.stage,
-                   "layout": "global flat" if w.layout == W.GLOBAL_FLAT else "per-unit",
-                   "rs_policy": "materialize" if materialized else "recompute"},
+                   "layout": ["global flat", "per-unit FlatParameter",
+                              "per-parameter dim-0 (FSDP2)"][w.layout],
+                   "rs_policy": ["recompute", "materialize", "fp32 grad shard"][s.policy]},
         "params_updated_per_s": round(w.psi / (ms * 1e-3), 1),
         "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
         "wall_ms_per_step": round(1e3 * wall / args.steps, 5),
@@ -305,7 +308,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(upd_gbs, 2), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(upd_gbs / PEAK_HBM_GBS, 4),
                      "traffic": traffic_for(w.name),
-                     "kernel": "zf_pass2 (fused AdamW+cast+gather)",
+                     "kernel": "zf_pass2 (fused AdamW" + ("" if w.fp32_params else
+                                                          "+cast+gather") + ")",
                      "bytes_per_launch": upd_bytes},
     }
     if not args.no_cpu_baseline:

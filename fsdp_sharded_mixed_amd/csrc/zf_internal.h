@@ -64,6 +64,7 @@ struct zf_plan {
   uint64_t magic;
   zf_plan_summary summary;
   std::vector<zf_unit_info> units;
+  std::vector<zf_group_info> groups;
   int32_t unr1, unr2;           // tile depth of pass 1 / pass 2 (x2 quads per thread)
   int32_t pass1_map;            // pass-1 tile walk (0 shared window, 1 XCD-contiguous)
   int64_t pass1_tiles;          // pass-1 blocks = squared-norm partials

@@ -5,7 +5,10 @@
 // right-padded with zeros to a multiple of the shard count N and split into
 // N equal shards, shard r for rank r.  Femtotron dev log #6 shards the
 // whole master as one giant 1-D vector (the global-flat layout); the notes'
-// simulator (0.4) and FSDP use one unit per layer.
+// simulator (0.4) and FSDP use one unit per layer.  FSDP2 (Megatron /
+// DeepSpeed / torchtitan source guide, 五.4) instead shards every parameter
+// along dim 0 like torch.chunk, padding each rank's chunk to ceil(R/N) rows:
+// one shard unit per parameter, padded at row granularity.
 #include <cstdlib>
 #include <cstring>
 #include <limits>
@@ -28,6 +31,9 @@ void fill_ledger(zf_plan* p) {
   s.state_bytes[1] = 2 * full + 2 * full + 12 * shard;
   s.state_bytes[2] = 2 * full + 2 * shard + 12 * shard;
   s.state_bytes[3] = (2 + 2 + 12) * shard;
+  // FSDP2 with fp32 parameters (source guide 五.6): the fp32 shard is the
+  // parameter and the master; fp32 grad shard; m and v.
+  s.state_bytes[4] = (4 + 4 + 8) * shard;
   // Stage-3 peak (notes, exercise 5): backward runs units last to first;
   // while it is in unit b a rank holds its resident shards (16-bit params
   // and fp32 states), the grad shards already reduce-scattered for the
@@ -57,7 +63,8 @@ extern "C" int zf_plan_flat(const zf_segment* segs, int64_t nseg, int32_t n_rank
   if (!out) return ZF_EINVAL;
   *out = nullptr;
   if (!segs || nseg < 1) return ZF_EINVAL;
-  if (layout != ZF_GLOBAL_FLAT && layout != ZF_PER_UNIT) return ZF_EINVAL;
+  if (layout != ZF_GLOBAL_FLAT && layout != ZF_PER_UNIT && layout != ZF_PER_PARAM_DIM0)
+    return ZF_EINVAL;
   if (stage < 0 || stage > 3) return ZF_EINVAL;
   if (n_ranks < 1 || n_ranks > ZF_MAX_RANKS) return ZF_ESIZE;
 
@@ -75,12 +82,33 @@ extern "C" int zf_plan_flat(const zf_segment* segs, int64_t nseg, int32_t n_rank
       if (segs[i].numel > kLimit - lam) { delete p; return ZF_ESIZE; }
       if (uid != cur) {
         if (uid != cur + 1) { delete p; return ZF_EINVAL; }
-        zf_unit_info u{};
-        u.lam = lam;
-        p->units.push_back(u);
+        zf_group_info g{};
+        g.first_unit = (int64_t)p->units.size();
+        p->groups.push_back(g);
+        if (layout != ZF_PER_PARAM_DIM0) {
+          zf_unit_info u{};
+          u.lam = lam;
+          p->units.push_back(u);
+        }
         cur = uid;
       }
-      p->units.back().L += segs[i].numel;
+      if (layout == ZF_PER_PARAM_DIM0) {
+        // one unit per parameter; its rows carry the padding granularity
+        const int64_t rows = segs[i].dim0 > 0 ? segs[i].dim0 : segs[i].numel;
+        if (segs[i].numel % rows != 0) { delete p; return ZF_EINVAL; }
+        zf_unit_info u{};
+        u.lam = lam;
+        u.L = segs[i].numel;
+        const int64_t cols = segs[i].numel / rows;
+        const int64_t chunk = (rows + n_ranks - 1) / n_ranks;
+        u.S = chunk * cols;
+        u.P = u.S * n_ranks;
+        p->units.push_back(u);
+      } else {
+        p->units.back().L += segs[i].numel;
+      }
+      p->groups.back().n_units = (int64_t)p->units.size() - p->groups.back().first_unit;
+      p->groups.back().numel += segs[i].numel;
       lam += segs[i].numel;
     }
   } catch (const std::bad_alloc&) {
@@ -89,29 +117,43 @@ extern "C" int zf_plan_flat(const zf_segment* segs, int64_t nseg, int32_t n_rank
   }
   int64_t off = 0, max_pad = 0;
   for (zf_unit_info& u : p->units) {
-    u.P = round_up(u.L, n_ranks);
-    u.S = u.P / n_ranks;
+    if (layout != ZF_PER_PARAM_DIM0) {
+      u.P = round_up(u.L, n_ranks);
+      u.S = u.P / n_ranks;
+    }
+    if (u.P < u.L || u.P >= kLimit) { delete p; return ZF_ESIZE; }
     u.O = off;
     off += u.P;
     if (u.P > max_pad) max_pad = u.P;
     if (off >= kLimit) { delete p; return ZF_ESIZE; }
+  }
+  int64_t max_group = 0;
+  for (zf_group_info& g : p->groups) {
+    for (int64_t k = 0; k < g.n_units; ++k) g.padded += p->units[g.first_unit + k].P;
+    if (g.numel > max_group) max_group = g.numel;
   }
   zf_plan_summary& s = p->summary;
   s.psi = lam;
   s.psi_pad = off;
   s.n_units = (int64_t)p->units.size();
   s.max_unit_pad = max_pad;
+  s.n_groups = (int64_t)p->groups.size();
+  s.max_group_numel = max_group;
   s.n_ranks = n_ranks;
   s.layout = layout;
   s.stage = stage;
   // Recompute the sums in the update pass (re-read 2N bytes per element)
   // unless writing and re-reading an fp32 copy (8 bytes) is cheaper.
-  s.policy = (2 * n_ranks > 8) ? 1 : 0;
+  // ZF_PER_PARAM_DIM0 (FSDP2) keeps a resident fp32 gradient shard, which
+  // holds the sums; otherwise they are recomputed from the replicas in the
+  // update pass unless writing and re-reading an fp32 copy (8 bytes) is
+  // cheaper than re-reading N replicas (2N bytes).
+  s.policy = layout == ZF_PER_PARAM_DIM0 ? 2 : ((2 * n_ranks > 8) ? 1 : 0);
 
   const int64_t nq = s.psi_pad / 4;  // quads; the ragged tail rides on the last tile
   p->unr1 = zf::unr_pass1(n_ranks);
   p->pass1_map = zf::map_pass1(n_ranks);
-  p->unr2 = zf::unr_pass2(n_ranks, s.psi_pad, s.policy == 1);
+  p->unr2 = zf::unr_pass2(n_ranks, s.psi_pad, s.policy != 0);
   const int64_t q1 = (int64_t)zf::kThreads * zf::kQuadsPerUnr * p->unr1;
   const int64_t q2 = (int64_t)zf::kThreads * zf::kQuadsPerUnr * p->unr2;
   const int64_t t1 = (nq + q1 - 1) / q1;
@@ -146,6 +188,13 @@ extern "C" int zf_plan_unit(const zf_plan* plan, int64_t u, zf_unit_info* out) {
   if (!plan || plan->magic != zf::kPlanMagic || !out) return ZF_EINVAL;
   if (u < 0 || u >= (int64_t)plan->units.size()) return ZF_EINVAL;
   *out = plan->units[u];
+  return ZF_OK;
+}
+
+extern "C" int zf_plan_group(const zf_plan* plan, int64_t g, zf_group_info* out) {
+  if (!plan || plan->magic != zf::kPlanMagic || !out) return ZF_EINVAL;
+  if (g < 0 || g >= (int64_t)plan->groups.size()) return ZF_EINVAL;
+  *out = plan->groups[g];
   return ZF_OK;
 }
 

@@ -390,7 +390,7 @@ __device__ __forceinline__ void adamw1(const Coef& c, float acc, float& p, float
   v = vv;
 }
 
-template <int NR, int GDT, int PDT, bool MAT, int Q>
+template <int NR, int GDT, int PDT, bool MAT, int Q, bool OUT16>
 __global__ __launch_bounds__(kThreads) void zf_pass2(Pass2Args a) {
   if (a.st->skipped) return;  // the whole grid leaves at once
   Coef c;
@@ -436,7 +436,8 @@ __global__ __launch_bounds__(kThreads) void zf_pass2(Pass2Args a) {
     stq32_nt(a.master, qi[h], (f32x4){pp[0], pp[1], pp[2], pp[3]});
     stq32_nt(a.m, qi[h], (f32x4){mm[0], mm[1], mm[2], mm[3]});
     stq32_nt(a.v, qi[h], (f32x4){vv[0], vv[1], vv[2], vv[3]});
-    stq16_nt(a.out, qi[h], (u32x2){pack2<PDT>(pp[0], pp[1]), pack2<PDT>(pp[2], pp[3])});
+    if constexpr (OUT16)
+      stq16_nt(a.out, qi[h], (u32x2){pack2<PDT>(pp[0], pp[1]), pack2<PDT>(pp[2], pp[3])});
   }
   const int64_t tail0 = nq * kQuad;
   if (tile == gridDim.x - 1 && (int64_t)threadIdx.x < a.n - tail0) {
@@ -447,7 +448,7 @@ __global__ __launch_bounds__(kThreads) void zf_pass2(Pass2Args a) {
     a.master[e] = pe;
     a.m[e] = me;
     a.v[e] = ve;
-    reinterpret_cast<uint16_t*>(a.out)[e] = narrow1<PDT>(pe);
+    if constexpr (OUT16) reinterpret_cast<uint16_t*>(a.out)[e] = narrow1<PDT>(pe);
   }
 }
 
@@ -482,6 +483,52 @@ __global__ __launch_bounds__(kThreads) void zf_gather_kernel(GatherArgs a) {
     if (tid < S - tail0) d[tail0 + tid] = s[tail0 + tid];
   } else {
     for (int64_t j = tid; j < S; j += stride) d[j] = s[j];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// FSDP2 unshard: cast each parameter's fp32 shards (padded-flat [O_u,
+// O_u + L_u): the N ranks' chunks side by side, padding rows excluded) to
+// 16 bits into the group buffer at the parameter's unpadded offset.
+// blockIdx.y = parameter of this launch; blockIdx.x = 2048-element tile.
+constexpr int kCastMax = 32;  // parameters per launch
+struct CastEntry {
+  int64_t src;  // O_u in the fp32 array
+  int64_t dst;  // offset in the group buffer
+  int64_t len;  // L_u
+};
+struct CastArgs {
+  const float* master;
+  uint16_t* out;
+  CastEntry e[kCastMax];
+};
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void zf_gather_cast_kernel(CastArgs a) {
+  const CastEntry e = a.e[blockIdx.y];
+  const int64_t t0 = (int64_t)blockIdx.x * kThreads * 8;
+  if (t0 >= e.len) return;
+  const float* src = a.master + e.src;
+  uint16_t* dst = a.out + e.dst;
+  const bool vec = (e.src % 4 == 0) && ((reinterpret_cast<uintptr_t>(dst) & 7u) == 0);
+  if (vec) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t q = t0 / 4 + h * kThreads + threadIdx.x;
+      const int64_t e0 = 4 * q;
+      if (e0 + 4 <= e.len) {
+        const f32x4 x = reinterpret_cast<const f32x4*>(src)[q];
+        reinterpret_cast<u32x2*>(dst)[q] = (u32x2){pack2<DT>(x.x, x.y), pack2<DT>(x.z, x.w)};
+      } else {
+        for (int64_t k = e0; k < e.len && k < e0 + 4; ++k) dst[k] = narrow1<DT>(src[k]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int64_t i = t0 + (int64_t)k * kThreads + threadIdx.x;
+      if (i < e.len) dst[i] = narrow1<DT>(src[i]);
+    }
   }
 }
 
@@ -557,16 +604,15 @@ int launch_pass1(const zf_plan* plan, int32_t dt, hipStream_t s, const Pass1Args
   return hipGetLastError() == hipSuccess ? ZF_OK : ZF_EHIP;
 }
 
-template <int GDT, int PDT, int U>
+template <int GDT, int PDT, int U, bool OUT16>
 void launch_pass2_nr(int nr, bool mat, dim3 grid, hipStream_t s, const Pass2Args& a) {
+  constexpr int Q = zf::kQuadsPerUnr * U;
   if (mat) {
-    hipLaunchKernelGGL((zf_pass2<0, GDT, PDT, true, zf::kQuadsPerUnr * U>), grid, dim3(kThreads), 0, s,
-                       a);
+    hipLaunchKernelGGL((zf_pass2<0, GDT, PDT, true, Q, OUT16>), grid, dim3(kThreads), 0, s, a);
     return;
   }
 #define ZF_P2(NRV) \
-  hipLaunchKernelGGL((zf_pass2<NRV, GDT, PDT, false, zf::kQuadsPerUnr * U>), grid, dim3(kThreads), 0, s, \
-                     a)
+  hipLaunchKernelGGL((zf_pass2<NRV, GDT, PDT, false, Q, OUT16>), grid, dim3(kThreads), 0, s, a)
   switch (nr) {
     case 1: ZF_P2(1); break;
     case 2: ZF_P2(2); break;
@@ -582,24 +628,28 @@ void launch_pass2_nr(int nr, bool mat, dim3 grid, hipStream_t s, const Pass2Args
 }
 
 template <int U>
-void launch_pass2_u(int nr, int32_t gdt, int32_t pdt, bool mat, dim3 grid, hipStream_t s,
-                    const Pass2Args& a) {
+void launch_pass2_u(int nr, int32_t gdt, int32_t pdt, bool mat, bool out16, dim3 grid,
+                    hipStream_t s, const Pass2Args& a) {
+  if (!out16) {  // fp32 parameters: no 16-bit copy, the param dtype is unused
+    if (gdt == ZF_BF16) launch_pass2_nr<ZF_BF16, ZF_BF16, U, false>(nr, mat, grid, s, a);
+    else launch_pass2_nr<ZF_F16, ZF_BF16, U, false>(nr, mat, grid, s, a);
+    return;
+  }
   if (gdt == ZF_BF16) {
-    if (pdt == ZF_BF16) launch_pass2_nr<ZF_BF16, ZF_BF16, U>(nr, mat, grid, s, a);
-    else launch_pass2_nr<ZF_BF16, ZF_F16, U>(nr, mat, grid, s, a);
+    if (pdt == ZF_BF16) launch_pass2_nr<ZF_BF16, ZF_BF16, U, true>(nr, mat, grid, s, a);
+    else launch_pass2_nr<ZF_BF16, ZF_F16, U, true>(nr, mat, grid, s, a);
   } else {
-    if (pdt == ZF_BF16) launch_pass2_nr<ZF_F16, ZF_BF16, U>(nr, mat, grid, s, a);
-    else launch_pass2_nr<ZF_F16, ZF_F16, U>(nr, mat, grid, s, a);
+    if (pdt == ZF_BF16) launch_pass2_nr<ZF_F16, ZF_BF16, U, true>(nr, mat, grid, s, a);
+    else launch_pass2_nr<ZF_F16, ZF_F16, U, true>(nr, mat, grid, s, a);
   }
 }
 
-int launch_pass2(const zf_plan* plan, int32_t gdt, int32_t pdt, hipStream_t s,
-                 const Pass2Args& a) {
+int launch_pass2(const zf_plan* plan, int32_t gdt, int32_t pdt, bool mat, bool out16,
+                 hipStream_t s, const Pass2Args& a) {
   const dim3 grid((uint32_t)plan->pass2_tiles);
   const int nr = plan->summary.n_ranks;
-  const bool mat = plan->ws_rs_offset >= 0;
-  if (plan->unr2 == 2) launch_pass2_u<2>(nr, gdt, pdt, mat, grid, s, a);
-  else launch_pass2_u<1>(nr, gdt, pdt, mat, grid, s, a);
+  if (plan->unr2 == 2) launch_pass2_u<2>(nr, gdt, pdt, mat, out16, grid, s, a);
+  else launch_pass2_u<1>(nr, gdt, pdt, mat, out16, grid, s, a);
   return hipGetLastError() == hipSuccess ? ZF_OK : ZF_EHIP;
 }
 
@@ -633,12 +683,14 @@ extern "C" int zf_shard_step(const zf_plan* plan, const zf_hparams* hp,
   GradPtrs gp;
   int rc = grads_ok(plan, args->grads, gp);
   if (rc != ZF_OK) return rc;
-  void* const bufs[] = {args->master, args->exp_avg, args->exp_avg_sq, args->params,
-                        args->state};
+  void* const bufs[] = {args->master, args->exp_avg, args->exp_avg_sq, args->state};
   for (void* b : bufs) {
     if (!b) return ZF_EINVAL;
     if (!aligned16(b)) return ZF_EALIGN;
   }
+  if (args->params && !aligned16(args->params)) return ZF_EALIGN;
+  if (args->grad_shards && !aligned16(args->grad_shards)) return ZF_EALIGN;
+  if (sm.policy == 2 && !args->grad_shards) return ZF_EINVAL;
   if (args->numel < sm.psi_pad) return ZF_ESIZE;
   if (sm.workspace_bytes > 0) {
     if (!args->workspace) return ZF_EINVAL;
@@ -648,8 +700,11 @@ extern "C" int zf_shard_step(const zf_plan* plan, const zf_hparams* hp,
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(args->workspace);
   Partial* partials = reinterpret_cast<Partial*>(ws + plan->ws_partials_offset);
-  const bool mat = plan->ws_rs_offset >= 0;
-  float* rs = mat ? reinterpret_cast<float*>(ws + plan->ws_rs_offset) : nullptr;
+  // the sums go to the caller's fp32 gradient shard if given, else to the
+  // workspace copy if the plan materialises them, else nowhere (recomputed)
+  float* rs = args->grad_shards;
+  if (!rs && plan->ws_rs_offset >= 0) rs = reinterpret_cast<float*>(ws + plan->ws_rs_offset);
+  const bool mat = rs != nullptr;
   const int nr = sm.n_ranks;
 
   (void)hipGetLastError();
@@ -705,7 +760,8 @@ extern "C" int zf_shard_step(const zf_plan* plan, const zf_hparams* hp,
   a2.lrf = (float)hp->lr;
   a2.ef = (float)hp->eps;
   a2.nr = nr;
-  rc = launch_pass2(plan, args->grad_dtype, args->param_dtype, s, a2);
+  rc = launch_pass2(plan, args->grad_dtype, args->param_dtype, mat, args->params != nullptr, s,
+                    a2);
   if (rc != ZF_OK) return rc;
   return record(args->phase_events, 3, s);
 }
@@ -756,6 +812,43 @@ extern "C" int zf_gather(const zf_plan* plan, int64_t unit, int32_t dtype,
   hipLaunchKernelGGL(zf_gather_kernel, dim3((uint32_t)bx, (uint32_t)nr), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), a);
   return hipGetLastError() == hipSuccess ? ZF_OK : ZF_EHIP;
+}
+
+extern "C" int zf_gather_cast(const zf_plan* plan, int64_t group, int32_t dtype,
+                              const float* master, int64_t master_numel, void* out,
+                              int64_t out_numel, void* stream) {
+  if (!valid_plan(plan) || !master || !out) return ZF_EINVAL;
+  if (!valid_dtype(dtype)) return ZF_EDTYPE;
+  if (group < 0 || group >= (int64_t)plan->groups.size()) return ZF_EINVAL;
+  if (!aligned16(master) || (reinterpret_cast<uintptr_t>(out) & 1u) != 0) return ZF_EALIGN;
+  const zf_group_info& g = plan->groups[group];
+  if (master_numel < plan->summary.psi_pad || out_numel < g.numel) return ZF_ESIZE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  int64_t dst = 0;
+  for (int64_t first = 0; first < g.n_units; first += kCastMax) {
+    CastArgs a;
+    a.master = master;
+    a.out = static_cast<uint16_t*>(out);
+    int64_t count = g.n_units - first, max_len = 0;
+    if (count > kCastMax) count = kCastMax;
+    for (int64_t k = 0; k < count; ++k) {
+      const zf_unit_info& u = plan->units[g.first_unit + first + k];
+      a.e[k].src = u.O;
+      a.e[k].dst = dst;
+      a.e[k].len = u.L;
+      dst += u.L;
+      if (u.L > max_len) max_len = u.L;
+    }
+    const int64_t bx = (max_len + kThreads * 8 - 1) / (kThreads * 8);
+    const dim3 grid((uint32_t)(bx < 1 ? 1 : bx), (uint32_t)count);
+    if (dtype == ZF_BF16)
+      hipLaunchKernelGGL(zf_gather_cast_kernel<ZF_BF16>, grid, dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL(zf_gather_cast_kernel<ZF_F16>, grid, dim3(kThreads), 0, s, a);
+    if (hipGetLastError() != hipSuccess) return ZF_EHIP;
+  }
+  return ZF_OK;
 }
 
 extern "C" int zf_read_result(const void* d_state, zf_step_result* out, void* stream) {

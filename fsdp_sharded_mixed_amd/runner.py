@@ -32,11 +32,17 @@ class DeviceRun:
         self.master = torch.zeros(n, dtype=torch.float32, device=dev)
         self.exp_avg = torch.zeros(n, dtype=torch.float32, device=dev)
         self.exp_avg_sq = torch.zeros(n, dtype=torch.float32, device=dev)
-        self.params = torch.zeros(n, dtype=pdt, device=dev)
+        # FSDP2 keeps fp32 parameters (no 16-bit copy) and resident fp32
+        # gradient shards; the other layouts keep a 16-bit copy
+        self.params = None if w.fp32_params else torch.zeros(n, dtype=pdt, device=dev)
+        self.grad_shards = (torch.zeros(n, dtype=torch.float32, device=dev)
+                            if s.policy == 2 else None)
         self.workspace = torch.empty(max(1, s.workspace_bytes), dtype=torch.uint8, device=dev)
         self.state = torch.empty(zf.state_bytes(), dtype=torch.uint8, device=dev)
         self.unit_buf = (torch.empty(s.max_unit_pad, dtype=pdt, device=dev)
-                         if w.stage == 3 else None)
+                         if w.stage == 3 and not w.fp32_params else None)
+        self.group_buf = (torch.empty(s.max_group_numel, dtype=pdt, device=dev)
+                          if w.fp32_params else None)
         self.hp = zf.hparams(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, w.max_norm)
         self.step_no = 0
         self.loss_scale = w.loss_scale
@@ -62,7 +68,8 @@ class DeviceRun:
                 self.master[pa:pa + (b - a)] = 1.0
         self.exp_avg.zero_()
         self.exp_avg_sq.zero_()
-        self.params.copy_(self.master.to(self.params.dtype))
+        if self.params is not None:
+            self.params.copy_(self.master.to(self.params.dtype))
         zf.state_init(self.state, w.loss_scale, w.dynamic, w.growth_interval)
         self.step_no = 0
         self.loss_scale = w.loss_scale
@@ -90,7 +97,8 @@ class DeviceRun:
         self.step_no += 1
         zf.shard_step(self.plan, self.hp, self.w.grad_dtype, self.w.param_dtype, self.grads,
                       self.master, self.exp_avg, self.exp_avg_sq, self.params, self.workspace,
-                      self.state, stream=stream, phase_events=phase_events)
+                      self.state, stream=stream, phase_events=phase_events,
+                      grad_shards=self.grad_shards)
 
     def result(self):
         return zf.read_result(self.state)
@@ -105,6 +113,22 @@ class DeviceRun:
         zf.gather(self.plan, u, self.w.param_dtype, self.unit_shards(u), self.unit_buf,
                   stream=stream)
         return self.unit_buf[:self.plan.units[u].P]
+
+    def gather_cast(self, g, stream=None):
+        """FSDP2 unshard of group g: the group's parameters, unpadded, 16-bit."""
+        zf.gather_cast(self.plan, g, self.w.param_dtype, self.master, self.group_buf,
+                       stream=stream)
+        return self.group_buf[:self.plan.groups[g].numel]
+
+    def gather_all(self, stream=None):
+        """Every unit's gather, in forward order (the per-unit stand-in for the
+        next forward's all-gathers)."""
+        if self.w.fp32_params:
+            for g in range(len(self.plan.groups)):
+                self.gather_cast(g, stream=stream)
+        elif self.w.stage == 3:
+            for u in range(len(self.plan.units)):
+                self.gather(u, stream=stream)
 
     def run_workload_step(self):
         """One step of the workload's own sequence: fresh grads for step k at

@@ -16,9 +16,9 @@ Shapes:
     input norm, post-attention norm (Femtotron dev log #7 lists nine tensors
     per layer, q/k/v/o first), then the final norm and the LM head; each
     Linear weight is row-major [out, in].
-  * FSDP units for the ZeRO-3 workload: {embedding}, one unit per decoder
-    layer, {final norm, LM head} (the torchtitan FSDP2 wrapping of the
-    Megatron / DeepSpeed / torchtitan source guide, ch. 五.4).
+  * FSDP units for the ZeRO-3 and FSDP2 workloads: {embedding}, one unit
+    per decoder layer, {final norm, LM head} (the torchtitan FSDP2 wrapping
+    of the Megatron / DeepSpeed / torchtitan source guide, ch. 五.4).
 
 Inputs are a pure function of (seed, stream, logical index): a replica's
 gradient for element i at step k comes from stream grad_stream(k, replica),
@@ -31,7 +31,7 @@ from dataclasses import dataclass, field
 from typing import List, Optional, Tuple
 
 F16, BF16 = 1, 2
-GLOBAL_FLAT, PER_UNIT = 0, 1
+GLOBAL_FLAT, PER_UNIT, PER_PARAM_DIM0 = 0, 1, 2
 
 KIND_WEIGHT, KIND_BIAS, KIND_NORM = 0, 1, 2
 
@@ -51,6 +51,7 @@ class Segment:
     numel: int
     unit: int
     kind: int = KIND_WEIGHT
+    rows: int = 0  # dim-0 size ([out, in] weights: out); 0 for 1-D tensors
 
 
 @dataclass
@@ -79,6 +80,7 @@ class Workload:
     norm_weights_one: bool = False
     inject_step: Optional[int] = None      # +inf injected into one replica at this step
     inject_replica: int = 1
+    fp32_params: bool = False              # FSDP2: the fp32 shard is the parameter
     extra: dict = field(default_factory=dict)
 
     @property
@@ -102,23 +104,23 @@ def llama_segments(hidden, inter, heads, kv_heads, layers, vocab, head_dim=64,
                    per_layer_units=False) -> List[Segment]:
     q = heads * head_dim
     kv = kv_heads * head_dim
-    segs = [Segment("embed", vocab * hidden, 0)]
+    segs = [Segment("embed", vocab * hidden, 0, rows=vocab)]
     for i in range(layers):
         u = i + 1 if per_layer_units else 0
         segs += [
-            Segment(f"l{i}.q", q * hidden, u),
-            Segment(f"l{i}.k", kv * hidden, u),
-            Segment(f"l{i}.v", kv * hidden, u),
-            Segment(f"l{i}.o", hidden * q, u),
-            Segment(f"l{i}.gate", inter * hidden, u),
-            Segment(f"l{i}.up", inter * hidden, u),
-            Segment(f"l{i}.down", hidden * inter, u),
+            Segment(f"l{i}.q", q * hidden, u, rows=q),
+            Segment(f"l{i}.k", kv * hidden, u, rows=kv),
+            Segment(f"l{i}.v", kv * hidden, u, rows=kv),
+            Segment(f"l{i}.o", hidden * q, u, rows=hidden),
+            Segment(f"l{i}.gate", inter * hidden, u, rows=inter),
+            Segment(f"l{i}.up", inter * hidden, u, rows=inter),
+            Segment(f"l{i}.down", hidden * inter, u, rows=hidden),
             Segment(f"l{i}.input_norm", hidden, u, KIND_NORM),
             Segment(f"l{i}.post_norm", hidden, u, KIND_NORM),
         ]
     last = layers + 1 if per_layer_units else 0
     segs += [Segment("final_norm", hidden, last, KIND_NORM),
-             Segment("lm_head", vocab * hidden, last)]
+             Segment("lm_head", vocab * hidden, last, rows=vocab)]
     return segs
 
 
@@ -176,6 +178,21 @@ def llama2b_z3() -> Workload:
         lr=1e-4, steps=3, seed=4)
 
 
+def llama2b_fsdp2() -> Workload:
+    """The 2.1B decoder under FSDP2 as torchtitan runs it by default (source
+    guide 五.4 and 五.6): every parameter sharded along dim 0, fp32 shards
+    that are the parameters, fp32 reduce-scatter into resident fp32 gradient
+    shards, bf16 only when a unit (a decoder layer) is gathered."""
+    return Workload(
+        name="llama-2.1b-n2-fsdp2",
+        description="Llama-style decoder h2048/i8192/32h/8kv/32L/V40960, Psi=2,114,062,336, "
+                    "FSDP2 per-parameter dim-0 shards over N=2, fp32 parameters and grad "
+                    "shards, bf16 cast at the 34 unit gathers",
+        segments=_h2048(32, per_layer_units=True), n_ranks=2, layout=PER_PARAM_DIM0, stage=3,
+        grad_dtype=BF16, param_dtype=BF16, sigma=1e-3, loss_scale=1.0, dynamic=False,
+        lr=1e-4, steps=3, seed=4, fp32_params=True)
+
+
 def llama4b() -> Workload:
     return Workload(
         name="llama-4.06b-n2",
@@ -192,6 +209,7 @@ ALL = {
     "llama-73m-n8": llama73m,
     "llama-654m-n2": llama654m,
     "llama-2.1b-n2-zero3": llama2b_z3,
+    "llama-2.1b-n2-fsdp2": llama2b_fsdp2,
     "llama-4.06b-n2": llama4b,
 }
 

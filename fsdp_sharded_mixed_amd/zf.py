@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libzf.so")
 
 F16, BF16 = 1, 2
-GLOBAL_FLAT, PER_UNIT = 0, 1
+GLOBAL_FLAT, PER_UNIT, PER_PARAM_DIM0 = 0, 1, 2
 MAX_RANKS = 64
 STATUS = {0: "ZF_OK", -1: "ZF_EINVAL", -2: "ZF_EALIGN", -3: "ZF_EDTYPE", -4: "ZF_ESIZE",
           -5: "ZF_EHIP", -6: "ZF_ENOMEM"}
@@ -27,20 +27,27 @@ class ZfError(RuntimeError):
 
 
 class Segment(C.Structure):
-    _fields_ = [("numel", C.c_int64), ("unit", C.c_int32), ("kind", C.c_int32)]
+    _fields_ = [("numel", C.c_int64), ("unit", C.c_int32), ("kind", C.c_int32),
+                ("dim0", C.c_int64)]
 
 
 class PlanSummary(C.Structure):
     _fields_ = [("psi", C.c_int64), ("psi_pad", C.c_int64), ("n_units", C.c_int64),
-                ("max_unit_pad", C.c_int64), ("n_ranks", C.c_int32), ("layout", C.c_int32),
+                ("max_unit_pad", C.c_int64), ("n_groups", C.c_int64),
+                ("max_group_numel", C.c_int64), ("n_ranks", C.c_int32), ("layout", C.c_int32),
                 ("stage", C.c_int32), ("policy", C.c_int32), ("workspace_bytes", C.c_int64),
-                ("state_bytes", C.c_int64 * 4), ("stage3_peak_bytes", C.c_int64),
+                ("state_bytes", C.c_int64 * 5), ("stage3_peak_bytes", C.c_int64),
                 ("comm_bytes", C.c_double * 5)]
 
 
 class UnitInfo(C.Structure):
     _fields_ = [("L", C.c_int64), ("P", C.c_int64), ("S", C.c_int64), ("O", C.c_int64),
                 ("lam", C.c_int64)]
+
+
+class GroupInfo(C.Structure):
+    _fields_ = [("first_unit", C.c_int64), ("n_units", C.c_int64), ("numel", C.c_int64),
+                ("padded", C.c_int64)]
 
 
 class Hparams(C.Structure):
@@ -52,7 +59,8 @@ class StepArgs(C.Structure):
     _fields_ = [("grad_dtype", C.c_int32), ("param_dtype", C.c_int32),
                 ("grads", C.POINTER(C.c_void_p)), ("master", C.c_void_p),
                 ("exp_avg", C.c_void_p), ("exp_avg_sq", C.c_void_p), ("params", C.c_void_p),
-                ("numel", C.c_int64), ("workspace", C.c_void_p), ("workspace_size", C.c_int64),
+                ("grad_shards", C.c_void_p), ("numel", C.c_int64), ("workspace", C.c_void_p),
+                ("workspace_size", C.c_int64),
                 ("state", C.c_void_p), ("phase_events", C.POINTER(C.c_void_p))]
 
 
@@ -69,6 +77,9 @@ _SIGNATURES = {
                                C.POINTER(C.c_void_p)]),
     "zf_plan_info": (C.c_int, [C.c_void_p, C.POINTER(PlanSummary)]),
     "zf_plan_unit": (C.c_int, [C.c_void_p, C.c_int64, C.POINTER(UnitInfo)]),
+    "zf_plan_group": (C.c_int, [C.c_void_p, C.c_int64, C.POINTER(GroupInfo)]),
+    "zf_gather_cast": (C.c_int, [C.c_void_p, C.c_int64, C.c_int32, C.c_void_p, C.c_int64,
+                                 C.c_void_p, C.c_int64, C.c_void_p]),
     "zf_plan_free": (None, [C.c_void_p]),
     "zf_workspace_bytes": (C.c_int64, [C.c_void_p]),
     "zf_state_bytes": (C.c_int64, []),
@@ -136,6 +147,7 @@ class Plan:
     handle: int
     summary: PlanSummary
     units: list
+    groups: list
 
     def __del__(self, _free=lib.zf_plan_free):
         h, self.handle = self.handle, None
@@ -157,16 +169,18 @@ def plan_flat(segments, n_ranks, layout, stage):
     arr = (Segment * len(segments))()
     for i, s in enumerate(segments):
         if isinstance(s, (tuple, list)):
-            numel, unit, kind = (list(s) + [0])[:3]
+            numel, unit, kind, dim0 = (list(s) + [0, 0])[:4]
         else:
-            numel, unit, kind = s.numel, s.unit, getattr(s, "kind", 0)
-        arr[i] = Segment(int(numel), int(unit), int(kind))
+            numel, unit = s.numel, s.unit
+            kind, dim0 = getattr(s, "kind", 0), getattr(s, "rows", 0)
+        arr[i] = Segment(int(numel), int(unit), int(kind), int(dim0))
     h = C.c_void_p()
     _check(lib.zf_plan_flat(arr, len(segments), int(n_ranks), int(layout), int(stage),
                             C.byref(h)), "zf_plan_flat")
     summary = plan_info(h.value)
     units = [plan_unit(h.value, u) for u in range(summary.n_units)]
-    return Plan(h.value, summary, units)
+    groups = [plan_group(h.value, g) for g in range(summary.n_groups)]
+    return Plan(h.value, summary, units, groups)
 
 
 def _handle(plan):
@@ -182,6 +196,12 @@ def plan_info(plan):
 def plan_unit(plan, u):
     out = UnitInfo()
     _check(lib.zf_plan_unit(_handle(plan), int(u), C.byref(out)), "zf_plan_unit")
+    return out
+
+
+def plan_group(plan, g):
+    out = GroupInfo()
+    _check(lib.zf_plan_group(_handle(plan), int(g), C.byref(out)), "zf_plan_group")
     return out
 
 
@@ -213,17 +233,19 @@ def _nbytes(t, nbytes):
 
 def shard_step(plan, hp, grad_dtype, param_dtype, grads, master, exp_avg, exp_avg_sq, params,
                workspace, state, stream=None, phase_events=None, numel=None,
-               workspace_size=None):
-    """zf_shard_step.  grads: N tensors (or addresses); phase_events: None or
-    4 raw hipEvent_t handles.  numel / workspace_size default to the sizes of
-    the tensors passed (the smallest per-element array)."""
+               workspace_size=None, grad_shards=None):
+    """zf_shard_step.  grads: N tensors (or addresses); params may be None
+    (fp32 parameters); grad_shards: None or the fp32 gradient shards;
+    phase_events: None or 4 raw hipEvent_t handles.  numel / workspace_size
+    default to the sizes of the tensors passed (the smallest array)."""
     gp = _ptr_array(grads)
     ev = (C.c_void_p * 4)(*phase_events) if phase_events is not None else None
     if numel is None:
-        numel = min(t.numel() for t in list(grads) + [master, exp_avg, exp_avg_sq, params])
+        arrays = list(grads) + [master, exp_avg, exp_avg_sq, params, grad_shards]
+        numel = min(t.numel() for t in arrays if t is not None)
     args = StepArgs(int(grad_dtype), int(param_dtype), gp, _ptr(master), _ptr(exp_avg),
-                    _ptr(exp_avg_sq), _ptr(params), int(numel), _ptr(workspace),
-                    _nbytes(workspace, workspace_size), _ptr(state), ev)
+                    _ptr(exp_avg_sq), _ptr(params), _ptr(grad_shards), int(numel),
+                    _ptr(workspace), _nbytes(workspace, workspace_size), _ptr(state), ev)
     _check(lib.zf_shard_step(_handle(plan), C.byref(hp), C.byref(args), _stream(stream)),
            "zf_shard_step")
 
@@ -241,6 +263,15 @@ def gather(plan, unit, dtype, shards, unit_buf, stream=None, unit_buf_numel=None
     n = unit_buf_numel if unit_buf_numel is not None else unit_buf.numel()
     _check(lib.zf_gather(_handle(plan), int(unit), int(dtype), _ptr_array(shards),
                          _ptr(unit_buf), int(n), _stream(stream)), "zf_gather")
+
+
+def gather_cast(plan, group, dtype, master, out, stream=None, master_numel=None,
+                out_numel=None):
+    """zf_gather_cast (FSDP2 unshard of one group into `out`)."""
+    mn = master_numel if master_numel is not None else master.numel()
+    on = out_numel if out_numel is not None else out.numel()
+    _check(lib.zf_gather_cast(_handle(plan), int(group), int(dtype), _ptr(master), int(mn),
+                              _ptr(out), int(on), _stream(stream)), "zf_gather_cast")
 
 
 def read_result(state, stream=None):

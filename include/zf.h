@@ -27,8 +27,11 @@
  *         into a padded_size full buffer.
  *   [MDT] Megatron / DeepSpeed / torchtitan architecture and source guide,
  *         ch. 四.3 (step: check fp16 overflow -> clip -> Adam per fp32
- *         partition -> copy to the 16-bit partition -> all-gather) and 五.7
- *         (global gradient-norm clipping).
+ *         partition -> copy to the 16-bit partition -> all-gather), 五.4 and
+ *         五.6 (FSDP2: per-parameter dim-0 shards, the fp32 shard is the
+ *         parameter, fp32 reduce-scatter into the shard's gradient, cast to
+ *         the parameter dtype at all-gather time), 六.2 (Stage 3 vs FSDP1 vs
+ *         FSDP2) and 五.7 (global gradient-norm clipping).
  *
  * Conventions for every call:
  *   - Sizes are element counts unless a name ends in _bytes.
@@ -78,15 +81,26 @@ enum zf_status {
 };
 
 enum zf_dtype { ZF_F16 = 1, ZF_BF16 = 2 };
-enum zf_layout { ZF_GLOBAL_FLAT = 0, ZF_PER_UNIT = 1 };
+/* Layouts:
+ *   ZF_GLOBAL_FLAT    all parameters form one FlatParameter ([F6]);
+ *   ZF_PER_UNIT       one FlatParameter per FSDP unit ([L13] 5.2, FSDP1);
+ *   ZF_PER_PARAM_DIM0 FSDP2 ([MDT] 五.4): every parameter is cut along dim 0
+ *                     into N chunks of ceil(R/N) rows (torch.chunk; short or
+ *                     empty last chunks), each rank's chunk padded with zero
+ *                     rows, so a parameter of R x C elements takes
+ *                     P = N*ceil(R/N)*C elements in the padded flat; the FSDP
+ *                     unit ids group parameters for zf_gather_cast. */
+enum zf_layout { ZF_GLOBAL_FLAT = 0, ZF_PER_UNIT = 1, ZF_PER_PARAM_DIM0 = 2 };
 
 /* One parameter tensor, in model order.  `unit` is its FSDP unit id (ids run
  * 0,0,..,1,1,..; ignored for ZF_GLOBAL_FLAT); `kind` is informational (0
- * weight, 1 bias, 2 norm weight). */
+ * weight, 1 bias, 2 norm weight); `dim0` is its number of rows, used by
+ * ZF_PER_PARAM_DIM0 (<= 0: a 1-D tensor; must divide numel). */
 typedef struct {
   int64_t numel;
   int32_t unit;
   int32_t kind;
+  int64_t dim0;
 } zf_segment;
 
 typedef struct zf_plan zf_plan;  /* opaque, immutable once made */
@@ -96,13 +110,19 @@ typedef struct {
   int64_t psi_pad;             /* Psi' = sum_u P_u */
   int64_t n_units;
   int64_t max_unit_pad;        /* max_u P_u: elements of a ZeRO-3 unit buffer */
-  int32_t n_ranks, layout, stage, policy;  /* policy: 0 recompute, 1 materialize */
+  int64_t n_groups;            /* FSDP units (== n_units except ZF_PER_PARAM_DIM0) */
+  int64_t max_group_numel;     /* max unpadded elements of a group (zf_gather_cast) */
+  int32_t n_ranks, layout, stage;
+  int32_t policy;              /* where pass 2 finds the sums: 0 recomputed from
+                                  the replicas, 1 the workspace's fp32 copy,
+                                  2 the caller's fp32 gradient shard (FSDP2) */
   int64_t workspace_bytes;
-  /* bytes of model state per rank once backward has finished, stages 0..3
-   * ([L13] 2.3 and 3.5): 16*Psi, 4*Psi' + 12*Psi'/N, 2*Psi' + 14*Psi'/N,
-   * 16*Psi'/N; and the stage-3 peak while backward holds one unit's full
-   * params and grads ([L13] exercise 5). */
-  int64_t state_bytes[4];
+  /* bytes of model state per rank once backward has finished ([L13] 2.3 and
+   * 3.5): [0..3] stages 0..3 = 16*Psi, 4*Psi' + 12*Psi'/N, 2*Psi' + 14*Psi'/N,
+   * 16*Psi'/N; [4] FSDP2 with fp32 parameters ([MDT] 五.6: fp32 shard +
+   * fp32 grad shard + m + v) = 16*Psi'/N; and the stage-3 peak while
+   * backward holds one unit's full params and grads ([L13] exercise 5). */
+  int64_t state_bytes[5];
   int64_t stage3_peak_bytes;
   /* bytes one rank would send per step with ring collectives ([L13] 4.1,
    * 4.2): [0] DP all-reduce, [1] stage 1, [2] stage 2, [3] stage 3,
@@ -132,8 +152,19 @@ int zf_plan_flat(const zf_segment* segs, int64_t nseg, int32_t n_ranks, int32_t 
 /* Copy the plan's summary.  Errors: ZF_EINVAL. */
 int zf_plan_info(const zf_plan* plan, zf_plan_summary* out);
 
-/* Copy unit u's offsets and sizes.  Errors: ZF_EINVAL (u out of range). */
+/* Copy unit u's offsets and sizes.  Errors: ZF_EINVAL (u out of range).
+ * Under ZF_PER_PARAM_DIM0 the units are the parameters. */
 int zf_plan_unit(const zf_plan* plan, int64_t u, zf_unit_info* out);
+
+typedef struct {
+  int64_t first_unit;  /* its units are first_unit .. first_unit + n_units - 1 */
+  int64_t n_units;
+  int64_t numel;       /* unpadded elements: sum of the units' L */
+  int64_t padded;      /* padded elements: sum of the units' P */
+} zf_group_info;
+
+/* Copy FSDP unit (group) g's extent.  Errors: ZF_EINVAL. */
+int zf_plan_group(const zf_plan* plan, int64_t g, zf_group_info* out);
 
 /* Release a plan (NULL is allowed).  Only after the stream has passed every
  * call that used it. */
@@ -170,10 +201,16 @@ typedef struct {
   float* exp_avg;             /* Psi' fp32 */
   float* exp_avg_sq;          /* Psi' fp32 */
   void* params;               /* Psi' 16-bit: stages 0-2 the gathered full
-                                 buffer; stage 3 the N resident shards */
+                                 buffer; stage 3 the N resident shards; or
+                                 NULL: no 16-bit copy (fp32 parameters, as
+                                 FSDP2 keeps them) */
+  float* grad_shards;         /* NULL, or Psi' fp32: the ranks' resident fp32
+                                 gradient shards; pass 1 writes the sums
+                                 there and pass 2 reads them (required by
+                                 ZF_PER_PARAM_DIM0 plans) */
   int64_t numel;              /* elements of each per-element array above
                                  (grads[q], master, exp_avg, exp_avg_sq,
-                                 params); must be >= Psi' */
+                                 params, grad_shards); must be >= Psi' */
   void* workspace;            /* device workspace (may be NULL only if
                                  zf_workspace_bytes(plan) is 0) */
   int64_t workspace_size;     /* its size in bytes; must be >=
@@ -206,6 +243,17 @@ int zf_shard_step(const zf_plan* plan, const zf_hparams* hp, const zf_step_args*
  * grads[q] and of rs_out, >= Psi'.  Errors as zf_shard_step. */
 int zf_reduce_scatter(const zf_plan* plan, int32_t grad_dtype, const void* const* grads,
                       float* rs_out, int64_t numel, void* stream);
+
+/* FSDP2 unshard of group g ([MDT] 五.4: each rank's fp32 shards are cast to
+ * the parameter dtype, all-gathered and copied out into the full
+ * parameters): out holds the group's parameters end to end, unpadded, in
+ * model order; element e of parameter u is RNE16(master[O_u + e]) -- rank
+ * e / S_u's shard, offset e % S_u.  master: the padded-flat fp32 array of
+ * zf_shard_step (master_numel >= Psi', 16-byte aligned); out: out_numel >=
+ * the group's numel, 2-byte aligned.  Errors: ZF_EINVAL, ZF_EALIGN,
+ * ZF_EDTYPE, ZF_ESIZE, ZF_EHIP. */
+int zf_gather_cast(const zf_plan* plan, int64_t group, int32_t dtype, const float* master,
+                   int64_t master_numel, void* out, int64_t out_numel, void* stream);
 
 /* ZeRO-3 / FSDP unit gather ([L13] 3.3 and 5.1; [F9] unshard):
  * unit_buf[r*S_u + j] = shards[r][j] for every rank r < N and j < S_u, i.e.

@@ -14,7 +14,19 @@ from fsdp_sharded_mixed_amd import workloads as W
 
 def plan(w):
     numel, unit = w.seg_arrays()
+    if w.layout == W.PER_PARAM_DIM0:
+        return O.layout_dim0(numel, [s.rows for s in w.segments], w.n_ranks)
     return O.layout(numel, unit, w.n_ranks, w.layout)
+
+
+def groups(w):
+    """FSDP units as (first parameter, count) for a per-parameter layout."""
+    out = []
+    for i, s in enumerate(w.segments):
+        if not out or s.unit != w.segments[out[-1][0]].unit:
+            out.append([i, 0])
+        out[-1][1] += 1
+    return [tuple(g) for g in out]
 
 
 def hparams(w):
@@ -104,7 +116,12 @@ class OracleRun:
         self.m = [np.zeros(s_tot, np.float32) for _ in range(n)]
         self.v = [np.zeros(s_tot, np.float32) for _ in range(n)]
         init16 = O.narrow(w.param_dtype, np.concatenate(self.master))
-        if w.stage < 3:
+        self.grad_shards = None
+        if w.fp32_params:
+            # FSDP2: fp32 parameters (no 16-bit copy) and fp32 grad shards
+            self.full = self.shards = None
+            self.grad_shards = [np.zeros(s_tot, np.float32) for _ in range(n)]
+        elif w.stage < 3:
             self.full = rank_shards_to_padded(
                 units, [init16[r * s_tot:(r + 1) * s_tot] for r in range(n)])
             self.shards = None
@@ -121,6 +138,9 @@ class OracleRun:
             grads = replicas(self.w, self.units, self.psi_pad, self.step_no, self.st.loss_scale)
             if self.w.inject_step == self.step_no:
                 inject_inf(self.w, self.units, grads)
+        if self.w.fp32_params:
+            return O.fsdp2_step(self.w.grad_dtype, self.w.n_ranks, self.units, grads,
+                                self.master, self.m, self.v, self.grad_shards, self.hp, self.st)
         return O.zero_step(self.w.grad_dtype, self.w.param_dtype, self.w.n_ranks, self.units,
                            self.w.stage, grads, self.master, self.m, self.v, self.full,
                            self.shards, self.hp, self.st)

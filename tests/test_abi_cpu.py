@@ -51,8 +51,8 @@ def test_binding_covers_every_declared_call(zf):
 
 
 def _oracle_units(w):
-    numel, unit = w.seg_arrays()
-    return O.layout(numel, unit, w.n_ranks, w.layout)
+    from tests import oracle_inputs as OI
+    return OI.plan(w)
 
 
 @pytest.mark.parametrize("name", list(W.ALL))
@@ -66,7 +66,7 @@ def test_plan_matches_oracle_layout(zf, name):
         assert (mine.L, mine.P, mine.S, mine.O, mine.lam) == (ref["L"], ref["P"], ref["S"],
                                                                 ref["O"], ref["lam"])
     assert s.max_unit_pad == units["P"].max()
-    for stage in range(4):
+    for stage in range(5):
         ab, peak = O.ledger(units, w.n_ranks, stage)
         assert s.state_bytes[stage] == ab
         if stage == 3:
@@ -94,6 +94,38 @@ def test_plan_bruteforce_small(zf):
         units, psi, psi_pad = O.layout(lens, uid, n, layout)
         assert plan.summary.psi_pad == psi_pad
         assert [(u.P, u.S, u.O) for u in plan.units] == [(u["P"], u["S"], u["O"]) for u in units]
+
+
+def test_fsdp2_plan_matches_oracle(zf):
+    """ZF_PER_PARAM_DIM0 units and groups against the oracle's dim-0 layout."""
+    rng = np.random.default_rng(6)
+    for _ in range(100):
+        n = int(rng.integers(1, 9))
+        k = int(rng.integers(1, 8))
+        rows = [int(x) for x in rng.integers(1, 30, k)]
+        cols = [int(x) for x in rng.integers(1, 6, k)]
+        ngroups = int(rng.integers(1, k + 1))
+        cuts = sorted(rng.choice(range(1, k), ngroups - 1, replace=False)) if k > 1 else []
+        gid, g = [], 0
+        for i in range(k):
+            if g < len(cuts) and i == cuts[g]:
+                g += 1
+            gid.append(g)
+        segs = [(r * c, gi, 0, r) for r, c, gi in zip(rows, cols, gid)]
+        plan = zf.plan_flat(segs, n, zf.PER_PARAM_DIM0, 3)
+        units, psi, psi_pad = O.layout_dim0([r * c for r, c in zip(rows, cols)], rows, n)
+        assert plan.summary.psi_pad == psi_pad and plan.summary.policy == 2
+        assert [(u.L, u.P, u.S, u.O, u.lam) for u in plan.units] == \
+            [(u["L"], u["P"], u["S"], u["O"], u["lam"]) for u in units]
+        assert plan.summary.n_groups == len(set(gid))
+        for gi, grp in enumerate(plan.groups):
+            members = [i for i in range(k) if gid[i] == gi]
+            assert (grp.first_unit, grp.n_units) == (members[0], len(members))
+            assert grp.numel == sum(rows[i] * cols[i] for i in members)
+        ab, _ = O.ledger(units, n, 4)
+        assert plan.summary.state_bytes[4] == ab
+    with pytest.raises(zf.ZfError):
+        zf.plan_flat([(10, 0, 0, 3)], 2, zf.PER_PARAM_DIM0, 3)  # 3 rows do not divide 10
 
 
 def test_policy_and_workspace(zf):
@@ -143,12 +175,13 @@ def test_step_argument_errors_enqueue_nothing(zf):
 
     def args(**kw):
         d = dict(grad_dtype=1, param_dtype=1, grads=grads, master=ok, exp_avg=ok, exp_avg_sq=ok,
-                 params=ok, numel=100, workspace=ok, workspace_size=need, state=ok,
-                 phase_events=None)
+                 params=ok, grad_shards=None, numel=100, workspace=ok, workspace_size=need,
+                 state=ok, phase_events=None)
         d.update(kw)
         return Z.StepArgs(d["grad_dtype"], d["param_dtype"], d["grads"], d["master"],
-                          d["exp_avg"], d["exp_avg_sq"], d["params"], d["numel"],
-                          d["workspace"], d["workspace_size"], d["state"], d["phase_events"])
+                          d["exp_avg"], d["exp_avg_sq"], d["params"], d["grad_shards"],
+                          d["numel"], d["workspace"], d["workspace_size"], d["state"],
+                          d["phase_events"])
 
     step = lambda a, p=plan.handle, h=hp: Z.lib.zf_shard_step(p, C.byref(h), C.byref(a), None)
     assert step(args(), p=None) == -1
@@ -165,6 +198,17 @@ def test_step_argument_errors_enqueue_nothing(zf):
     assert step(args(workspace_size=need - 1)) == -4
     assert step(args(numel=99)) == -4
     assert step(args(), h=Z.hparams(1e-3, beta1=1.0)) == -1
+    assert step(args(grad_shards=ok + 4)) == -2
+    # an FSDP2 plan needs the fp32 gradient shards
+    p2 = Z.plan_flat([(100, 0, 0, 10)], 2, Z.PER_PARAM_DIM0, 3)
+    assert p2.summary.policy == 2
+    assert Z.lib.zf_shard_step(p2.handle, C.byref(hp),
+                               C.byref(args(workspace_size=Z.workspace_bytes(p2))), None) == -1
+    assert Z.lib.zf_gather_cast(p2.handle, 1, 1, ok, 100, ok, 100, None) == -1
+    assert Z.lib.zf_gather_cast(p2.handle, 0, 3, ok, 100, ok, 100, None) == -3
+    assert Z.lib.zf_gather_cast(p2.handle, 0, 1, ok + 4, 100, ok, 100, None) == -2
+    assert Z.lib.zf_gather_cast(p2.handle, 0, 1, ok, 99, ok, 100, None) == -4
+    assert Z.lib.zf_gather_cast(p2.handle, 0, 1, ok, 100, ok, 99, None) == -4
     assert Z.lib.zf_shard_step(plan.handle, None, C.byref(args()), None) == -1
     assert Z.lib.zf_reduce_scatter(plan.handle, 9, grads, ok, 100, None) == -3
     assert Z.lib.zf_reduce_scatter(plan.handle, 1, grads, ok + 4, 100, None) == -2

@@ -54,9 +54,10 @@ def check_samples(dev, so, pidx, what):
     G.assert_state_close(f"{what} master", m, so.p)
     G.assert_state_close(f"{what} exp_avg", ea, so.m)
     G.assert_state_close(f"{what} exp_avg_sq", eas, so.v)
-    prm = take(dev.params.view(torch.int16), pidx).numpy().view(np.uint16)
-    ref = O.narrow(dev.w.param_dtype, so.p)
-    assert G.ulp16_distance(prm, ref).max() <= 1, f"{what} params"
+    if dev.params is not None:
+        prm = take(dev.params.view(torch.int16), pidx).numpy().view(np.uint16)
+        ref = O.narrow(dev.w.param_dtype, so.p)
+        assert G.ulp16_distance(prm, ref).max() <= 1, f"{what} params"
     return float((m.view(np.uint32) == so.p.view(np.uint32)).mean())
 
 
@@ -97,9 +98,29 @@ def run_workload(R, name, rs_check_step=1):
         G.say(f"  step {k}: skipped={res_d.skipped} t={res_d.t} S={res_d.scale_used}->"
               f"{res_d.scale_next} norm={res_d.norm:.6f} (oracle {res_o.norm:.6f}) "
               f"coef={res_d.coef:.6f} exact-share={share:.4f}")
-        if w.stage == 3:
+        if w.fp32_params:
+            check_group_gathers(dev, so, idx, w)
+            if not res_d.skipped:
+                acc = O.regen_acc(w.grad_dtype, w.n_ranks, w.seed, k, w.sigma, scale, idx)
+                got = take(dev.grad_shards, pidx).numpy()
+                assert np.array_equal(got.view(np.uint32), acc.view(np.uint32)), "grad shards"
+        elif w.stage == 3:
             check_unit_gathers(dev, so, idx, w)
     return dev, trace
+
+
+def check_group_gathers(dev, so, idx, w):
+    """FSDP2: cast-gather every group in forward order and check the sampled
+    elements (a group buffer holds its parameters unpadded, in order)."""
+    ref16 = O.narrow(w.param_dtype, so.p)
+    for g, info in enumerate(dev.plan.groups):
+        buf = dev.gather_cast(g)
+        lam0 = dev.plan.units[info.first_unit].lam
+        sel = (idx >= lam0) & (idx < lam0 + info.numel)
+        if sel.any():
+            k = torch.from_numpy(idx[sel] - lam0).to(buf.device)
+            got = buf.view(torch.int16)[k].cpu().numpy().view(np.uint16)
+            assert G.ulp16_distance(got, ref16[sel]).max() <= 1, f"group {g}"
 
 
 def check_unit_gathers(dev, so, idx, w):
@@ -143,6 +164,15 @@ def test_llama2b_zero3(R):
     and per-unit gathers into one reused buffer."""
     dev, trace = run_workload(R, "llama-2.1b-n2-zero3")
     assert len(dev.plan.units) == 34
+
+
+def test_llama2b_fsdp2(R):
+    """2.1B decoder under FSDP2: per-parameter dim-0 shards over N = 2, fp32
+    parameters, the reduce-scatter sums in resident fp32 gradient shards,
+    34 cast-gathers per step."""
+    dev, trace = run_workload(R, "llama-2.1b-n2-fsdp2", rs_check_step=0)
+    assert len(dev.plan.groups) == 34 and len(dev.plan.units) == 291
+    assert all(t[1] == 0 for t in trace)
 
 
 def test_llama4b_n2_injected_overflow(R):
