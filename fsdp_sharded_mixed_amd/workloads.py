@@ -19,9 +19,13 @@ Shapes:
   * FSDP units for the ZeRO-3 and FSDP2 workloads: {embedding}, one unit
     per decoder layer, {final norm, LM head} (the torchtitan FSDP2 wrapping
     of the Megatron / DeepSpeed / torchtitan source guide, ch. 五.4).
+  * Gradient buckets for the accumulation workloads: Megatron's buffer holds
+    the parameters last layer first and cuts it into buckets of
+    max(40M, 1M * N) elements (source guide, ch. 三.3).
 
 Inputs are a pure function of (seed, stream, logical index): a replica's
-gradient for element i at step k comes from stream grad_stream(k, replica),
+gradient for element i at step k (micro-batch a) comes from stream
+grad_stream(k, replica, a),
 the fp32 master initialisation from STREAM_MASTER, and the index that receives
 an injected +inf from the first output of STREAM_INJECT.  The generator is
 splitmix64 feeding an Irwin-Hall(12) normal; both the HIP input library and
@@ -39,10 +43,15 @@ STREAM_MASTER = 1 << 40
 STREAM_INJECT = 2 << 40
 
 
-def grad_stream(step: int, replica: int) -> int:
-    """Stream id of replica `replica`'s gradient at step `step` (steps count from 1)."""
-    assert step >= 1 and 0 <= replica < (1 << 20) and step < (1 << 20)
-    return (step << 20) | replica
+ACCUM_REDUCE_EACH, ACCUM_NO_SYNC = 0, 1
+
+
+def grad_stream(step: int, replica: int, micro: int = 0) -> int:
+    """Stream id of replica `replica`'s gradient in micro-batch `micro` of
+    step `step` (steps count from 1, micro-batches from 0; a step without
+    accumulation is micro-batch 0)."""
+    assert 1 <= step < (1 << 20) and 0 <= replica < 256 and 0 <= micro < 4096
+    return (step << 20) | (micro << 8) | replica
 
 
 @dataclass
@@ -81,7 +90,22 @@ class Workload:
     inject_step: Optional[int] = None      # +inf injected into one replica at this step
     inject_replica: int = 1
     fp32_params: bool = False              # FSDP2: the fp32 shard is the parameter
+    # gradient accumulation over n_micro micro-batches: ACCUM_REDUCE_EACH
+    # reduce-scatters every micro-batch into the fp32 gradient shard,
+    # ACCUM_NO_SYNC accumulates each replica locally in fp32 and reduces once
+    n_micro: int = 1
+    accum_mode: int = ACCUM_REDUCE_EACH
+    # None: FSDP units from the segments' unit ids.  Otherwise Megatron
+    # gradient buckets over the segments in the given order (0: the default
+    # bucket size max(40M, 1M * N)); each side computes the bucket ids itself
+    bucket_numel: Optional[int] = None
     extra: dict = field(default_factory=dict)
+
+    @property
+    def backward_rs(self) -> bool:
+        """The gradients are reduce-scattered bucket by bucket during backward
+        and the step consumes the reduced fp32 gradient shards."""
+        return self.bucket_numel is not None or self.n_micro > 1
 
     @property
     def psi(self) -> int:
@@ -204,6 +228,35 @@ def llama4b() -> Workload:
         lr=1e-4, steps=4, seed=5, inject_step=2, inject_replica=1)
 
 
+def _h2048_buckets(layers):
+    """Megatron's buffer order: parameters last layer first (the order in
+    which backward produces their gradients); bucket ids assigned later."""
+    return list(reversed(_h2048(layers)))
+
+
+def llama654m_buckets(mode=ACCUM_REDUCE_EACH) -> Workload:
+    """The 654M decoder in Megatron's gradient buffer (reverse order, default
+    40M-element buckets padded to N) with four accumulated micro-batches:
+    every bucket is reduce-scattered as its gradients arrive, into fp32
+    gradient shards (or, no_sync, each replica accumulates in fp32 and the
+    buckets are reduced once after the last micro-batch); then the step."""
+    n, a = 2, 4
+    psi = sum(s.numel for s in _h2048(8))
+    tag = "buckets" if mode == ACCUM_REDUCE_EACH else "nosync"
+    how = ("reduce-scatter of every micro-batch into fp32 grad shards"
+           if mode == ACCUM_REDUCE_EACH else
+           "no_sync fp32 local accumulation, one reduce-scatter at the last micro-batch")
+    return Workload(
+        name=f"llama-654m-n2-{tag}-a4",
+        description="Llama-style decoder h2048/i8192/32h/8kv/8L/V40960, Psi=654,346,240, "
+                    "Megatron buffer order with 40M-element gradient buckets, N=2, 4 "
+                    f"micro-batches of bf16 grads, {how}, global norm about 3",
+        segments=_h2048_buckets(8), n_ranks=n, layout=PER_UNIT, stage=2,
+        grad_dtype=BF16, param_dtype=BF16, sigma=3.0 * (n / (psi * a)) ** 0.5, loss_scale=1.0,
+        dynamic=False, lr=1e-4, steps=3, seed=6 if mode == ACCUM_REDUCE_EACH else 7,
+        n_micro=a, accum_mode=mode, bucket_numel=0)
+
+
 ALL = {
     "tiny": tiny,
     "llama-73m-n8": llama73m,
@@ -211,6 +264,8 @@ ALL = {
     "llama-2.1b-n2-zero3": llama2b_z3,
     "llama-2.1b-n2-fsdp2": llama2b_fsdp2,
     "llama-4.06b-n2": llama4b,
+    "llama-654m-n2-buckets-a4": llama654m_buckets,
+    "llama-654m-n2-nosync-a4": lambda: llama654m_buckets(ACCUM_NO_SYNC),
 }
 
 

@@ -99,6 +99,17 @@ def lib():
                                        C.POINTER(Hparams), C.POINTER(ScaleState),
                                        C.POINTER(Result)]),
             "or_gather_unit": (C.c_int, [vp, i64, i32, i64, vp, vp]),
+            "or_step_reduced": (C.c_int, [i32, i32, vp, i64, i32, vp, vp, vp, vp, vp, vp,
+                                          C.POINTER(Hparams), C.POINTER(ScaleState),
+                                          C.POINTER(Result)]),
+            "or_rs_accumulate": (C.c_int, [i32, i32, vp, i64, i64, vp, vp, i32]),
+            "or_local_accumulate": (C.c_int, [i32, i64, vp, vp, i32]),
+            "or_bucket_assign": (C.c_int, [vp, i64, i32, i64, vp, C.POINTER(i64)]),
+            "or_regen_accum_sumsq": (C.c_int, [i32, i32, i32, i32, u64, i64, dbl, dbl, i64, i64,
+                                               C.POINTER(Inject), C.POINTER(dbl),
+                                               C.POINTER(i32)]),
+            "or_regen_accum_acc": (C.c_int, [i32, i32, i32, i32, u64, i64, dbl, dbl, i64, vp,
+                                             C.POINTER(Inject), vp]),
             "or_dp_step": (C.c_int, [i32, i32, i32, i64, vp, vp, vp, vp, vp,
                                      C.POINTER(Hparams), C.POINTER(ScaleState),
                                      C.POINTER(Result)]),
@@ -269,6 +280,50 @@ def zero_step(grad_dtype, param_dtype, n_ranks, units, stage, grads, master, exp
     return res
 
 
+def step_reduced(param_dtype, n_ranks, units, stage, acc, master, exp_avg, exp_avg_sq,
+                 params_full, param_shards, hp, st):
+    """The optimizer side of a step from already reduced fp32 gradient shards."""
+    units = np.ascontiguousarray(units, UNIT_DTYPE)
+    res = Result()
+    pf = _p(params_full) if params_full is not None else None
+    ps = _ptrs(param_shards) if param_shards is not None else None
+    _check(lib().or_step_reduced(param_dtype, n_ranks, _p(units), len(units), stage, _ptrs(acc),
+                                 _ptrs(master), _ptrs(exp_avg), _ptrs(exp_avg_sq), pf, ps,
+                                 C.byref(hp), C.byref(st), C.byref(res)), "step_reduced")
+    return res
+
+
+F32 = 3
+
+
+def rs_accumulate(grad_dtype, n_ranks, units, u, grads, shards, accumulate):
+    """Bucket (unit) u's reduce-scatter of one micro-batch into fp32 shards;
+    grads are 16-bit replicas, or fp32 ones when grad_dtype is F32."""
+    units = np.ascontiguousarray(units, UNIT_DTYPE)
+    gt = np.float32 if grad_dtype == F32 else np.uint16
+    grads = [np.ascontiguousarray(g, gt) for g in grads]
+    _check(lib().or_rs_accumulate(grad_dtype, n_ranks, _p(units), len(units), u, _ptrs(grads),
+                                  _ptrs(shards), int(accumulate)), "rs_accumulate")
+
+
+def local_accumulate(grad_dtype, grad, acc, accumulate):
+    """acc (fp32, in place) += widened 16-bit grad, or = it when not accumulating."""
+    grad = np.ascontiguousarray(grad, np.uint16)
+    assert acc.dtype == np.float32 and acc.flags.c_contiguous and acc.size == grad.size
+    _check(lib().or_local_accumulate(grad_dtype, grad.size, _p(grad), _p(acc), int(accumulate)),
+           "local_accumulate")
+
+
+def bucket_assign(numel, n_ranks, bucket_numel=0):
+    """Megatron bucket id of every segment, and the bucket count."""
+    numel = np.ascontiguousarray(numel, np.int64)
+    out = np.empty(numel.size, np.int32)
+    nb = C.c_int64()
+    _check(lib().or_bucket_assign(_p(numel), numel.size, n_ranks, int(bucket_numel), _p(out),
+                                  C.byref(nb)), "bucket_assign")
+    return out, nb.value
+
+
 def gather_unit(units, n_ranks, u, param_shards):
     units = np.ascontiguousarray(units, UNIT_DTYPE)
     out = np.empty(int(units[u]["P"]), np.uint16)
@@ -301,4 +356,23 @@ def regen_acc(dtype, n_ranks, seed, step, sigma, scale, idx, inject=None):
     inj = C.byref(inject) if inject is not None else None
     _check(lib().or_regen_acc(dtype, n_ranks, seed, step, sigma, scale, idx.size, _p(idx), inj,
                               _p(out)), "regen_acc")
+    return out
+
+
+def regen_accum_sumsq(dtype, n_ranks, n_micro, mode, seed, step, sigma, scale, i0, i1,
+                      inject=None):
+    ss, nf = C.c_double(), C.c_int32()
+    inj = C.byref(inject) if inject is not None else None
+    _check(lib().or_regen_accum_sumsq(dtype, n_ranks, n_micro, mode, seed, step, sigma, scale,
+                                      int(i0), int(i1), inj, C.byref(ss), C.byref(nf)),
+           "regen_accum_sumsq")
+    return ss.value, nf.value
+
+
+def regen_accum_acc(dtype, n_ranks, n_micro, mode, seed, step, sigma, scale, idx, inject=None):
+    idx = np.ascontiguousarray(idx, np.int64)
+    out = np.empty(idx.size, np.float32)
+    inj = C.byref(inject) if inject is not None else None
+    _check(lib().or_regen_accum_acc(dtype, n_ranks, n_micro, mode, seed, step, sigma, scale,
+                                    idx.size, _p(idx), inj, _p(out)), "regen_accum_acc")
     return out

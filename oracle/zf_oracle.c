@@ -151,9 +151,11 @@ void or_gen32(float* dst, int64_t n, uint64_t seed, uint64_t stream, int64_t log
   for (i = 0; i < n; ++i) dst[i] = or_normal_z(st, logical_base + i) * sf;
 }
 
-/* Gradient stream of (step, replica); steps count from 1. */
-static uint64_t grad_stream(int64_t step, int64_t replica) {
-  return ((uint64_t)step << 20) | (uint64_t)replica;
+/* Gradient stream of (step, micro-batch, replica); steps count from 1,
+ * micro-batches from 0 (a step without accumulation is micro-batch 0),
+ * replicas < 256, micro-batches < 4096. */
+static uint64_t grad_stream(int64_t step, int64_t micro, int64_t replica) {
+  return ((uint64_t)step << 20) | ((uint64_t)micro << 8) | (uint64_t)replica;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -420,10 +422,11 @@ void or_adamw_array(int64_t n, const float* acc, const or_scalars* sc, float* p,
   }
 }
 
-/* One emulated ZeRO step for all N ranks ([L13] 3.1 steps 3-6, 3.2, 3.3;
- * [MDT] 四.3 step order).
- *   1. reduce-scatter: each rank gets the fixed-order sum over its shard;
- *   2. overflow: any non-finite reduced value, padding included;
+/* The optimizer side of one step from already reduce-scattered gradients
+ * ([L13] 3.1 steps 4-6; [MDT] 四.3 step order): acc[r] is rank r's fp32
+ * gradient shard (the fixed-order sums over ranks, accumulated over
+ * micro-batches when there are several).
+ *   2. overflow: any non-finite value of any shard, padding included;
  *   3. squared norm: sum of (double)acc^2 over the real elements in logical
  *      order (unit by unit, ranks in order), so the value does not depend on
  *      the layout; the padding is zero by contract and would add nothing;
@@ -431,32 +434,23 @@ void or_adamw_array(int64_t n, const float* acc, const or_scalars* sc, float* p,
  *   7. each rank runs AdamW on its shard (padding included: zero stays zero);
  *   8. each rank casts its shard to 16 bits; stages 0-2 place it in the full
  *      padded buffer (the post-update all-gather, [L13] 3.1 step 6), stage 3
- *      keeps it as the rank's resident shard ([L13] exercise 4).
+ *      keeps it as the rank's resident shard ([L13] exercise 4), unless
+ *      param_shards is NULL: fp32 parameters (FSDP2, [MDT] 五.6), no copy.
  * master/exp_avg/exp_avg_sq/param_shards[r] are rank r's shard buffers:
  * sum_u S_u elements, unit u at offset M_u.                               */
-int or_zero_step(int32_t grad_dtype, int32_t param_dtype, int32_t n_ranks, const or_unit* units,
-                 int64_t n_units, int32_t stage, const uint16_t* const* grads,
-                 float* const* master, float* const* exp_avg, float* const* exp_avg_sq,
-                 uint16_t* params_full, uint16_t* const* param_shards, const or_hparams* hp,
-                 or_scale_state* st, or_result* res) {
+int or_step_reduced(int32_t param_dtype, int32_t n_ranks, const or_unit* units, int64_t n_units,
+                    int32_t stage, float* const* acc, float* const* master,
+                    float* const* exp_avg, float* const* exp_avg_sq, uint16_t* params_full,
+                    uint16_t* const* param_shards, const or_hparams* hp, or_scale_state* st,
+                    or_result* res) {
   int64_t s_tot = 0, u, j, k;
   int32_t r, overflow = 0;
   double ss = 0.0;
-  float** acc;
   or_scalars sc;
-  int rc = 0;
-  if (!units || n_units < 1 || !grads || !master || !exp_avg || !exp_avg_sq || !hp || !st || !res)
+  if (!units || n_units < 1 || !acc || !master || !exp_avg || !exp_avg_sq || !hp || !st || !res)
     return -1;
   if (stage < 3 && !params_full) return -1;
-  if (stage == 3 && !param_shards) return -1;
   for (u = 0; u < n_units; ++u) s_tot += units[u].S;
-  acc = (float**)calloc((size_t)n_ranks, sizeof(float*));
-  if (!acc) return -2;
-  for (r = 0; r < n_ranks; ++r) {
-    acc[r] = (float*)malloc((size_t)(s_tot > 0 ? s_tot : 1) * sizeof(float));
-    if (!acc[r]) { rc = -2; goto done; }
-  }
-  or_reduce_scatter(grad_dtype, n_ranks, units, n_units, grads, acc);
 
   for (r = 0; r < n_ranks; ++r)
     for (k = 0; k < s_tot; ++k)
@@ -472,11 +466,12 @@ int or_zero_step(int32_t grad_dtype, int32_t param_dtype, int32_t n_ranks, const
   }
 
   or_finish(ss, overflow, n_ranks, hp, st, &sc, res);
-  if (res->skipped) goto done;
+  if (res->skipped) return 0;
 
   for (r = 0; r < n_ranks; ++r)
     or_adamw_array(s_tot, acc[r], &sc, master[r], exp_avg[r], exp_avg_sq[r]);
 
+  if (stage == 3 && !param_shards) return 0;  /* fp32 parameters: no 16-bit copy */
   for (r = 0; r < n_ranks; ++r) {
     for (u = 0; u < n_units; ++u) {
       const or_unit* U = &units[u];
@@ -489,10 +484,122 @@ int or_zero_step(int32_t grad_dtype, int32_t param_dtype, int32_t n_ranks, const
       }
     }
   }
-done:
+  return 0;
+}
+
+/* One emulated ZeRO step for all N ranks ([L13] 3.1 steps 3-6, 3.2, 3.3):
+ * the reduce-scatter (each rank gets the fixed-order sum over its shard of
+ * every unit), then the optimizer side (or_step_reduced). */
+int or_zero_step(int32_t grad_dtype, int32_t param_dtype, int32_t n_ranks, const or_unit* units,
+                 int64_t n_units, int32_t stage, const uint16_t* const* grads,
+                 float* const* master, float* const* exp_avg, float* const* exp_avg_sq,
+                 uint16_t* params_full, uint16_t* const* param_shards, const or_hparams* hp,
+                 or_scale_state* st, or_result* res) {
+  int64_t s_tot = 0, u;
+  int32_t r;
+  float** acc;
+  int rc;
+  if (!units || n_units < 1 || !grads) return -1;
+  for (u = 0; u < n_units; ++u) s_tot += units[u].S;
+  acc = (float**)calloc((size_t)n_ranks, sizeof(float*));
+  if (!acc) return -2;
+  rc = 0;
+  for (r = 0; r < n_ranks && rc == 0; ++r) {
+    acc[r] = (float*)malloc((size_t)(s_tot > 0 ? s_tot : 1) * sizeof(float));
+    if (!acc[r]) rc = -2;
+  }
+  if (rc == 0) {
+    or_reduce_scatter(grad_dtype, n_ranks, units, n_units, grads, acc);
+    rc = or_step_reduced(param_dtype, n_ranks, units, n_units, stage, acc, master, exp_avg,
+                         exp_avg_sq, params_full, param_shards, hp, st, res);
+  }
   for (r = 0; r < n_ranks; ++r) free(acc[r]);
   free(acc);
   return rc;
+}
+
+/* One element of a gradient buffer: 16-bit (widened exactly) or binary32. */
+static float grad_at(int32_t dtype, const void* g, int64_t p) {
+  if (dtype == OR_F32) return ((const float*)g)[p];
+  return widen(dtype, ((const uint16_t*)g)[p]);
+}
+
+/* Backward-side reduce-scatter of one bucket as its gradients arrive
+ * ([L13] 3.2: with buckets, one reduce-scatter per bucket during backward;
+ * [MDT] 三.3: each bucket padded to a multiple of the DP size and split
+ * evenly, rank r owning the r-th piece; 四.3: IPG buckets reduced to their
+ * owners).  Unit u of the plan is the bucket; shards[r] are rank r's shard
+ * buffers (unit u at offset M_u).
+ * Gradient accumulation ([L13] 5.6 and [MDT] 五.7: either every micro-batch
+ * is reduce-scattered and the result added to the sharded gradient, or the
+ * full gradients are accumulated locally and reduced once at the last
+ * micro-batch): the micro-batch's fixed-order sum over ranks is formed
+ * first and then added to the shard (reading: the reduced tensor is
+ * produced by the collective before the shard's gradient accumulates it);
+ * accumulate == 0 stores the sum, as the first micro-batch does.
+ * grad_dtype OR_F32 takes binary32 replicas: the locally accumulated fp32
+ * gradients of the no_sync scheme ([MDT] 三.3: fp32 main_grad buffers
+ * reduced in fp32).                                                       */
+int or_rs_accumulate(int32_t grad_dtype, int32_t n_ranks, const or_unit* units, int64_t n_units,
+                     int64_t u, const void* const* grads, float* const* shards,
+                     int32_t accumulate) {
+  int64_t j;
+  int32_t r, q;
+  const or_unit* U;
+  if (!units || !grads || !shards || u < 0 || u >= n_units) return -1;
+  if (grad_dtype != OR_F16 && grad_dtype != OR_BF16 && grad_dtype != OR_F32) return -1;
+  U = &units[u];
+  for (r = 0; r < n_ranks; ++r) {
+    for (j = 0; j < U->S; ++j) {
+      int64_t p = U->O + (int64_t)r * U->S + j;
+      float sum = grad_at(grad_dtype, grads[0], p);
+      for (q = 1; q < n_ranks; ++q) sum = sum + grad_at(grad_dtype, grads[q], p);
+      shards[r][U->M + j] = accumulate ? shards[r][U->M + j] + sum : sum;
+    }
+  }
+  return 0;
+}
+
+/* Local gradient accumulation of one replica under no_sync ([MDT] 三.3: the
+ * backward hook adds each micro-batch's gradient into the parameter's fp32
+ * main_grad; no communication until the last micro-batch): acc[i] =
+ * acc[i] + f32(grad[i]), or f32(grad[i]) for the first micro-batch. */
+int or_local_accumulate(int32_t grad_dtype, int64_t n, const uint16_t* grad, float* acc,
+                        int32_t accumulate) {
+  int64_t i;
+  if (!grad || !acc || n < 0) return -1;
+  if (grad_dtype != OR_F16 && grad_dtype != OR_BF16) return -1;
+  for (i = 0; i < n; ++i) {
+    float g = widen(grad_dtype, grad[i]);
+    acc[i] = accumulate ? acc[i] + g : g;
+  }
+  return 0;
+}
+
+/* Megatron's gradient buckets ([MDT] 三.3): parameters in buffer order
+ * are grouped into buckets of bucket_numel elements, by default
+ * max(40,000,000, 1,000,000 * dp_size).  Reading: parameters are not split;
+ * a bucket is closed as soon as its element count reaches bucket_numel, and
+ * the last bucket takes whatever remains.  unit_out[s] receives segment s's
+ * bucket id (0, 0, .., 1, ..).                                           */
+int or_bucket_assign(const int64_t* seg_numel, int64_t nseg, int32_t n_ranks,
+                     int64_t bucket_numel, int32_t* unit_out, int64_t* n_buckets) {
+  int64_t s, fill = 0, B;
+  int32_t cur = 0;
+  if (!seg_numel || !unit_out || !n_buckets || nseg < 1 || n_ranks < 1) return -1;
+  B = bucket_numel > 0 ? bucket_numel : 1000000LL * n_ranks;
+  if (bucket_numel <= 0 && B < 40000000LL) B = 40000000LL;
+  for (s = 0; s < nseg; ++s) {
+    if (seg_numel[s] < 1) return -1;
+    unit_out[s] = cur;
+    fill += seg_numel[s];
+    if (fill >= B && s + 1 < nseg) {
+      cur += 1;
+      fill = 0;
+    }
+  }
+  *n_buckets = (int64_t)cur + 1;
+  return 0;
 }
 
 /* ZeRO-3 / FSDP gather of one unit before it is used ([L13] 3.3 and 5.1
@@ -607,45 +714,82 @@ int or_dp_step(int32_t grad_dtype, int32_t param_dtype, int32_t n_ranks, int64_t
  * overrides one (step, replica, index) with given 16-bit bits.           */
 
 #define OR_MAX_REPLICAS 64
+#define OR_MAX_MICRO 16
 
-/* Starting states of the N gradient streams of `step`. */
-static int grad_states(uint64_t seed, int64_t step, int32_t n_ranks, uint64_t* st) {
-  int32_t q;
-  if (n_ranks < 1 || n_ranks > OR_MAX_REPLICAS) return -1;
-  for (q = 0; q < n_ranks; ++q) st[q] = or_stream_state(seed, grad_stream(step, q));
+/* Starting states of the gradient streams of `step`: st[a*N + q] for
+ * micro-batch a, replica q. */
+static int grad_states(uint64_t seed, int64_t step, int32_t n_micro, int32_t n_ranks,
+                       uint64_t* st) {
+  int32_t q, a;
+  if (n_ranks < 1 || n_ranks > OR_MAX_REPLICAS || n_micro < 1 || n_micro > OR_MAX_MICRO)
+    return -1;
+  for (a = 0; a < n_micro; ++a)
+    for (q = 0; q < n_ranks; ++q)
+      st[a * n_ranks + q] = or_stream_state(seed, grad_stream(step, a, q));
   return 0;
 }
 
-static float regen_acc_one(int32_t dtype, int32_t n_ranks, const uint64_t* st, int64_t step,
-                           float sf, float kf, int64_t i, const or_inject* inj) {
+/* Replica q's widened gradient at index i in micro-batch a (an injection
+ * applies to micro-batch 0). */
+static float regen_grad(int32_t dtype, int32_t n_ranks, const uint64_t* st, int64_t step,
+                        float sf, float kf, int64_t i, int32_t a, int32_t q,
+                        const or_inject* inj) {
+  uint16_t h;
+  if (a == 0 && inj && inj->step == step && inj->replica == q && inj->index == i) {
+    h = inj->bits;
+  } else {
+    float x = or_normal_z(st[a * n_ranks + q], i) * sf;
+    x = x * kf;
+    h = narrow(dtype, x);
+  }
+  return widen(dtype, h);
+}
+
+/* The reduced (and accumulated) gradient of logical index i.  mode 0:
+ * every micro-batch is reduce-scattered and added to the shard
+ * (or_rs_accumulate per micro-batch); mode 1: no_sync, each replica
+ * accumulates in fp32 (or_local_accumulate) and the fp32 buffers are
+ * summed once in rank order.  With one micro-batch both are the plain
+ * reduce-scatter sum. */
+static float regen_acc_one(int32_t dtype, int32_t n_ranks, int32_t n_micro, int32_t mode,
+                           const uint64_t* st, int64_t step, float sf, float kf, int64_t i,
+                           const or_inject* inj) {
   float acc = 0.0f;
-  int32_t q;
-  for (q = 0; q < n_ranks; ++q) {
-    uint16_t h;
-    if (inj && inj->step == step && inj->replica == q && inj->index == i) {
-      h = inj->bits;
-    } else {
-      float x = or_normal_z(st[q], i) * sf;
-      x = x * kf;
-      h = narrow(dtype, x);
+  int32_t q, a;
+  if (mode == 0) {
+    for (a = 0; a < n_micro; ++a) {
+      float sum = 0.0f;
+      for (q = 0; q < n_ranks; ++q) {
+        float g = regen_grad(dtype, n_ranks, st, step, sf, kf, i, a, q, inj);
+        sum = (q == 0) ? g : sum + g;
+      }
+      acc = (a == 0) ? sum : acc + sum;
     }
-    acc = (q == 0) ? widen(dtype, h) : acc + widen(dtype, h);
+  } else {
+    for (q = 0; q < n_ranks; ++q) {
+      float loc = 0.0f;
+      for (a = 0; a < n_micro; ++a) {
+        float g = regen_grad(dtype, n_ranks, st, step, sf, kf, i, a, q, inj);
+        loc = (a == 0) ? g : loc + g;
+      }
+      acc = (q == 0) ? loc : acc + loc;
+    }
   }
   return acc;
 }
 
-int or_regen_sumsq(int32_t grad_dtype, int32_t n_ranks, uint64_t seed, int64_t step, double sigma,
-                   double scale, int64_t i0, int64_t i1, const or_inject* inj, double* sumsq,
-                   int32_t* nonfinite) {
+int or_regen_accum_sumsq(int32_t grad_dtype, int32_t n_ranks, int32_t n_micro, int32_t mode,
+                         uint64_t seed, int64_t step, double sigma, double scale, int64_t i0,
+                         int64_t i1, const or_inject* inj, double* sumsq, int32_t* nonfinite) {
   int64_t i;
   double ss = 0.0;
   int32_t nf = 0;
   float sf = (float)sigma, kf = (float)scale;
-  uint64_t st[OR_MAX_REPLICAS];
-  if (!sumsq || !nonfinite || i1 < i0) return -1;
-  if (grad_states(seed, step, n_ranks, st) != 0) return -1;
+  uint64_t st[OR_MAX_REPLICAS * OR_MAX_MICRO];
+  if (!sumsq || !nonfinite || i1 < i0 || (mode != 0 && mode != 1)) return -1;
+  if (grad_states(seed, step, n_micro, n_ranks, st) != 0) return -1;
   for (i = i0; i < i1; ++i) {
-    float a = regen_acc_one(grad_dtype, n_ranks, st, step, sf, kf, i, inj);
+    float a = regen_acc_one(grad_dtype, n_ranks, n_micro, mode, st, step, sf, kf, i, inj);
     if (!isfinite(a)) nf = 1;
     ss += (double)a * (double)a;
   }
@@ -654,15 +798,30 @@ int or_regen_sumsq(int32_t grad_dtype, int32_t n_ranks, uint64_t seed, int64_t s
   return 0;
 }
 
+int or_regen_accum_acc(int32_t grad_dtype, int32_t n_ranks, int32_t n_micro, int32_t mode,
+                       uint64_t seed, int64_t step, double sigma, double scale, int64_t n,
+                       const int64_t* logical_idx, const or_inject* inj, float* acc_out) {
+  int64_t k;
+  float sf = (float)sigma, kf = (float)scale;
+  uint64_t st[OR_MAX_REPLICAS * OR_MAX_MICRO];
+  if (!logical_idx || !acc_out || (mode != 0 && mode != 1)) return -1;
+  if (grad_states(seed, step, n_micro, n_ranks, st) != 0) return -1;
+  for (k = 0; k < n; ++k)
+    acc_out[k] = regen_acc_one(grad_dtype, n_ranks, n_micro, mode, st, step, sf, kf,
+                               logical_idx[k], inj);
+  return 0;
+}
+
+int or_regen_sumsq(int32_t grad_dtype, int32_t n_ranks, uint64_t seed, int64_t step, double sigma,
+                   double scale, int64_t i0, int64_t i1, const or_inject* inj, double* sumsq,
+                   int32_t* nonfinite) {
+  return or_regen_accum_sumsq(grad_dtype, n_ranks, 1, 0, seed, step, sigma, scale, i0, i1, inj,
+                              sumsq, nonfinite);
+}
+
 int or_regen_acc(int32_t grad_dtype, int32_t n_ranks, uint64_t seed, int64_t step, double sigma,
                  double scale, int64_t n, const int64_t* logical_idx, const or_inject* inj,
                  float* acc_out) {
-  int64_t k;
-  float sf = (float)sigma, kf = (float)scale;
-  uint64_t st[OR_MAX_REPLICAS];
-  if (!logical_idx || !acc_out) return -1;
-  if (grad_states(seed, step, n_ranks, st) != 0) return -1;
-  for (k = 0; k < n; ++k)
-    acc_out[k] = regen_acc_one(grad_dtype, n_ranks, st, step, sf, kf, logical_idx[k], inj);
-  return 0;
+  return or_regen_accum_acc(grad_dtype, n_ranks, 1, 0, seed, step, sigma, scale, n, logical_idx,
+                            inj, acc_out);
 }

@@ -15,7 +15,8 @@
  *         2.1 (Adam), 2.2 (fp32 master weights), 2.3 (bytes per parameter),
  *         2.4-2.5 (ZeRO tables 1 and 2), 3.1-3.3 (the three stages),
  *         3.4 (bit-exactness conditions), 3.5 (memory), 3.6 (padding),
- *         4.1-4.2 (communication volume), 5.2 (FlatParameter), exercises 1-5.
+ *         4.1-4.2 (communication volume), 5.2 (FlatParameter), 5.6 (the two
+ *         gradient-accumulation schemes), exercises 1-5.
  *  [F6]   Femtotron dev log #6 (ZeRO-1 and ZeRO-2): the master as one 1-D vector.
  *  [F7]   Femtotron dev log #7 (ZeRO-3): the ZeRO-2 gradient hook (pad, then
  *         reduce-scatter with AVG), ZeRO-3 is not bit-exact (reduction tree).
@@ -24,8 +25,9 @@
  *         ch. 四.3 (DeepSpeed stage 1/2 flat partitions; "check overflow ->
  *         clip -> step"), 五.4 and 五.6 (FSDP2: per-parameter dim-0 shards,
  *         fp32 shard is the parameter, cast at all-gather time, fp32
- *         reduce-scatter), 六.2 (Stage 3 vs FSDP1 vs FSDP2) and 五.7
- *         (gradient-norm clipping in train_step).
+ *         reduce-scatter), 六.2 (Stage 3 vs FSDP1 vs FSDP2), 三.3 (Megatron
+ *         gradient buckets, fp32 gradient accumulation) and 五.7
+ *         (gradient-norm clipping and accumulation on the shard).
  *
  * Where the pages leave a step open, the reading taken is stated at the
  * function that takes it.  Parity status: every function is pinned by a
@@ -39,7 +41,7 @@
 extern "C" {
 #endif
 
-enum { OR_F16 = 1, OR_BF16 = 2 };
+enum { OR_F16 = 1, OR_BF16 = 2, OR_F32 = 3 };
 enum { OR_GLOBAL_FLAT = 0, OR_PER_UNIT = 1 };
 
 /* One FlatParameter unit ([L13] 5.2).  All counts are elements. */
@@ -113,6 +115,18 @@ int or_reduce_scatter(int32_t grad_dtype, int32_t n_ranks, const or_unit* units,
 int or_finish(double sumsq, int32_t overflow, int32_t n_ranks, const or_hparams* hp,
               or_scale_state* st, or_scalars* sc, or_result* res);
 void or_adamw_array(int64_t n, const float* acc, const or_scalars* sc, float* p, float* m, float* v);
+int or_step_reduced(int32_t param_dtype, int32_t n_ranks, const or_unit* units, int64_t n_units,
+                    int32_t stage, float* const* acc, float* const* master,
+                    float* const* exp_avg, float* const* exp_avg_sq, uint16_t* params_full,
+                    uint16_t* const* param_shards, const or_hparams* hp, or_scale_state* st,
+                    or_result* res);
+int or_rs_accumulate(int32_t grad_dtype, int32_t n_ranks, const or_unit* units, int64_t n_units,
+                     int64_t u, const void* const* grads, float* const* shards,
+                     int32_t accumulate);
+int or_local_accumulate(int32_t grad_dtype, int64_t n, const uint16_t* grad, float* acc,
+                        int32_t accumulate);
+int or_bucket_assign(const int64_t* seg_numel, int64_t nseg, int32_t n_ranks,
+                     int64_t bucket_numel, int32_t* unit_out, int64_t* n_buckets);
 int or_zero_step(int32_t grad_dtype, int32_t param_dtype, int32_t n_ranks, const or_unit* units,
                  int64_t n_units, int32_t stage, const uint16_t* const* grads,
                  float* const* master, float* const* exp_avg, float* const* exp_avg_sq,
@@ -138,6 +152,15 @@ int or_regen_sumsq(int32_t grad_dtype, int32_t n_ranks, uint64_t seed, int64_t s
 int or_regen_acc(int32_t grad_dtype, int32_t n_ranks, uint64_t seed, int64_t step, double sigma,
                  double scale, int64_t n, const int64_t* logical_idx, const or_inject* inj,
                  float* acc_out);
+/* With gradient accumulation over n_micro micro-batches (mode 0: reduce
+ * every micro-batch and add to the shard; mode 1: no_sync, fp32 local
+ * accumulation then one reduction). */
+int or_regen_accum_sumsq(int32_t grad_dtype, int32_t n_ranks, int32_t n_micro, int32_t mode,
+                         uint64_t seed, int64_t step, double sigma, double scale, int64_t i0,
+                         int64_t i1, const or_inject* inj, double* sumsq, int32_t* nonfinite);
+int or_regen_accum_acc(int32_t grad_dtype, int32_t n_ranks, int32_t n_micro, int32_t mode,
+                       uint64_t seed, int64_t step, double sigma, double scale, int64_t n,
+                       const int64_t* logical_idx, const or_inject* inj, float* acc_out);
 
 #ifdef __cplusplus
 }

@@ -12,8 +12,17 @@ import oracle as O
 from fsdp_sharded_mixed_amd import workloads as W
 
 
-def plan(w):
+def unit_ids(w):
+    """Unit id of every segment: the workload's own, or the oracle's Megatron
+    bucket assignment for a bucketed workload."""
     numel, unit = w.seg_arrays()
+    if w.bucket_numel is not None:
+        unit, _ = O.bucket_assign(numel, w.n_ranks, w.bucket_numel)
+    return numel, list(unit)
+
+
+def plan(w):
+    numel, unit = unit_ids(w)
     if w.layout == W.PER_PARAM_DIM0:
         return O.layout_dim0(numel, [s.rows for s in w.segments], w.n_ranks)
     return O.layout(numel, unit, w.n_ranks, w.layout)
@@ -22,8 +31,9 @@ def plan(w):
 def groups(w):
     """FSDP units as (first parameter, count) for a per-parameter layout."""
     out = []
-    for i, s in enumerate(w.segments):
-        if not out or s.unit != w.segments[out[-1][0]].unit:
+    _, unit = unit_ids(w)
+    for i in range(len(w.segments)):
+        if not out or unit[i] != unit[out[-1][0]]:
             out.append([i, 0])
         out[-1][1] += 1
     return [tuple(g) for g in out]
@@ -39,8 +49,9 @@ def scale_state(w):
                         growth_interval=w.growth_interval, dynamic=int(w.dynamic))
 
 
-def replicas(w, units, psi_pad, step, scale, sigma=None, seed=None):
-    """N padded replica gradients for `step`, keyed by logical index (pads zero)."""
+def replicas(w, units, psi_pad, step, scale, sigma=None, seed=None, micro=0):
+    """N padded replica gradients for `step` (micro-batch `micro`), keyed by
+    logical index (pads zero)."""
     sigma = w.sigma if sigma is None else sigma
     seed = w.seed if seed is None else seed
     out = []
@@ -48,7 +59,8 @@ def replicas(w, units, psi_pad, step, scale, sigma=None, seed=None):
         g = np.zeros(psi_pad, np.uint16)
         for u in units:
             g[u["O"]:u["O"] + u["L"]] = O.gen16(u["L"], w.grad_dtype, seed,
-                                                W.grad_stream(step, q), u["lam"], sigma, scale)
+                                                W.grad_stream(step, q, micro), u["lam"], sigma,
+                                                scale)
         out.append(g)
     return out
 
@@ -117,6 +129,8 @@ class OracleRun:
         self.v = [np.zeros(s_tot, np.float32) for _ in range(n)]
         init16 = O.narrow(w.param_dtype, np.concatenate(self.master))
         self.grad_shards = None
+        if w.backward_rs:
+            self.grad_shards = [np.zeros(s_tot, np.float32) for _ in range(n)]
         if w.fp32_params:
             # FSDP2: fp32 parameters (no 16-bit copy) and fp32 grad shards
             self.full = self.shards = None
@@ -132,8 +146,38 @@ class OracleRun:
         self.st = scale_state(w)
         self.step_no = 0
 
+    def backward(self, micro_grads):
+        """The backward-side reduction of one step's micro-batches into the
+        fp32 gradient shards, bucket by bucket (O.rs_accumulate), either for
+        every micro-batch or, no_sync, once over fp32 local accumulations."""
+        w, units = self.w, self.units
+        if w.accum_mode == W.ACCUM_REDUCE_EACH:
+            for a, grads in enumerate(micro_grads):
+                for u in range(len(units)):
+                    O.rs_accumulate(w.grad_dtype, w.n_ranks, units, u, grads, self.grad_shards,
+                                    a > 0)
+        else:
+            loc = [np.zeros(self.psi_pad, np.float32) for _ in range(w.n_ranks)]
+            for a, grads in enumerate(micro_grads):
+                for q in range(w.n_ranks):
+                    O.local_accumulate(w.grad_dtype, grads[q], loc[q], a > 0)
+            for u in range(len(units)):
+                O.rs_accumulate(O.F32, w.n_ranks, units, u, loc, self.grad_shards, False)
+
     def step(self, grads=None):
         self.step_no += 1
+        if self.w.backward_rs:
+            micro_grads = grads
+            if micro_grads is None:
+                micro_grads = [replicas(self.w, self.units, self.psi_pad, self.step_no,
+                                        self.st.loss_scale, micro=a)
+                               for a in range(self.w.n_micro)]
+                if self.w.inject_step == self.step_no:
+                    inject_inf(self.w, self.units, micro_grads[0])
+            self.backward(micro_grads)
+            return O.step_reduced(self.w.param_dtype, self.w.n_ranks, self.units, self.w.stage,
+                                  self.grad_shards, self.master, self.m, self.v, self.full,
+                                  self.shards, self.hp, self.st)
         if grads is None:
             grads = replicas(self.w, self.units, self.psi_pad, self.step_no, self.st.loss_scale)
             if self.w.inject_step == self.step_no:

@@ -74,6 +74,26 @@ MUTANTS = [
     ("FSDP2 ledger counts a 16-bit parameter copy",
      "*after_backward_bytes = 4 * s_tot + 4 * s_tot + 8 * s_tot;",
      "*after_backward_bytes = 2 * s_tot + 4 * s_tot + 4 * s_tot + 8 * s_tot;"),
+    ("accumulating reduce-scatter drops the previous shard",
+     "shards[r][U->M + j] = accumulate ? shards[r][U->M + j] + sum : sum;",
+     "shards[r][U->M + j] = sum;"),
+    ("local accumulation overwrites",
+     "acc[i] = accumulate ? acc[i] + g : g;", "acc[i] = g;"),
+    ("bucket closes one segment late",
+     "if (fill >= B && s + 1 < nseg) {", "if (fill > B && s + 1 < nseg) {"),
+    ("default bucket size ignores the DP size",
+     "B = bucket_numel > 0 ? bucket_numel : 1000000LL * n_ranks;",
+     "B = bucket_numel > 0 ? bucket_numel : 40000000LL;"),
+    ("fp32 replicas read as 16-bit values",
+     "if (dtype == OR_F32) return ((const float*)g)[p];",
+     "if (dtype == OR_F32) return widen(OR_BF16, ((const uint16_t*)g)[p]);"),
+    ("reduced step never flags an overflow",
+     "if (!isfinite(acc[r][k])) overflow = 1;", "if (0 && !isfinite(acc[r][k])) overflow = 1;"),
+    ("micro-batch streams overlap the next step's",
+     "((uint64_t)micro << 8)", "((uint64_t)micro << 20)"),
+    ("no_sync regeneration sums ranks before micro-batches",
+     "  if (mode == 0) {\n    for (a = 0; a < n_micro; ++a) {",
+     "  if (mode == 0 || mode == 1) {\n    for (a = 0; a < n_micro; ++a) {"),
     ("ring traffic without the (N-1)/N factor",
      "return passes * ((double)(n_ranks - 1) / (double)n_ranks) * 2.0 * (double)psi_pad;",
      "return passes * 2.0 * (double)psi_pad;"),

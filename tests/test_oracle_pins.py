@@ -663,3 +663,210 @@ def test_fsdp2_equals_fsdp1_and_dp(orc, n):
             O.fsdp2_gather(u2, n, 0, 2, w.param_dtype, m2),
             O.fsdp2_gather(u2, n, 2, 1, w.param_dtype, m2),
             O.fsdp2_gather(u2, n, 3, 2, w.param_dtype, m2)]), prm)
+
+
+# ------------------------------------- buckets and gradient accumulation ----
+def test_bucket_rule_closed_forms(orc):
+    """[MDT] 三.3: buckets of max(40M, 1M * dp_size) elements by default;
+    parameters are not split, a bucket closes once it is full."""
+    # the default size: 40M up to 40 ranks, 1M per rank above
+    for n, cap in ((1, 40_000_000), (8, 40_000_000), (40, 40_000_000), (41, 41_000_000),
+                   (64, 64_000_000)):
+        ids, nb = O.bucket_assign([cap - 1, 1, 1], n)
+        assert list(ids) == [0, 0, 1] and nb == 2, n
+        ids, nb = O.bucket_assign([cap - 1, 2], n)
+        assert list(ids) == [0, 0] and nb == 1
+    # uniform segments: ceil(k / ceil(B / s)) buckets, all full but the last
+    for k, s, b in ((10, 3, 7), (12, 5, 5), (7, 10, 3), (9, 4, 12), (1, 9, 100)):
+        ids, nb = O.bucket_assign([s] * k, 2, b)
+        per = -(-b // s)
+        assert nb == -(-k // per)
+        assert list(ids) == [i // per for i in range(k)]
+    # a full bucket closes exactly at its size, never one segment late
+    ids, nb = O.bucket_assign([4, 6, 10, 1, 9, 3], 2, 10)
+    assert list(ids) == [0, 0, 1, 2, 2, 3] and nb == 4
+    # the 654M decoder in Megatron's order: each bucket but the last holds
+    # at least 40M elements, and removing its last parameter leaves < 40M
+    w = W.get("llama-654m-n2-buckets-a4")
+    numel = np.array([s.numel for s in w.segments])
+    ids, nb = O.bucket_assign(numel, w.n_ranks)
+    for b in range(nb):
+        sel = numel[ids == b]
+        if b < nb - 1:
+            assert sel.sum() >= 40_000_000 and sel.sum() - sel[-1] < 40_000_000
+    assert np.all(np.diff(ids) >= 0) and np.all(np.diff(ids) <= 1)
+
+
+def _dyadic_replicas(rng, n, n_micro, psi_pad, units, lo=-3, hi=4, step=2.0 ** -10):
+    """16-bit replicas holding small multiples of 2^-10 (exact in fp16 and
+    bf16, and every partial sum of a few of them exact in binary32)."""
+    out = []
+    for _ in range(n_micro):
+        reps = []
+        for _ in range(n):
+            g = np.zeros(psi_pad, np.float32)
+            for u in units:
+                g[u["O"]:u["O"] + u["L"]] = rng.integers(lo, hi, u["L"]) * step
+            reps.append(g)
+        out.append(reps)
+    return out
+
+
+@pytest.mark.parametrize("mode", [W.ACCUM_REDUCE_EACH, W.ACCUM_NO_SYNC])
+@pytest.mark.parametrize("n", [1, 2, 3, 8])
+def test_accumulation_exact_on_dyadic_inputs(orc, n, mode):
+    """With exactly representable partial sums both accumulation schemes
+    give the exact total over micro-batches and ranks ([L13] 5.6: the two
+    schemes differ in memory and communication, not in the result)."""
+    rng = np.random.default_rng(100 + n)
+    w = _small_workload(n, W.PER_UNIT, grad_dtype=W.BF16, dynamic=False, scale=1.0)
+    w.n_micro, w.accum_mode = 4, mode
+    run = OI.OracleRun(w)
+    reps = _dyadic_replicas(rng, n, w.n_micro, run.psi_pad, run.units)
+    micro16 = [[O.narrow(W.BF16, g) for g in r] for r in reps]
+    run.backward(micro16)
+    exact = sum(sum(g.astype(np.float64) for g in r) for r in reps)
+    got = OI.rank_shards_to_padded(run.units, run.grad_shards)
+    assert np.array_equal(got.astype(np.float64), exact)
+
+
+def test_accumulated_step_equals_one_step_on_summed_gradients(orc):
+    """A step after accumulating micro-batches whose per-replica sums are
+    exact equals the plain step on replicas holding those sums, bit for bit
+    (state, params, norm), in both schemes and every stage: accumulation
+    changes only where the sum is formed."""
+    rng = np.random.default_rng(7)
+    for mode in (W.ACCUM_REDUCE_EACH, W.ACCUM_NO_SYNC):
+        for stage in (2, 3):
+            n = 3
+            w = _small_workload(n, W.PER_UNIT, grad_dtype=W.BF16, dynamic=False, scale=1.0,
+                                stage=stage, max_norm=0.01)
+            w.n_micro, w.accum_mode = 4, mode
+            acc_run = OI.OracleRun(w)
+            w1 = _small_workload(n, W.PER_UNIT, grad_dtype=W.BF16, dynamic=False, scale=1.0,
+                                 stage=stage, max_norm=0.01)
+            one_run = OI.OracleRun(w1)
+            for _ in range(3):
+                reps = _dyadic_replicas(rng, n, 4, acc_run.psi_pad, acc_run.units, -2, 3)
+                micro16 = [[O.narrow(W.BF16, g) for g in r] for r in reps]
+                summed = [O.narrow(W.BF16, sum(reps[a][q] for a in range(4))) for q in range(n)]
+                for q in range(n):  # the per-replica sums are bf16-exact
+                    assert np.array_equal(O.widen(W.BF16, summed[q]),
+                                          sum(reps[a][q] for a in range(4)))
+                r1 = acc_run.step(micro16)
+                r2 = one_run.step(summed)
+                assert r1.skipped == r2.skipped == 0 and r1.sumsq == r2.sumsq
+                assert r1.coef < 1.0
+                for a1, a2 in ((acc_run.master, one_run.master), (acc_run.m, one_run.m),
+                               (acc_run.v, one_run.v)):
+                    assert all(np.array_equal(x.view(np.uint32), y.view(np.uint32))
+                               for x, y in zip(a1, a2))
+                if stage < 3:
+                    assert np.array_equal(acc_run.full, one_run.full)
+                else:
+                    assert all(np.array_equal(x, y)
+                               for x, y in zip(acc_run.shards, one_run.shards))
+
+
+@pytest.mark.parametrize("mode", [W.ACCUM_REDUCE_EACH, W.ACCUM_NO_SYNC])
+def test_accumulation_error_bound(orc, mode):
+    """Random bf16 micro-batches: the accumulated fp32 gradient is within the
+    recursive-summation bound (k-1)*u*sum|terms| (u = 2^-24, k = A*N terms)
+    of the exact sum, and the two schemes differ only by rounding order."""
+    n, a = 4, 8
+    w = _small_workload(n, W.PER_UNIT, grad_dtype=W.BF16, dynamic=False, scale=1.0)
+    w.n_micro, w.accum_mode = a, mode
+    run = OI.OracleRun(w)
+    micro16 = [OI.replicas(w, run.units, run.psi_pad, 1, 1.0, micro=k) for k in range(a)]
+    run.backward(micro16)
+    terms = np.array([[O.widen(W.BF16, g).astype(np.float64) for g in r] for r in micro16])
+    exact = terms.sum(axis=(0, 1))
+    bound = (a * n - 1) * 2.0 ** -24 * np.abs(terms).sum(axis=(0, 1))
+    got = OI.rank_shards_to_padded(run.units, run.grad_shards).astype(np.float64)
+    assert np.all(np.abs(got - exact) <= bound)
+    assert np.any(got != exact)  # rounding happened: the bound is what holds
+
+
+def test_bucket_rs_equals_whole_reduce_scatter(orc):
+    """The bucket-by-bucket reduce-scatter (first micro-batch, any bucket
+    order) is the whole-model reduce-scatter bit for bit, and accumulate == 0
+    overwrites whatever the shard held."""
+    for n in (1, 2, 5):
+        w = _small_workload(n, W.PER_UNIT, lens=(37, 5, 101, 64, 3))
+        units, psi, psi_pad = OI.plan(w)
+        grads = OI.replicas(w, units, psi_pad, 1, w.loss_scale)
+        s_tot = int(units["S"].sum())
+        ref = O.reduce_scatter(w.grad_dtype, n, units, grads)
+        for order in (range(len(units)), reversed(range(len(units)))):
+            sh = [np.full(s_tot, np.nan, np.float32) for _ in range(n)]
+            for u in order:
+                O.rs_accumulate(w.grad_dtype, n, units, u, grads, sh, False)
+            assert all(np.array_equal(x.view(np.uint32), y.view(np.uint32))
+                       for x, y in zip(sh, ref))
+        # accumulating the same micro-batch again doubles it exactly
+        for u in range(len(units)):
+            O.rs_accumulate(w.grad_dtype, n, units, u, grads, sh, True)
+        assert all(np.array_equal(x, 2 * y) for x, y in zip(sh, ref))
+
+
+def test_local_accumulate_and_fp32_reduce(orc):
+    """no_sync pieces: local accumulation is exact widening on the first
+    micro-batch and one binary32 addition after; the fp32 reduce-scatter sums
+    fp32 replicas in rank order (checked against numpy float32 sums)."""
+    rng = np.random.default_rng(3)
+    g16 = O.narrow(W.F16, (rng.standard_normal(1000) * 3).astype(np.float32))
+    acc = np.full(1000, np.nan, np.float32)
+    O.local_accumulate(W.F16, g16, acc, False)
+    assert np.array_equal(acc, g16.view(np.float16).astype(np.float32))
+    h16 = O.narrow(W.F16, (rng.standard_normal(1000) * 1e-3).astype(np.float32))
+    before = acc.copy()
+    O.local_accumulate(W.F16, h16, acc, True)
+    assert np.array_equal(acc, before + h16.view(np.float16).astype(np.float32))
+    n = 3
+    w = _small_workload(n, W.PER_UNIT)
+    units, psi, psi_pad = OI.plan(w)
+    f32 = [(rng.standard_normal(psi_pad) * 10.0 ** rng.integers(-3, 3, psi_pad)).astype(np.float32)
+           for _ in range(n)]
+    s_tot = int(units["S"].sum())
+    sh = [np.zeros(s_tot, np.float32) for _ in range(n)]
+    for u in range(len(units)):
+        O.rs_accumulate(O.F32, n, units, u, f32, sh, False)
+    ref = (f32[0] + f32[1]) + f32[2]
+    got = OI.rank_shards_to_padded(units, sh)
+    for u in units:
+        seg = slice(u["O"], u["O"] + u["P"])
+        assert np.array_equal(got[seg].view(np.uint32), ref[seg].view(np.uint32))
+
+
+@pytest.mark.parametrize("mode", [W.ACCUM_REDUCE_EACH, W.ACCUM_NO_SYNC])
+def test_regen_accum_matches_direct(orc, mode):
+    """The regeneration used for full-size checks reproduces the accumulated
+    gradient the direct path forms from materialised micro-batches, and its
+    squared norm, with an injection in micro-batch 0."""
+    n, a = 4, 4
+    w = _small_workload(n, W.PER_UNIT, grad_dtype=W.F16, lens=(12000, 77, 8129))
+    w.n_micro, w.accum_mode = a, mode
+    run = OI.OracleRun(w)
+    micro16 = [OI.replicas(w, run.units, run.psi_pad, 2, w.loss_scale, micro=k)
+               for k in range(a)]
+    run.backward(micro16)
+    acc = OI.rank_shards_to_logical(run.units, run.grad_shards)
+    idx = np.arange(run.psi)
+    got = O.regen_accum_acc(w.grad_dtype, n, a, mode, w.seed, 2, w.sigma, w.loss_scale, idx)
+    assert np.array_equal(got.view(np.uint32), acc.view(np.uint32))
+    ss, nf = O.regen_accum_sumsq(w.grad_dtype, n, a, mode, w.seed, 2, w.sigma, w.loss_scale,
+                                 0, run.psi)
+    assert nf == 0 and ss == float(np.cumsum(acc.astype(np.float64) ** 2)[-1])  # in order
+    # the two schemes round differently somewhere on this input, so the
+    # comparison above tells them apart
+    other = O.regen_accum_acc(w.grad_dtype, n, a, 1 - mode, w.seed, 2, w.sigma, w.loss_scale,
+                              idx)
+    assert np.any(other != got)
+    inj = O.Inject(step=2, replica=1, index=40, bits=0x7C00)
+    got = O.regen_accum_acc(w.grad_dtype, n, a, mode, w.seed, 2, w.sigma, w.loss_scale,
+                            np.array([39, 40, 41]), inject=inj)
+    assert np.isinf(got[1]) and np.isfinite(got[[0, 2]]).all()
+    # one micro-batch is the plain regeneration
+    one = O.regen_accum_acc(w.grad_dtype, n, 1, mode, w.seed, 2, w.sigma, w.loss_scale, idx)
+    assert np.array_equal(one, O.regen_acc(w.grad_dtype, n, w.seed, 2, w.sigma, w.loss_scale,
+                                           idx))
