@@ -3,7 +3,10 @@
 
 A step is one zf_shard_step over one batch of N resident replica gradients
 (reduce-scatter sums, overflow/norm/clip, fused AdamW + cast + gather), plus
-the per-unit gathers for a ZeRO-3 workload.  Inputs are seeded synthetic
+the per-unit gathers for a ZeRO-3 workload.  For a workload with gradient
+accumulation, a step is first the backward-side reduction of its
+micro-batches (every bucket's reduce-scatter, accumulated into the fp32
+gradient shards), then the step on the reduced shards.  Inputs are seeded synthetic
 data generated on the device before the timed region; every step reuses the
 same batch (the state evolves).
 
@@ -29,10 +32,30 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, vendor figure
 DEFAULT_WORKLOAD = "llama-73m-n8"
 
 
+def backward_bytes_per_param(w):
+    """Bytes of the backward-side reduction per parameter per step, over its
+    n_micro micro-batches (A): every micro-batch reads the N 16-bit replicas
+    and writes the fp32 shard, reading it back from the second one on; or,
+    no_sync, every replica's fp32 main_grad is written (and read back from
+    the second micro-batch on), then the N main_grads are read once and the
+    shard written."""
+    a, n = w.n_micro, w.n_ranks
+    if w.accum_mode == 0:
+        return a * 2 * n + (a - 1) * 4 + a * 4
+    return a * 2 * n + (a - 1) * 4 * n + a * 4 * n + 4 * n + 4
+
+
 def algorithmic_bytes_per_param(w):
     """Bytes the method itself moves per real parameter per applied step:
     read N 16-bit replicas, read and write fp32 master/m/v, write the 16-bit
-    param; ZeRO-3 adds the unit gather (read 2 + write 2)."""
+    param; ZeRO-3 adds the unit gather (read 2 + write 2).  With the
+    backward-side reduction: its bytes (backward_bytes_per_param), then the
+    step reads the fp32 shard twice (norm pass, update pass)."""
+    if w.backward_rs:
+        b = backward_bytes_per_param(w) + 4 + 4 + 12 + 12
+        if w.fp32_params:
+            return b + 4 + 2
+        return b + 2 + (4 if w.stage == 3 else 0)
     if w.fp32_params:
         # FSDP2: replicas in, fp32 grad shard out and back in, fp32 state in
         # and out, then each unit gather reads fp32 and writes 16-bit
@@ -48,6 +71,12 @@ def update_kernel_bytes_per_elem(w, materialized):
     sums, or the N replicas again), fp32 master/m/v in and out, and the
     16-bit parameter out unless the parameters are fp32 (FSDP2)."""
     return (4 if materialized else 2 * w.n_ranks) + 12 + 12 + (0 if w.fp32_params else 2)
+
+
+def backward_kernel_bytes_per_elem(w):
+    """The backward-side launches of one step per (padded) element: the same
+    terms as backward_bytes_per_param."""
+    return backward_bytes_per_param(w)
 
 
 PROFILES = os.path.join(ROOT, "profiles")
@@ -169,19 +198,23 @@ def cpu_baseline(w, min_seconds=10.0, max_steps=40):
     ws = W.Workload(**{**w.__dict__, "segments": segs})
     units, psi, psi_pad = OI.plan(ws)
     run = OI.OracleRun(ws, units, psi, psi_pad)
-    grads = OI.replicas(ws, units, psi_pad, 1, ws.loss_scale)
+    if ws.backward_rs:
+        grads = [OI.replicas(ws, units, psi_pad, 1, ws.loss_scale, micro=a)
+                 for a in range(ws.n_micro)]
+    else:
+        grads = OI.replicas(ws, units, psi_pad, 1, ws.loss_scale)
     steps, t0 = 0, time.perf_counter()
     while steps < max_steps and (time.perf_counter() - t0) < min_seconds:
-        O.zero_step(ws.grad_dtype, ws.param_dtype, ws.n_ranks, units, ws.stage, grads,
-                    run.master, run.m, run.v, run.full, run.shards, run.hp, run.st)
+        run.step(grads)
         steps += 1
     dt = time.perf_counter() - t0
     gbs = algorithmic_bytes_per_param(ws) * psi * steps / dt / 1e9
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "params_per_s": round(psi * steps / dt, 1),
             "sample": f"first {len(segs)} parameter tensors ({psi:,} params) of {w.name}, "
-                      f"N={ws.n_ranks}, {steps} steps over one batch, {dt:.1f} s, "
-                      f"single-threaded C oracle"}
+                      f"N={ws.n_ranks}, {steps} steps over one batch"
+                      + (f" of {ws.n_micro} micro-batches" if ws.backward_rs else "")
+                      + f", {dt:.1f} s, single-threaded C oracle"}
 
 
 def main():
@@ -231,12 +264,19 @@ def main():
     torch.cuda.synchronize()
     copy_gbs = 2 * COPY_BYTES * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del src, dst
-    dev = runner.DeviceRun(w, device="cuda:0")
+    dev = runner.DeviceRun(w, device="cuda:0", resident_micro=True)
     dev.init_state()
-    dev.fill_grads(1, w.loss_scale)
+    if w.backward_rs:
+        dev.fill_micro(1, w.loss_scale)
+    else:
+        dev.fill_grads(1, w.loss_scale)
     torch.cuda.synchronize()
 
-    def one_step(phase_events=None):
+    def one_step(phase_events=None, backward_event=None):
+        if w.backward_rs:
+            if backward_event is not None:
+                backward_event.record()
+            dev.backward_all()
         dev.step(phase_events=phase_events)
         dev.gather_all()
 
@@ -262,14 +302,18 @@ def main():
 
     # per-kernel durations: a second run of K steps with HIP events recorded
     # by the library between its kernels, on the step's stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     for row in evs:
         for e in row:
             e.record()
     torch.cuda.synchronize()
     for row in evs:
-        one_step(phase_events=[e.cuda_event for e in row])
+        one_step(phase_events=[e.cuda_event for e in row[1:]], backward_event=row[0])
     torch.cuda.synchronize()
+    evs_b = [r[0] for r in evs]
+    evs = [r[1:] for r in evs]
+    bw = (sum(b.elapsed_time(r[0]) for b, r in zip(evs_b, evs)) / args.steps
+          if w.backward_rs else 0.0)
     p1 = sum(r[0].elapsed_time(r[1]) for r in evs) / args.steps
     fin = sum(r[1].elapsed_time(r[2]) for r in evs) / args.steps
     p2 = sum(r[2].elapsed_time(r[3]) for r in evs) / args.steps
@@ -278,8 +322,33 @@ def main():
     materialized = s.policy != 0
     alg = algorithmic_bytes_per_param(w) * w.psi
     gbs = alg / (ms * 1e-3) / 1e9
-    upd_bytes = update_kernel_bytes_per_elem(w, materialized) * s.psi_pad
+    upd_bytes = update_kernel_bytes_per_elem(w, materialized or w.backward_rs) * s.psi_pad
     upd_gbs = upd_bytes / (p2 * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(upd_gbs, 2), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(upd_gbs / PEAK_HBM_GBS, 4),
+            "traffic": traffic_for(w.name),
+            "kernel": "zf_pass2 (fused AdamW" + ("" if w.fp32_params else "+cast+gather") + ")",
+            "bytes_per_launch": upd_bytes}
+    kernels = {"pass1_rs_norm": round(p1, 5), "finish": round(fin, 5),
+               "pass2_update": round(p2, 5)}
+    if w.backward_rs:
+        bw_bytes = backward_kernel_bytes_per_elem(w) * s.psi_pad
+        bw_gbs = bw_bytes / (bw * 1e-3) / 1e9
+        kernels["backward_buckets"] = round(bw, 5)
+        kernels["backward_launches"] = (w.n_micro * s.n_groups if w.accum_mode == 0 else
+                                        w.n_micro * w.n_ranks + s.n_groups)
+        if bw_bytes > upd_bytes:
+            # the backward-side reduction moves the most bytes: it is the
+            # roofline row (all its launches of one step, back to back)
+            roof = {"bound": "hbm", "achieved": round(bw_gbs, 2), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(bw_gbs / PEAK_HBM_GBS, 4),
+                    "traffic": None,
+                    "kernel": ("zf_bucket_rs_kernel (every bucket of every micro-batch)"
+                               if w.accum_mode == 0 else
+                               "zf_accumulate_kernel + zf_bucket_rs_kernel (no_sync)"),
+                    "bytes_per_launch": bw_bytes, "launches_per_step":
+                        kernels["backward_launches"]}
+        kernels["backward_gbs"] = round(bw_gbs, 2)
     line = {
         "metric": "ZeRO step GB/s (algorithmic bytes) and % of HBM peak; params updated/s",
         "value": round(gbs, 2),
@@ -303,15 +372,14 @@ def main():
         "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
         "wall_ms_per_step": round(1e3 * wall / args.steps, 5),
         "device_copy_gbs": round(copy_gbs, 1),
-        "kernels_ms": {"pass1_rs_norm": round(p1, 5), "finish": round(fin, 5),
-                       "pass2_update": round(p2, 5)},
-        "roofline": {"bound": "hbm", "achieved": round(upd_gbs, 2), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(upd_gbs / PEAK_HBM_GBS, 4),
-                     "traffic": traffic_for(w.name),
-                     "kernel": "zf_pass2 (fused AdamW" + ("" if w.fp32_params else
-                                                          "+cast+gather") + ")",
-                     "bytes_per_launch": upd_bytes},
+        "kernels_ms": kernels,
+        "roofline": roof,
     }
+    if w.backward_rs:
+        line["config"]["micro_batches"] = w.n_micro
+        line["config"]["accumulation"] = ["reduce-scatter every micro-batch",
+                                          "no_sync fp32 local, one reduce-scatter"][w.accum_mode]
+        line["config"]["buckets"] = s.n_groups
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)

@@ -178,6 +178,35 @@ extern "C" int zf_plan_flat(const zf_segment* segs, int64_t nseg, int32_t n_rank
   return ZF_OK;
 }
 
+// Megatron gradient buckets (source guide 三.3): consecutive parameters of
+// the buffer fill a bucket until it holds bucket_numel elements (default
+// max(40M, 1M * dp_size)); parameters are not split.
+extern "C" int zf_plan_buckets(const int64_t* numel, int64_t nseg, int32_t n_ranks,
+                               int64_t bucket_numel, int32_t* unit_out, int64_t* n_buckets) {
+  if (!numel || !unit_out || !n_buckets || nseg < 1) return ZF_EINVAL;
+  if (n_ranks < 1 || n_ranks > ZF_MAX_RANKS) return ZF_ESIZE;
+  int64_t cap = bucket_numel;
+  if (cap <= 0) {
+    cap = int64_t(1000000) * n_ranks;
+    if (cap < 40000000) cap = 40000000;
+  }
+  int64_t fill = 0;
+  int32_t id = 0;
+  for (int64_t i = 0; i < nseg; ++i) {
+    if (numel[i] < 1) return ZF_EINVAL;
+    if (numel[i] > std::numeric_limits<int64_t>::max() - fill) return ZF_ESIZE;
+    unit_out[i] = id;
+    fill += numel[i];
+    if (fill >= cap && i + 1 < nseg) {
+      if (id == std::numeric_limits<int32_t>::max()) return ZF_ESIZE;
+      ++id;
+      fill = 0;
+    }
+  }
+  *n_buckets = (int64_t)id + 1;
+  return ZF_OK;
+}
+
 extern "C" int zf_plan_info(const zf_plan* plan, zf_plan_summary* out) {
   if (!plan || plan->magic != zf::kPlanMagic || !out) return ZF_EINVAL;
   *out = plan->summary;

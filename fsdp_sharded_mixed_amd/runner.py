@@ -15,20 +15,38 @@ from . import zf
 TORCH_16 = {W.F16: torch.float16, W.BF16: torch.bfloat16}
 
 
+def plan_workload(w):
+    """The library's plan of a workload: its FSDP units, or Megatron gradient
+    buckets from zf_plan_buckets when the workload is bucketed."""
+    segs = w.segments
+    if w.bucket_numel is not None:
+        ids, _ = zf.plan_buckets([sg.numel for sg in segs], w.n_ranks, w.bucket_numel)
+        segs = [(sg.numel, ids[i], sg.kind, sg.rows) for i, sg in enumerate(segs)]
+    return zf.plan_flat(segs, w.n_ranks, w.layout, w.stage)
+
+
 class DeviceRun:
     """A workload's device state: N replicas, fp32 master/m/v, 16-bit params,
     workspace and state block, plus a reused unit buffer for stage 3."""
 
-    def __init__(self, w, device="cuda:0", grads=True):
+    def __init__(self, w, device="cuda:0", grads=True, resident_micro=False):
+        """resident_micro: keep all n_micro micro-batches' replicas resident
+        (the bench's inputs), instead of refilling one set per micro-batch."""
         self.w = w
         self.device = torch.device(device)
-        self.plan = zf.plan_flat(w.segments, w.n_ranks, w.layout, w.stage)
+        self.plan = plan_workload(w)
         s = self.plan.summary
         self.psi, self.psi_pad = s.psi, s.psi_pad
         n, dev = s.psi_pad, self.device
         gdt, pdt = TORCH_16[w.grad_dtype], TORCH_16[w.param_dtype]
-        self.grads = [torch.zeros(n, dtype=gdt, device=dev) for _ in range(w.n_ranks)] \
-            if grads else []
+        n_sets = w.n_micro if (resident_micro and w.backward_rs) else 1
+        self.micro_grads = [[torch.zeros(n, dtype=gdt, device=dev) for _ in range(w.n_ranks)]
+                            if grads else [] for _ in range(n_sets)]
+        self.grads = self.micro_grads[0]
+        # no_sync: every replica's fp32 local accumulation buffer (main_grad)
+        self.main_grads = ([torch.zeros(n, dtype=torch.float32, device=dev)
+                            for _ in range(w.n_ranks)]
+                           if w.backward_rs and w.accum_mode == W.ACCUM_NO_SYNC else None)
         self.master = torch.zeros(n, dtype=torch.float32, device=dev)
         self.exp_avg = torch.zeros(n, dtype=torch.float32, device=dev)
         self.exp_avg_sq = torch.zeros(n, dtype=torch.float32, device=dev)
@@ -36,7 +54,7 @@ class DeviceRun:
         # gradient shards; the other layouts keep a 16-bit copy
         self.params = None if w.fp32_params else torch.zeros(n, dtype=pdt, device=dev)
         self.grad_shards = (torch.zeros(n, dtype=torch.float32, device=dev)
-                            if s.policy == 2 else None)
+                            if s.policy == 2 or w.backward_rs else None)
         self.workspace = torch.empty(max(1, s.workspace_bytes), dtype=torch.uint8, device=dev)
         self.state = torch.empty(zf.state_bytes(), dtype=torch.uint8, device=dev)
         self.unit_buf = (torch.empty(s.max_unit_pad, dtype=pdt, device=dev)
@@ -74,31 +92,69 @@ class DeviceRun:
         self.step_no = 0
         self.loss_scale = w.loss_scale
 
-    def fill_grads(self, step, scale, sigma=None):
-        """Replica q's gradient for `step`, keyed by logical index (pads stay 0)."""
+    def fill_grads(self, step, scale, sigma=None, micro=0, bufs=None):
+        """Replica q's gradient for `step` (micro-batch `micro`) into bufs
+        (default self.grads), keyed by logical index (pads stay 0)."""
         w = self.w
         sigma = w.sigma if sigma is None else sigma
-        for q, g in enumerate(self.grads):
+        for q, g in enumerate(self.grads if bufs is None else bufs):
             for u in self.plan.units:
-                I.fill_normal16(g, u.L, w.grad_dtype, w.seed, W.grad_stream(step, q), u.lam,
-                                sigma, scale, offset=u.O)
+                I.fill_normal16(g, u.L, w.grad_dtype, w.seed, W.grad_stream(step, q, micro),
+                                u.lam, sigma, scale, offset=u.O)
                 if u.P > u.L:  # the padding must be zero (a test may have poisoned it)
                     g[u.O + u.L:u.O + u.P].zero_()
 
-    def inject_inf(self):
+    def fill_micro(self, step, scale):
+        """Every micro-batch of `step` into the resident sets (and the
+        injection into micro-batch 0 when it is due)."""
+        for a, bufs in enumerate(self.micro_grads):
+            self.fill_grads(step, scale, micro=a, bufs=bufs)
+        if self.w.inject_step == step:
+            self.inject_inf(self.micro_grads[0])
+
+    def inject_inf(self, bufs=None):
         """+inf into the workload's inject replica at its inject index."""
         i = I.inject_index(self.w, self.psi)
         p = self.logical_to_padded(i)
-        self.grads[self.w.inject_replica][p] = float("inf")
+        (self.grads if bufs is None else bufs)[self.w.inject_replica][p] = float("inf")
         return i
+
+    # ---- backward-side reduction -------------------------------------------
+    def backward(self, micro, bufs=None, stream=None):
+        """Micro-batch `micro`'s share of the backward-side reduction: every
+        bucket reduce-scattered into the fp32 gradient shards (accumulating
+        after the first micro-batch), or, no_sync, every replica accumulated
+        into its fp32 main_grad and the buckets reduced at the last one.
+        Buckets go in plan order, which is the order backward fills them."""
+        w, bufs = self.w, (self.grads if bufs is None else bufs)
+        ng = len(self.plan.groups)
+        if w.accum_mode == W.ACCUM_REDUCE_EACH:
+            for g in range(ng):
+                zf.bucket_reduce_scatter(self.plan, g, w.grad_dtype, bufs, self.grad_shards,
+                                         micro > 0, stream=stream)
+            return
+        for q in range(w.n_ranks):
+            zf.accumulate(w.grad_dtype, bufs[q], self.main_grads[q], n=self.psi_pad,
+                          accumulate=micro > 0, stream=stream)
+        if micro == w.n_micro - 1:
+            for g in range(ng):
+                zf.bucket_reduce_scatter(self.plan, g, zf.F32, self.main_grads,
+                                         self.grad_shards, False, stream=stream)
+
+    def backward_all(self, stream=None):
+        """All micro-batches from the resident sets."""
+        for a in range(self.w.n_micro):
+            self.backward(a, self.micro_grads[a % len(self.micro_grads)], stream=stream)
 
     # ---- the step ------------------------------------------------------------
     def step(self, stream=None, phase_events=None):
         self.step_no += 1
-        zf.shard_step(self.plan, self.hp, self.w.grad_dtype, self.w.param_dtype, self.grads,
-                      self.master, self.exp_avg, self.exp_avg_sq, self.params, self.workspace,
-                      self.state, stream=stream, phase_events=phase_events,
-                      grad_shards=self.grad_shards)
+        reduced = self.w.backward_rs
+        zf.shard_step(self.plan, self.hp, self.w.grad_dtype, self.w.param_dtype,
+                      None if reduced else self.grads, self.master, self.exp_avg,
+                      self.exp_avg_sq, self.params, self.workspace, self.state, stream=stream,
+                      phase_events=phase_events, grad_shards=self.grad_shards,
+                      grads_reduced=reduced)
 
     def result(self):
         return zf.read_result(self.state)
@@ -132,11 +188,21 @@ class DeviceRun:
 
     def run_workload_step(self):
         """One step of the workload's own sequence: fresh grads for step k at
-        the current loss scale, the injection if due, then the step."""
+        the current loss scale (every micro-batch, each reduced bucket by
+        bucket as it is filled, when the workload accumulates), the
+        injection if due, then the step."""
         k = self.step_no + 1
-        self.fill_grads(k, self.loss_scale)
-        if self.w.inject_step == k:
-            self.inject_inf()
+        if self.w.backward_rs:
+            for a in range(self.w.n_micro):
+                bufs = self.micro_grads[a % len(self.micro_grads)]
+                self.fill_grads(k, self.loss_scale, micro=a, bufs=bufs)
+                if self.w.inject_step == k and a == 0:
+                    self.inject_inf(bufs)
+                self.backward(a, bufs)
+        else:
+            self.fill_grads(k, self.loss_scale)
+            if self.w.inject_step == k:
+                self.inject_inf()
         self.step()
         res = self.result()
         self.loss_scale = res.scale_next

@@ -13,7 +13,7 @@ from dataclasses import dataclass
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libzf.so")
 
-F16, BF16 = 1, 2
+F16, BF16, F32 = 1, 2, 3
 GLOBAL_FLAT, PER_UNIT, PER_PARAM_DIM0 = 0, 1, 2
 MAX_RANKS = 64
 STATUS = {0: "ZF_OK", -1: "ZF_EINVAL", -2: "ZF_EALIGN", -3: "ZF_EDTYPE", -4: "ZF_ESIZE",
@@ -59,7 +59,8 @@ class StepArgs(C.Structure):
     _fields_ = [("grad_dtype", C.c_int32), ("param_dtype", C.c_int32),
                 ("grads", C.POINTER(C.c_void_p)), ("master", C.c_void_p),
                 ("exp_avg", C.c_void_p), ("exp_avg_sq", C.c_void_p), ("params", C.c_void_p),
-                ("grad_shards", C.c_void_p), ("numel", C.c_int64), ("workspace", C.c_void_p),
+                ("grad_shards", C.c_void_p), ("grads_reduced", C.c_int32),
+                ("reserved", C.c_int32), ("numel", C.c_int64), ("workspace", C.c_void_p),
                 ("workspace_size", C.c_int64),
                 ("state", C.c_void_p), ("phase_events", C.POINTER(C.c_void_p))]
 
@@ -90,6 +91,13 @@ _SIGNATURES = {
                                     C.c_int64, C.c_void_p]),
     "zf_gather": (C.c_int, [C.c_void_p, C.c_int64, C.c_int32, C.POINTER(C.c_void_p),
                             C.c_void_p, C.c_int64, C.c_void_p]),
+    "zf_plan_buckets": (C.c_int, [C.POINTER(C.c_int64), C.c_int64, C.c_int32, C.c_int64,
+                                  C.POINTER(C.c_int32), C.POINTER(C.c_int64)]),
+    "zf_bucket_reduce_scatter": (C.c_int, [C.c_void_p, C.c_int64, C.c_int32,
+                                           C.POINTER(C.c_void_p), C.c_void_p, C.c_int64,
+                                           C.c_int32, C.c_void_p]),
+    "zf_accumulate": (C.c_int, [C.c_int32, C.c_void_p, C.c_void_p, C.c_int64, C.c_int32,
+                                C.c_void_p]),
     "zf_read_result": (C.c_int, [C.c_void_p, C.POINTER(StepResult), C.c_void_p]),
     "zf_strerror": (C.c_char_p, [C.c_int]),
 }
@@ -233,19 +241,22 @@ def _nbytes(t, nbytes):
 
 def shard_step(plan, hp, grad_dtype, param_dtype, grads, master, exp_avg, exp_avg_sq, params,
                workspace, state, stream=None, phase_events=None, numel=None,
-               workspace_size=None, grad_shards=None):
-    """zf_shard_step.  grads: N tensors (or addresses); params may be None
-    (fp32 parameters); grad_shards: None or the fp32 gradient shards;
-    phase_events: None or 4 raw hipEvent_t handles.  numel / workspace_size
-    default to the sizes of the tensors passed (the smallest array)."""
-    gp = _ptr_array(grads)
+               workspace_size=None, grad_shards=None, grads_reduced=False):
+    """zf_shard_step.  grads: N tensors (or addresses), or None with
+    grads_reduced (grad_shards then hold the reduced gradients); params may
+    be None (fp32 parameters); grad_shards: None or the fp32 gradient
+    shards; phase_events: None or 4 raw hipEvent_t handles.  numel /
+    workspace_size default to the sizes of the tensors passed (the smallest
+    array)."""
+    gp = _ptr_array(grads) if grads is not None else None
     ev = (C.c_void_p * 4)(*phase_events) if phase_events is not None else None
     if numel is None:
-        arrays = list(grads) + [master, exp_avg, exp_avg_sq, params, grad_shards]
-        numel = min(t.numel() for t in arrays if t is not None)
+        arrays = list(grads or []) + [master, exp_avg, exp_avg_sq, params, grad_shards]
+        numel = min(t.numel() for t in arrays if t is not None and not isinstance(t, int))
     args = StepArgs(int(grad_dtype), int(param_dtype), gp, _ptr(master), _ptr(exp_avg),
-                    _ptr(exp_avg_sq), _ptr(params), _ptr(grad_shards), int(numel),
-                    _ptr(workspace), _nbytes(workspace, workspace_size), _ptr(state), ev)
+                    _ptr(exp_avg_sq), _ptr(params), _ptr(grad_shards), int(bool(grads_reduced)),
+                    0, int(numel), _ptr(workspace), _nbytes(workspace, workspace_size),
+                    _ptr(state), ev)
     _check(lib.zf_shard_step(_handle(plan), C.byref(hp), C.byref(args), _stream(stream)),
            "zf_shard_step")
 
@@ -256,6 +267,36 @@ def reduce_scatter(plan, grad_dtype, grads, rs_out, stream=None, numel=None):
     _check(lib.zf_reduce_scatter(_handle(plan), int(grad_dtype), _ptr_array(grads),
                                  _ptr(rs_out), int(numel), _stream(stream)),
            "zf_reduce_scatter")
+
+
+def plan_buckets(numel, n_ranks, bucket_numel=0):
+    """zf_plan_buckets: the bucket id of every segment (buffer order) and the count."""
+    n = len(numel)
+    arr = (C.c_int64 * n)(*[int(x) for x in numel])
+    out = (C.c_int32 * n)()
+    nb = C.c_int64()
+    _check(lib.zf_plan_buckets(arr, n, int(n_ranks), int(bucket_numel), out, C.byref(nb)),
+           "zf_plan_buckets")
+    return list(out), nb.value
+
+
+def bucket_reduce_scatter(plan, group, grad_dtype, grads, grad_shards, accumulate,
+                          stream=None, numel=None):
+    """zf_bucket_reduce_scatter of group (bucket) `group` into grad_shards."""
+    if numel is None:
+        numel = min(t.numel() for t in list(grads) + [grad_shards])
+    _check(lib.zf_bucket_reduce_scatter(_handle(plan), int(group), int(grad_dtype),
+                                        _ptr_array(grads), _ptr(grad_shards), int(numel),
+                                        int(bool(accumulate)), _stream(stream)),
+           "zf_bucket_reduce_scatter")
+
+
+def accumulate(grad_dtype, grad, acc, n=None, accumulate=True, stream=None):
+    """zf_accumulate: acc (+)= f32(grad) over n elements (tensors or addresses)."""
+    if n is None:
+        n = min(grad.numel(), acc.numel())
+    _check(lib.zf_accumulate(int(grad_dtype), _ptr(grad), _ptr(acc), int(n),
+                             int(bool(accumulate)), _stream(stream)), "zf_accumulate")
 
 
 def gather(plan, unit, dtype, shards, unit_buf, stream=None, unit_buf_numel=None):

@@ -31,7 +31,9 @@
  *         五.6 (FSDP2: per-parameter dim-0 shards, the fp32 shard is the
  *         parameter, fp32 reduce-scatter into the shard's gradient, cast to
  *         the parameter dtype at all-gather time), 六.2 (Stage 3 vs FSDP1 vs
- *         FSDP2) and 五.7 (global gradient-norm clipping).
+ *         FSDP2), 三.3 (Megatron's gradient buffer and buckets, no_sync
+ *         accumulation in fp32) and 五.7 (global gradient-norm clipping;
+ *         gradient accumulation on the shard).
  *
  * Conventions for every call:
  *   - Sizes are element counts unless a name ends in _bytes.
@@ -80,7 +82,9 @@ enum zf_status {
   ZF_ENOMEM = -6   /* host allocation for a plan failed                        */
 };
 
-enum zf_dtype { ZF_F16 = 1, ZF_BF16 = 2 };
+/* ZF_F32 is accepted only where a call says so (the fp32 replicas of
+ * zf_bucket_reduce_scatter). */
+enum zf_dtype { ZF_F16 = 1, ZF_BF16 = 2, ZF_F32 = 3 };
 /* Layouts:
  *   ZF_GLOBAL_FLAT    all parameters form one FlatParameter ([F6]);
  *   ZF_PER_UNIT       one FlatParameter per FSDP unit ([L13] 5.2, FSDP1);
@@ -207,7 +211,16 @@ typedef struct {
   float* grad_shards;         /* NULL, or Psi' fp32: the ranks' resident fp32
                                  gradient shards; pass 1 writes the sums
                                  there and pass 2 reads them (required by
-                                 ZF_PER_PARAM_DIM0 plans) */
+                                 ZF_PER_PARAM_DIM0 plans and by
+                                 grads_reduced) */
+  int32_t grads_reduced;      /* 0: reduce-scatter `grads` in pass 1.
+                                 1: grad_shards already hold the reduced
+                                 (and accumulated) gradients, as left by
+                                 zf_bucket_reduce_scatter; `grads` and
+                                 grad_dtype are ignored (grads may be NULL)
+                                 and pass 1 only reads grad_shards for the
+                                 overflow flag and the norm partials */
+  int32_t reserved;           /* must be 0 */
   int64_t numel;              /* elements of each per-element array above
                                  (grads[q], master, exp_avg, exp_avg_sq,
                                  params, grad_shards); must be >= Psi' */
@@ -243,6 +256,54 @@ int zf_shard_step(const zf_plan* plan, const zf_hparams* hp, const zf_step_args*
  * grads[q] and of rs_out, >= Psi'.  Errors as zf_shard_step. */
 int zf_reduce_scatter(const zf_plan* plan, int32_t grad_dtype, const void* const* grads,
                       float* rs_out, int64_t numel, void* stream);
+
+/* Megatron gradient buckets ([MDT] 三.3): assign a bucket id to every
+ * parameter, in buffer order.  Megatron lays the buffer out last layer
+ * first, so that gradients fill it from the head as backward runs; callers
+ * that follow it pass the segments in that order.  A bucket closes as soon
+ * as it holds at least bucket_numel elements; a parameter is never split;
+ * the last bucket takes the rest.  bucket_numel <= 0 selects the default
+ * max(40,000,000, 1,000,000 * n_ranks).  unit_out[s] receives segment s's
+ * bucket id (0, 0, .., 1, ..), usable as zf_segment.unit with ZF_PER_UNIT:
+ * each bucket is then a FlatParameter padded to a multiple of n_ranks and
+ * split evenly, as the distributed optimizer pads its buckets.  Host only.
+ * Errors: ZF_EINVAL (NULL, nseg < 1, numel < 1), ZF_ESIZE (n_ranks out of
+ * range). */
+int zf_plan_buckets(const int64_t* numel, int64_t nseg, int32_t n_ranks, int64_t bucket_numel,
+                    int32_t* unit_out, int64_t* n_buckets);
+
+/* Backward-side reduce-scatter of one bucket as its gradients become ready
+ * ([L13] 3.2: one reduce-scatter per bucket during backward; [MDT] 三.3 and
+ * 四.3), accumulating over micro-batches ([L13] 5.6 and [MDT] 五.7: each
+ * micro-batch reduce-scattered and added to the sharded gradient).  For
+ * every p in group g's padded range [O, O + padded) -- a bucket or unit of a
+ * ZF_PER_UNIT plan, the whole flat of a ZF_GLOBAL_FLAT plan, an FSDP unit
+ * of a ZF_PER_PARAM_DIM0 plan:
+ *   sum = f32(grads[0][p]) + f32(grads[1][p]) + ... + f32(grads[N-1][p])
+ *   grad_shards[p] = accumulate ? grad_shards[p] + sum : sum
+ * each + one binary32 addition, in rank order.  grad_dtype: ZF_F16 or
+ * ZF_BF16 replicas, or ZF_F32 for fp32 replicas (the no_sync scheme: every
+ * replica accumulates locally with zf_accumulate and is reduced once, at
+ * the last micro-batch).  grads: host array of N device pointers to padded-
+ * flat replicas, 16-byte aligned, of numel elements (only the group's range
+ * is read); grad_shards: numel fp32, 16-byte aligned; numel >= Psi'.
+ * Distinct groups touch disjoint ranges: they may run in any order or on
+ * different streams.  A zf_shard_step with grads_reduced = 1 then consumes
+ * grad_shards.  Errors: ZF_EINVAL, ZF_EALIGN, ZF_EDTYPE, ZF_ESIZE,
+ * ZF_EHIP. */
+int zf_bucket_reduce_scatter(const zf_plan* plan, int64_t group, int32_t grad_dtype,
+                             const void* const* grads, float* grad_shards, int64_t numel,
+                             int32_t accumulate, void* stream);
+
+/* Local gradient accumulation under no_sync ([MDT] 三.3: the backward hook
+ * adds each micro-batch's gradient into the parameter's fp32 main_grad and
+ * nothing is communicated until the last micro-batch):
+ *   acc[i] = accumulate ? acc[i] + f32(grad[i]) : f32(grad[i]),  i < n.
+ * grad: n ZF_F16 / ZF_BF16 values (2-byte aligned); acc: n fp32 (4-byte
+ * aligned); any offsets, e.g. one bucket's range of a replica.  n >= 0.
+ * Errors: ZF_EINVAL, ZF_EALIGN, ZF_EDTYPE, ZF_EHIP. */
+int zf_accumulate(int32_t grad_dtype, const void* grad, float* acc, int64_t n, int32_t accumulate,
+                  void* stream);
 
 /* FSDP2 unshard of group g ([MDT] 五.4: each rank's fp32 shards are cast to
  * the parameter dtype, all-gathered and copied out into the full

@@ -86,14 +86,16 @@ def oracle_padded_params(run):
 
 
 def regen_sumsq_threaded(w, step, scale, psi, inject=None, chunks=None):
-    """Exact global sum of squared reduced gradients (and the overflow flag)
-    by regeneration, split over a thread pool; partials added in order."""
+    """Exact global sum of squared reduced (and, over the workload's
+    micro-batches, accumulated) gradients and the overflow flag by
+    regeneration, split over a thread pool; partials added in order."""
     chunks = chunks or max(POOL_THREADS * 4, 1)
     edges = np.linspace(0, psi, chunks + 1).astype(np.int64)
 
     def part(k):
-        return O.regen_sumsq(w.grad_dtype, w.n_ranks, w.seed, step, w.sigma, scale,
-                             int(edges[k]), int(edges[k + 1]), inject)
+        return O.regen_accum_sumsq(w.grad_dtype, w.n_ranks, w.n_micro, w.accum_mode, w.seed,
+                                   step, w.sigma, scale, int(edges[k]), int(edges[k + 1]),
+                                   inject)
 
     with ThreadPoolExecutor(POOL_THREADS) as ex:
         parts = list(ex.map(part, range(chunks)))
@@ -137,7 +139,7 @@ class SampledOracle:
         ss, bad = regen_sumsq_threaded(w, self.step_no, scale, self.psi, inj)
         sc, res = O.finish(ss, bad, w.n_ranks, self.hp, self.st)
         if not res.skipped:
-            acc = O.regen_acc(w.grad_dtype, w.n_ranks, w.seed, self.step_no, w.sigma, scale,
-                              self.idx, inj)
+            acc = O.regen_accum_acc(w.grad_dtype, w.n_ranks, w.n_micro, w.accum_mode, w.seed,
+                                    self.step_no, w.sigma, scale, self.idx, inj)
             O.adamw_array(acc, sc, self.p, self.m, self.v)
         return res

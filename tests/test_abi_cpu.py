@@ -57,8 +57,9 @@ def _oracle_units(w):
 
 @pytest.mark.parametrize("name", list(W.ALL))
 def test_plan_matches_oracle_layout(zf, name):
+    from fsdp_sharded_mixed_amd import runner
     w = W.get(name)
-    plan = zf.plan_flat(w.segments, w.n_ranks, w.layout, w.stage)
+    plan = runner.plan_workload(w)
     units, psi, psi_pad = _oracle_units(w)
     s = plan.summary
     assert (s.psi, s.psi_pad, s.n_units) == (psi, psi_pad, len(units))
@@ -175,13 +176,13 @@ def test_step_argument_errors_enqueue_nothing(zf):
 
     def args(**kw):
         d = dict(grad_dtype=1, param_dtype=1, grads=grads, master=ok, exp_avg=ok, exp_avg_sq=ok,
-                 params=ok, grad_shards=None, numel=100, workspace=ok, workspace_size=need,
-                 state=ok, phase_events=None)
+                 params=ok, grad_shards=None, grads_reduced=0, reserved=0, numel=100,
+                 workspace=ok, workspace_size=need, state=ok, phase_events=None)
         d.update(kw)
         return Z.StepArgs(d["grad_dtype"], d["param_dtype"], d["grads"], d["master"],
                           d["exp_avg"], d["exp_avg_sq"], d["params"], d["grad_shards"],
-                          d["numel"], d["workspace"], d["workspace_size"], d["state"],
-                          d["phase_events"])
+                          d["grads_reduced"], d["reserved"], d["numel"], d["workspace"],
+                          d["workspace_size"], d["state"], d["phase_events"])
 
     step = lambda a, p=plan.handle, h=hp: Z.lib.zf_shard_step(p, C.byref(h), C.byref(a), None)
     assert step(args(), p=None) == -1
@@ -220,6 +221,36 @@ def test_step_argument_errors_enqueue_nothing(zf):
     assert Z.lib.zf_gather(plan.handle, 0, 1, (C.c_void_p * 2)(ok, ok + 1), ok, 100, None) == -2
     assert Z.lib.zf_gather(plan.handle, 0, 1, shards, None, 100, None) == -1
     assert Z.lib.zf_gather(plan.handle, 0, 1, shards, ok, 99, None) == -4
+    # reduced gradients: the fp32 shards are required, the flag is 0 or 1
+    assert step(args(grads_reduced=1, grads=None)) == -1
+    assert step(args(grads_reduced=2, grad_shards=ok)) == -1
+    assert step(args(reserved=1)) == -1
+    assert step(args(grads_reduced=1, grads=None, grad_shards=ok, param_dtype=7)) == -3
+    assert step(args(grads_reduced=1, grads=None, grad_shards=ok + 8)) == -2
+    # bucket reduce-scatter
+    brs = Z.lib.zf_bucket_reduce_scatter
+    assert brs(None, 0, 1, grads, ok, 100, 0, None) == -1
+    assert brs(plan.handle, 1, 1, grads, ok, 100, 0, None) == -1
+    assert brs(plan.handle, -1, 1, grads, ok, 100, 0, None) == -1
+    assert brs(plan.handle, 0, 4, grads, ok, 100, 0, None) == -3
+    assert brs(plan.handle, 0, 0, grads, ok, 100, 0, None) == -3
+    assert brs(plan.handle, 0, 1, None, ok, 100, 0, None) == -1
+    assert brs(plan.handle, 0, 1, grads, None, 100, 0, None) == -1
+    assert brs(plan.handle, 0, 1, grads, ok + 4, 100, 0, None) == -2
+    assert brs(plan.handle, 0, 3, (C.c_void_p * 2)(ok, ok + 8), ok, 100, 0, None) == -2
+    assert brs(plan.handle, 0, 1, (C.c_void_p * 2)(None, ok), ok, 100, 0, None) == -1
+    assert brs(plan.handle, 0, 1, grads, ok, 99, 0, None) == -4
+    assert brs(plan.handle, 0, 1, grads, ok, 100, 2, None) == -1
+    # local accumulation (16-bit gradients only; element alignment)
+    acc = Z.lib.zf_accumulate
+    assert acc(1, None, ok, 10, 0, None) == -1
+    assert acc(1, ok, None, 10, 0, None) == -1
+    assert acc(3, ok, ok, 10, 0, None) == -3
+    assert acc(1, ok + 1, ok, 10, 0, None) == -2
+    assert acc(1, ok, ok + 2, 10, 0, None) == -2
+    assert acc(1, ok, ok, -1, 0, None) == -1
+    assert acc(1, ok, ok, 10, 5, None) == -1
+    assert acc(2, ok + 2, ok + 4, 0, 1, None) == 0  # nothing to do: no launch
     assert Z.lib.zf_state_init(None, 1.0, 0, 10, None) == -1
     assert Z.lib.zf_state_init(ok, 0.0, 0, 10, None) == -1
     assert Z.lib.zf_state_init(ok + 4, 1.0, 0, 10, None) == -2
@@ -238,3 +269,33 @@ def test_input_library_stream_output_matches_oracle():
             for j in range(3):
                 assert I.stream_output(seed, stream, j) == O.lib().or_splitmix64_next(
                     C.byref(state))
+
+
+def test_bucket_plan_matches_oracle(zf):
+    """zf_plan_buckets and the oracle's Megatron bucket rule agree on random
+    segment lists, explicit and default bucket sizes, and the 654M decoder
+    in Megatron's order; bad arguments are rejected."""
+    rng = np.random.default_rng(5)
+    for trial in range(300):
+        k = int(rng.integers(1, 40))
+        numel = [int(x) for x in rng.integers(1, 50, k)]
+        n = int(rng.integers(1, 65))
+        b = int(rng.integers(-1, 120))
+        ids, nb = zf.plan_buckets(numel, n, b)
+        ref, nref = O.bucket_assign(numel, n, b)
+        assert ids == list(ref) and nb == nref
+    w = W.get("llama-654m-n2-buckets-a4")
+    numel = [s.numel for s in w.segments]
+    ids, nb = zf.plan_buckets(numel, 2, 0)
+    ref, nref = O.bucket_assign(numel, 2, 0)
+    assert ids == list(ref) and nb == nref == 12
+    for bad in (([], 2, 0), ([5, 0], 2, 0)):
+        with pytest.raises(zf.ZfError):
+            zf.plan_buckets(*bad)
+    with pytest.raises(zf.ZfError):
+        zf.plan_buckets([5], 65, 0)
+    # a bucketed plan's groups are the buckets, padded to a multiple of N
+    p = zf.plan_flat([(nm, i) for nm, i in zip(numel, ids)], 2, W.PER_UNIT, 2)
+    assert p.summary.n_groups == p.summary.n_units == 12
+    for g, u in zip(p.groups, p.units):
+        assert g.padded == u.P and u.P % 2 == 0 and u.P - u.L < 2

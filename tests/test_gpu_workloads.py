@@ -76,10 +76,18 @@ def run_workload(R, name, rs_check_step=1):
     trace = []
     for k in range(1, w.steps + 1):
         scale = dev.loss_scale
-        dev.fill_grads(k, scale)
-        if w.inject_step == k:
-            dev.inject_inf()
-        if k == rs_check_step:
+        if w.backward_rs:
+            # every micro-batch filled and reduced bucket by bucket, then the step
+            for a in range(w.n_micro):
+                dev.fill_grads(k, scale, micro=a)
+                if w.inject_step == k and a == 0:
+                    dev.inject_inf()
+                dev.backward(a)
+        else:
+            dev.fill_grads(k, scale)
+            if w.inject_step == k:
+                dev.inject_inf()
+        if k == rs_check_step and not w.backward_rs:
             from fsdp_sharded_mixed_amd import zf
             rs = torch.empty(dev.psi_pad, dtype=torch.float32, device=dev.device)
             zf.reduce_scatter(dev.plan, w.grad_dtype, dev.grads, rs)
@@ -98,12 +106,13 @@ def run_workload(R, name, rs_check_step=1):
         G.say(f"  step {k}: skipped={res_d.skipped} t={res_d.t} S={res_d.scale_used}->"
               f"{res_d.scale_next} norm={res_d.norm:.6f} (oracle {res_o.norm:.6f}) "
               f"coef={res_d.coef:.6f} exact-share={share:.4f}")
+        if (w.fp32_params or w.backward_rs) and not res_d.skipped:
+            acc = O.regen_accum_acc(w.grad_dtype, w.n_ranks, w.n_micro, w.accum_mode, w.seed, k,
+                                    w.sigma, scale, idx)
+            got = take(dev.grad_shards, pidx).numpy()
+            assert np.array_equal(got.view(np.uint32), acc.view(np.uint32)), "grad shards"
         if w.fp32_params:
             check_group_gathers(dev, so, idx, w)
-            if not res_d.skipped:
-                acc = O.regen_acc(w.grad_dtype, w.n_ranks, w.seed, k, w.sigma, scale, idx)
-                got = take(dev.grad_shards, pidx).numpy()
-                assert np.array_equal(got.view(np.uint32), acc.view(np.uint32)), "grad shards"
         elif w.stage == 3:
             check_unit_gathers(dev, so, idx, w)
     return dev, trace
@@ -182,3 +191,15 @@ def test_llama4b_n2_injected_overflow(R):
     assert [(t[1], t[2]) for t in trace] == [(0, 1), (1, 1), (0, 2), (0, 3)]
     assert trace[1][3] == 32768.0 and trace[1][4] == 16384.0
     assert trace[2][3] == 16384.0
+
+
+@pytest.mark.parametrize("name", ["llama-654m-n2-buckets-a4", "llama-654m-n2-nosync-a4"])
+def test_llama654m_bucketed_accumulation(R, name):
+    """654M decoder in Megatron's gradient buffer (12 buckets of >= 40M
+    elements, last layer first), N = 2, four micro-batches per step: every
+    bucket reduce-scattered into the fp32 gradient shards each micro-batch,
+    or (no_sync) fp32 local accumulation and one reduction; global norm
+    about 3, so clipping is active."""
+    dev, trace = run_workload(R, name, rs_check_step=0)
+    assert len(dev.plan.groups) == 12
+    assert all(t[1] == 0 and abs(t[5] - 3.0) < 0.1 and t[6] < 1.0 for t in trace)
