@@ -3,7 +3,9 @@
 
 A step is one zf_shard_step over one batch of N resident replica gradients
 (reduce-scatter sums, overflow/norm/clip, fused AdamW + cast + gather), plus
-the per-unit gathers for a ZeRO-3 workload.  For a workload with gradient
+the per-unit gathers for a ZeRO-3 workload.  Under ZeRO-Offload a step is the
+GPU reduction, the download of the sums, CPU-Adam on the host state and the
+chunked upload of the 16-bit parameters.  For a workload with gradient
 accumulation, a step is first the backward-side reduction of its
 micro-batches (every bucket's reduce-scatter, accumulated into the fp32
 gradient shards), then the step on the reduced shards.  Inputs are seeded synthetic
@@ -95,19 +97,28 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def traffic_for(workload):
-    """Measured HBM bytes per launch of the update kernel from the committed
-    rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, each scaled by the
-    same counter's reading for a 1 GiB copy), or None if there is none or the
-    kernel source has changed since it was taken."""
-    path = os.path.join(PROFILES, f"zf_pass2_{workload}_traffic.json")
+def traffic_for(workload, kernel="zf_pass2", per="launch"):
+    """Measured HBM bytes of one of the step's kernels (per launch, or summed
+    over one step's launches) from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled by the same counter's reading for a
+    1 GiB copy), or None if there is none or the kernel sources have changed
+    since it was taken."""
+    path = os.path.join(PROFILES, f"zf_step_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         d = json.load(f)
-    if d.get("kernel_source_sha256_16") != kernel_source_hash():
+    if d.get("kernel_source_sha256_16") != kernel_source_hash() or kernel not in d:
         return None
-    return d["zf_pass2"]["hbm_bytes_per_launch"]
+    return d[kernel]["hbm_bytes_per_" + per]
+
+
+def backward_traffic(w):
+    """Measured HBM bytes of one step's backward-side launches, or None."""
+    parts = [traffic_for(w.name, k, "step") for k in
+             (("zf_bucket_rs_kernel",) if w.accum_mode == 0 else
+              ("zf_bucket_rs_kernel", "zf_accumulate_kernel"))]
+    return None if any(p is None for p in parts) else sum(parts)
 
 
 def _csv_rows(directory, suffix):
@@ -154,8 +165,12 @@ def summarize_pmc(fetch_dir, write_dir, workload, out, commands):
         hits = [v for k, v in vals.items() if key in k]
         if not hits:
             raise SystemExit(f"no dispatch of {key}")
-        xs = sorted(hits[0])
+        xs = sorted(x for h in hits for x in h)
         return xs[len(xs) // 2]  # median over dispatches (KiB)
+
+    def total(vals, key):
+        xs = [x for k, v in vals.items() if key in k for x in v]
+        return sum(xs), len(xs)
 
     fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
     copy_key = next(k for k in fetch if "copy" in k.lower() and "zf_" not in k)
@@ -166,14 +181,24 @@ def summarize_pmc(fetch_dir, write_dir, workload, out, commands):
            "calibration": {"kernel": copy_key, "bytes_each_way": COPY_BYTES,
                            "fetch_scale": f_scale, "write_scale": w_scale},
            "commands": commands}
-    for key in ("zf_pass1", "zf_pass2", "zf_gather"):
+    # one finish kernel per step: the step count of the run
+    _, steps = total(fetch, "zf_finish")
+    res["steps"] = steps
+    keys = ("zf_pass1_reduced", "zf_pass1<", "zf_pass2", "zf_gather_kernel",
+            "zf_gather_cast_kernel", "zf_bucket_rs_kernel", "zf_accumulate_kernel")
+    for key in keys:
         try:
             fb = pick(fetch, key) * 1024.0 * f_scale
             wb = pick(write, key) * 1024.0 * w_scale
         except SystemExit:
             continue
-        res[key] = {"fetch_bytes": fb, "write_bytes": wb, "hbm_bytes_per_launch": fb + wb,
-                    "per_param": (fb + wb) / w.psi}
+        ft, nf = total(fetch, key)
+        wt, _ = total(write, key)
+        step_bytes = (ft * f_scale + wt * w_scale) * 1024.0 / max(steps, 1)
+        res[key.rstrip("<")] = {
+            "launches_per_step": nf / max(steps, 1), "fetch_bytes": fb, "write_bytes": wb,
+            "hbm_bytes_per_launch": fb + wb, "hbm_bytes_per_step": step_bytes,
+            "per_param_per_step": step_bytes / w.psi}
     with open(out, "w") as f:
         json.dump(res, f, indent=1)
     print(json.dumps(res, indent=1))
@@ -215,6 +240,71 @@ def cpu_baseline(w, min_seconds=10.0, max_steps=40):
                       f"N={ws.n_ranks}, {steps} steps over one batch"
                       + (f" of {ws.n_micro} micro-batches" if ws.backward_rs else "")
                       + f", {dt:.1f} s, single-threaded C oracle"}
+
+
+def offload_line(args, w, dev, ms, wall, copy_gbs):
+    """The bench line of a ZeRO-Offload workload: the step's wall time, its
+    phases from the library's events (GPU reduction; the download of the
+    sums; CPU-Adam with the chunked upload), and CPU-Adam alone on the same
+    host arrays."""
+    import torch
+    from fsdp_sharded_mixed_amd import workloads as W, zf
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for row in evs:
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+    for row in evs:
+        dev.step(phase_events=[e.cuda_event for e in row])
+    torch.cuda.synchronize()
+    red = sum(r[0].elapsed_time(r[1]) for r in evs) / args.steps
+    down = sum(r[1].elapsed_time(r[2]) for r in evs) / args.steps
+    upd = sum(r[2].elapsed_time(r[3]) for r in evs) / args.steps
+    res = dev.last_result
+    assert res.skipped == 0
+    # CPU-Adam alone over the whole padded flat, same threads
+    n = dev.psi_pad
+    reps = 3
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        zf.cpu_adam(dev.hp, dev.h_grad, dev.master, dev.exp_avg, dev.exp_avg_sq, res.gs,
+                    res.bc1, res.bc2, params=dev.h_params, param_dtype=w.param_dtype,
+                    n_threads=dev.n_threads)
+    cpu_s = (time.perf_counter() - t0) / reps
+    threads = dev.n_threads if dev.n_threads > 0 else (os.cpu_count() or 1)
+    s = dev.plan.summary
+    alg = algorithmic_bytes_per_param(w) * w.psi
+    gbs = alg / (ms * 1e-3) / 1e9
+    p1_bytes = (2 * w.n_ranks + 4) * s.psi_pad
+    p1_gbs = p1_bytes / (red * 1e-3) / 1e9
+    return {
+        "metric": "ZeRO step GB/s (algorithmic bytes) and % of HBM peak; params updated/s",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32 state, " + ("bf16" if w.grad_dtype == W.BF16 else "f16") + " grads",
+        "data": "synthetic (seeded splitmix64/Irwin-Hall normal grads and master init, "
+                "random-init weights)",
+        "config": {"workload": w.name, "psi": w.psi, "psi_padded": s.psi_pad,
+                   "virtual_ranks": w.n_ranks, "zero_stage": w.stage,
+                   "offload": "fp32 state + CPU-Adam on the host",
+                   "cpu_adam_threads": threads, "pipeline_chunks": dev.n_chunks},
+        "params_updated_per_s": round(w.psi / (ms * 1e-3), 1),
+        "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+        "wall_ms_per_step": round(1e3 * wall / args.steps, 5),
+        "device_copy_gbs": round(copy_gbs, 1),
+        "phases_ms": {"gpu_reduce": round(red, 4), "download": round(down, 4),
+                      "cpu_adam_and_upload": round(upd, 4)},
+        "pcie_down_gbs": round(4 * n / (down * 1e-3) / 1e9, 2),
+        "cpu_adam": {"ms": round(cpu_s * 1e3, 3), "params_per_s": round(n / cpu_s, 1),
+                     "host_gbs": round(30 * n / cpu_s / 1e9, 2), "threads": threads,
+                     "host_cpus": os.cpu_count()},
+        "roofline": {"bound": "hbm", "achieved": round(p1_gbs, 2), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(p1_gbs / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_for(w.name, "zf_pass1"),
+                     "kernel": "zf_pass1 (reduce-scatter sums + norm partials, the offload "
+                               "step's GPU kernel)", "bytes_per_launch": p1_bytes},
+    }
 
 
 def main():
@@ -300,6 +390,13 @@ def main():
     res = dev.result()
     assert res.skipped == 0
 
+    if w.offload:
+        line = offload_line(args, w, dev, ms, wall, copy_gbs)
+        if not args.no_cpu_baseline:
+            line["cpu_baseline"] = cpu_baseline(w)
+        print(json.dumps(line), flush=True)
+        return
+
     # per-kernel durations: a second run of K steps with HIP events recorded
     # by the library between its kernels, on the step's stream
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
@@ -326,7 +423,7 @@ def main():
     upd_gbs = upd_bytes / (p2 * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(upd_gbs, 2), "peak": PEAK_HBM_GBS,
             "unit": "GB/s", "frac": round(upd_gbs / PEAK_HBM_GBS, 4),
-            "traffic": traffic_for(w.name),
+            "traffic": traffic_for(w.name, "zf_pass2"),
             "kernel": "zf_pass2 (fused AdamW" + ("" if w.fp32_params else "+cast+gather") + ")",
             "bytes_per_launch": upd_bytes}
     kernels = {"pass1_rs_norm": round(p1, 5), "finish": round(fin, 5),
@@ -342,11 +439,11 @@ def main():
             # roofline row (all its launches of one step, back to back)
             roof = {"bound": "hbm", "achieved": round(bw_gbs, 2), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(bw_gbs / PEAK_HBM_GBS, 4),
-                    "traffic": None,
+                    "traffic": backward_traffic(w),
                     "kernel": ("zf_bucket_rs_kernel (every bucket of every micro-batch)"
                                if w.accum_mode == 0 else
                                "zf_accumulate_kernel + zf_bucket_rs_kernel (no_sync)"),
-                    "bytes_per_launch": bw_bytes, "launches_per_step":
+                    "bytes_per_step": bw_bytes, "launches_per_step":
                         kernels["backward_launches"]}
         kernels["backward_gbs"] = round(bw_gbs, 2)
     line = {

@@ -1,6 +1,7 @@
 """Compile the HIP libraries in-tree for gfx950.
 
-libzf.so         the step (planner + kernels + C ABI, include/zf.h)
+libzf.so         the step (planner + kernels + C ABI, include/zf.h) and the
+                 host side of ZeRO-Offload (CPU-Adam, the offload step)
 libzf_inputs.so  the seeded input generator (include/zf_inputs.h)
 
 Flags that matter for the arithmetic contract:
@@ -25,14 +26,18 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-command-line-argument",
+    "-Wall", "-Wno-unused-command-line-argument", "-pthread",
     "-I", INCLUDE, "-I", CSRC,
 ]
 
 
-def _hipcc(out, sources):
+def _hipcc(out, sources, host_sources=()):
+    """Link `sources` (HIP) and `host_sources` (plain host C++) into `out`."""
     tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-o", tmp, *sources]
+    cmd = [HIPCC, *FLAGS, "-o", tmp]
+    if host_sources:
+        cmd += ["-x", "c++", *host_sources]
+    cmd += ["-x", "hip", *sources]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out
@@ -40,7 +45,8 @@ def _hipcc(out, sources):
 
 def build():
     """Build both libraries; returns their paths."""
-    zf = _hipcc(LIB_ZF, [os.path.join(CSRC, "zf_plan.cpp"), os.path.join(CSRC, "zf_step.hip")])
+    zf = _hipcc(LIB_ZF, [os.path.join(CSRC, f) for f in ("zf_step.hip", "zf_offload.hip")],
+                [os.path.join(CSRC, f) for f in ("zf_plan.cpp", "zf_cpu_adam.cpp")])
     inputs = _hipcc(LIB_INPUTS, [os.path.join(CSRC, "zf_inputs.hip")])
     return zf, inputs
 

@@ -1,4 +1,5 @@
-// zf_internal.h -- the plan record shared by the planner and the step code.
+// zf_internal.h -- the plan record and step internals shared by the planner,
+// the step code and the offload step.
 #pragma once
 #include <cstdint>
 #include <vector>
@@ -57,6 +58,52 @@ inline int unr_pass2(int n_ranks, int64_t psi_pad, bool materialize) {
 #endif
 }
 constexpr int kMaxLevel2Blocks = 1024;
+
+// The device state block (the caller's zf_state_bytes() buffer), also read
+// on the host by the offload step.
+struct alignas(16) DevState {
+  double loss_scale;     // S for the next step
+  double beta1_pow;      // beta1^t after t applied steps (1 at t = 0)
+  double beta2_pow;
+  int64_t t;
+  int32_t growth_ctr, growth_interval, dynamic, pad0;
+  // result of the last step
+  int32_t overflow, skipped;
+  double sumsq, norm, coef, scale_used;
+  float gs, bc1, bc2, pad1;
+};
+static_assert(sizeof(DevState) <= 256, "state block");
+constexpr int64_t kStateBytes = 256;
+
+// Validates `args` and enqueues the step on `stream`: pass 1, the norm
+// reduction and the finish kernel, then (update == true) the update pass.
+// With update == false the fp32 state and params are neither needed nor
+// touched and grad_shards must be given (pass 1 leaves the sums there).
+int step_enqueue(const zf_plan* plan, const zf_hparams* hp, const zf_step_args* args,
+                 void* stream, bool update);
+
+// Binary32 hyperparameters of the update, each rounded once from its double.
+struct UpdateConsts {
+  float dec, b1, c1, b2, c2, lrf, ef;
+};
+inline UpdateConsts update_consts(const zf_hparams* hp) {
+  UpdateConsts c;
+  c.dec = (float)(1.0 - hp->lr * hp->weight_decay);
+  c.b1 = (float)hp->beta1;
+  c.c1 = (float)(1.0 - hp->beta1);
+  c.b2 = (float)hp->beta2;
+  c.c2 = (float)(1.0 - hp->beta2);
+  c.lrf = (float)hp->lr;
+  c.ef = (float)hp->eps;
+  return c;
+}
+
+// CPU-Adam (host, AVX2): the update pass's element arithmetic over [0, n)
+// with the given step scalars, split over n_threads threads (<= 0: all).
+bool host_simd_ok();
+void cpu_adam_run(const zf_hparams* hp, float gs, float bc1, float bc2, int64_t n,
+                  const float* grad, float* master, float* exp_avg, float* exp_avg_sq,
+                  uint16_t* params, int32_t param_dtype, int32_t n_threads);
 
 }  // namespace zf
 

@@ -1,0 +1,147 @@
+// zf_offload.hip -- the ZeRO-Offload step: GPU reduction, PCIe both ways,
+// CPU-Adam in between (host code; the kernels are the step's).
+//
+// CMU 15-779 Lecture 13 notes, "Zero Redundancy and PyTorch FSDP", 7.1-7.2:
+// only the 16-bit parameters stay on the GPU; gradients go down, the CPU
+// updates the fp32 state, and the new 16-bit parameters go up in chunks
+// that overlap the CPU update of the next chunk.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "zf_internal.h"
+
+namespace {
+
+constexpr int64_t kChunkAlign = 16;  // chunk starts: whole CPU-Adam vectors
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+void fill_result(const zf::DevState& h, zf_step_result* out) {
+  if (!out) return;
+  out->overflow = h.overflow;
+  out->skipped = h.skipped;
+  out->t = h.t;
+  out->sumsq = h.sumsq;
+  out->norm = h.norm;
+  out->coef = h.coef;
+  out->scale_used = h.scale_used;
+  out->scale_next = h.loss_scale;
+  out->gs = h.gs;
+  out->growth_ctr = h.growth_ctr;
+  out->bc1 = h.bc1;
+  out->bc2 = h.bc2;
+}
+
+}  // namespace
+
+extern "C" int zf_offload_step(const zf_plan* plan, const zf_hparams* hp,
+                               const zf_offload_args* a, void* stream, zf_step_result* result) {
+  if (!plan || plan->magic != zf::kPlanMagic || !hp || !a) return ZF_EINVAL;
+  if (a->reserved != 0 || a->n_chunks < 1 || a->n_chunks > 4096) return ZF_EINVAL;
+  if (a->param_dtype != ZF_F16 && a->param_dtype != ZF_BF16) return ZF_EDTYPE;
+  if (!a->params || !a->grad_shards || !a->h_state || !a->h_grad || !a->h_master ||
+      !a->h_exp_avg || !a->h_exp_avg_sq || !a->h_params)
+    return ZF_EINVAL;
+  if (!aligned(a->params, 16) || !aligned(a->h_state, 16)) return ZF_EALIGN;
+  const void* hf[] = {a->h_grad, a->h_master, a->h_exp_avg, a->h_exp_avg_sq};
+  for (const void* q : hf)
+    if (!aligned(q, 16)) return ZF_EALIGN;
+  if (!aligned(a->h_params, 16)) return ZF_EALIGN;
+  if (!zf::host_simd_ok()) return ZF_EUNSUP;
+  const int64_t n = plan->summary.psi_pad;
+  if (a->numel < n) return ZF_ESIZE;
+
+  // the GPU side: pass 1, norm reduction, finish (validates the rest)
+  zf_step_args s{};
+  s.grad_dtype = a->grad_dtype;
+  s.param_dtype = a->param_dtype;
+  s.grads = a->grads;
+  s.params = a->params;
+  s.grad_shards = a->grad_shards;
+  s.grads_reduced = a->grads_reduced;
+  s.numel = a->numel;
+  s.workspace = a->workspace;
+  s.workspace_size = a->workspace_size;
+  s.state = a->state;
+  // the step records "before pass 1" and "after the finish" into ours
+  void* step_events[4] = {nullptr, nullptr, nullptr, nullptr};
+  if (a->phase_events) {
+    step_events[0] = a->phase_events[0];
+    step_events[2] = a->phase_events[1];
+    s.phase_events = step_events;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  auto record = [&](int i) {
+    if (!a->phase_events || !a->phase_events[i]) return true;
+    return hipEventRecord(static_cast<hipEvent_t>(a->phase_events[i]), st) == hipSuccess;
+  };
+  int rc = zf::step_enqueue(plan, hp, &s, stream, false);
+  if (rc != ZF_OK) return rc;
+  const int64_t C = std::min<int64_t>(a->n_chunks, (n + kChunkAlign - 1) / kChunkAlign);
+  auto chunk = [&](int64_t c, int64_t& b, int64_t& e) {
+    const int64_t blocks = (n + kChunkAlign - 1) / kChunkAlign;
+    b = std::min(n, blocks * c / C * kChunkAlign);
+    e = std::min(n, blocks * (c + 1) / C * kChunkAlign);
+  };
+  // down: the state block, then the sums chunk by chunk, each with an event
+  std::vector<hipEvent_t> down(C, nullptr);
+  auto cleanup = [&]() {
+    for (hipEvent_t& ev : down)
+      if (ev) (void)hipEventDestroy(ev);
+  };
+  if (hipMemcpyAsync(a->h_state, a->state, sizeof(zf::DevState), hipMemcpyDeviceToHost, st) !=
+      hipSuccess)
+    return ZF_EHIP;
+  for (int64_t c = 0; c < C; ++c) {
+    int64_t b, e;
+    chunk(c, b, e);
+    if (hipEventCreateWithFlags(&down[c], hipEventDisableTiming) != hipSuccess ||
+        hipMemcpyAsync(a->h_grad + b, a->grad_shards + b, (e - b) * sizeof(float),
+                       hipMemcpyDeviceToHost, st) != hipSuccess ||
+        hipEventRecord(down[c], st) != hipSuccess) {
+      cleanup();
+      return ZF_EHIP;
+    }
+  }
+  if (!record(2)) {
+    cleanup();
+    return ZF_EHIP;
+  }
+  // the state block arrived with the first chunk (same stream, earlier)
+  if (hipEventSynchronize(down[0]) != hipSuccess) {
+    cleanup();
+    return ZF_EHIP;
+  }
+  zf::DevState h;
+  std::memcpy(&h, a->h_state, sizeof(h));
+  if (!h.skipped) {
+    uint16_t* hp16 = static_cast<uint16_t*>(a->h_params);
+    char* dp16 = static_cast<char*>(a->params);
+    for (int64_t c = 0; c < C; ++c) {
+      int64_t b, e;
+      chunk(c, b, e);
+      if (hipEventSynchronize(down[c]) != hipSuccess) {
+        cleanup();
+        return ZF_EHIP;
+      }
+      zf::cpu_adam_run(hp, h.gs, h.bc1, h.bc2, e - b, a->h_grad + b, a->h_master + b,
+                       a->h_exp_avg + b, a->h_exp_avg_sq + b, hp16 + b, a->param_dtype,
+                       a->n_threads);
+      // up: this chunk's 16-bit parameters while the CPU takes the next one
+      if (hipMemcpyAsync(dp16 + 2 * b, hp16 + b, (e - b) * sizeof(uint16_t),
+                         hipMemcpyHostToDevice, st) != hipSuccess) {
+        cleanup();
+        return ZF_EHIP;
+      }
+    }
+  }
+  const bool ok = record(3) && hipStreamSynchronize(st) == hipSuccess;
+  cleanup();
+  if (!ok) return ZF_EHIP;
+  fill_result(h, result);
+  return ZF_OK;
+}

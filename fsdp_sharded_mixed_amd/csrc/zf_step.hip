@@ -34,21 +34,8 @@ namespace {
 
 using zf::kThreads;
 
-// ---------------------------------------------------------------------------
-// Device state block (the caller's zf_state_bytes() buffer).
-struct __align__(16) DevState {
-  double loss_scale;     // S for the next step
-  double beta1_pow;      // beta1^t after t applied steps (1 at t = 0)
-  double beta2_pow;
-  int64_t t;
-  int32_t growth_ctr, growth_interval, dynamic, pad0;
-  // result of the last step
-  int32_t overflow, skipped;
-  double sumsq, norm, coef, scale_used;
-  float gs, bc1, bc2, pad1;
-};
-static_assert(sizeof(DevState) <= 256, "state block");
-constexpr int64_t kStateBytes = 256;
+using zf::DevState;
+using zf::kStateBytes;
 
 struct __align__(16) Partial {
   double ss;
@@ -870,8 +857,8 @@ extern "C" int zf_state_init(void* d_state, double loss_scale, int32_t dynamic,
   return hipGetLastError() == hipSuccess ? ZF_OK : ZF_EHIP;
 }
 
-extern "C" int zf_shard_step(const zf_plan* plan, const zf_hparams* hp,
-                             const zf_step_args* args, void* stream) {
+int zf::step_enqueue(const zf_plan* plan, const zf_hparams* hp, const zf_step_args* args,
+                     void* stream, bool update) {
   if (!valid_plan(plan) || !hp || !args) return ZF_EINVAL;
   const zf_plan_summary& sm = plan->summary;
   if (args->grads_reduced != 0 && args->grads_reduced != 1) return ZF_EINVAL;
@@ -889,11 +876,12 @@ extern "C" int zf_shard_step(const zf_plan* plan, const zf_hparams* hp,
   } else if ((rc = grads_ok(plan, args->grads, gp)) != ZF_OK) {
     return rc;
   }
-  void* const bufs[] = {args->master, args->exp_avg, args->exp_avg_sq, args->state};
-  for (void* b : bufs) {
-    if (!b) return ZF_EINVAL;
-    if (!aligned16(b)) return ZF_EALIGN;
+  void* const bufs[] = {args->state, args->master, args->exp_avg, args->exp_avg_sq};
+  for (int i = 0; i < (update ? 4 : 1); ++i) {
+    if (!bufs[i]) return ZF_EINVAL;
+    if (!aligned16(bufs[i])) return ZF_EALIGN;
   }
+  if (!update && !args->grad_shards) return ZF_EINVAL;
   if (args->params && !aligned16(args->params)) return ZF_EALIGN;
   if (args->grad_shards && !aligned16(args->grad_shards)) return ZF_EALIGN;
   if (sm.policy == 2 && !args->grad_shards) return ZF_EINVAL;
@@ -956,8 +944,10 @@ extern "C" int zf_shard_step(const zf_plan* plan, const zf_hparams* hp,
   hipLaunchKernelGGL(zf_finish, dim3(1), dim3(kThreads), 0, s, af);
   if (hipGetLastError() != hipSuccess) return ZF_EHIP;
   if ((rc = record(args->phase_events, 2, s)) != ZF_OK) return rc;
+  if (!update) return ZF_OK;
 
   // binary32 hyperparameters, each rounded once from its double value
+  const zf::UpdateConsts uc = zf::update_consts(hp);
   Pass2Args a2;
   a2.g = gp;
   a2.rs = rs;
@@ -967,13 +957,13 @@ extern "C" int zf_shard_step(const zf_plan* plan, const zf_hparams* hp,
   a2.out = args->params;
   a2.st = static_cast<const DevState*>(args->state);
   a2.n = sm.psi_pad;
-  a2.dec = (float)(1.0 - hp->lr * hp->weight_decay);
-  a2.b1 = (float)hp->beta1;
-  a2.c1 = (float)(1.0 - hp->beta1);
-  a2.b2 = (float)hp->beta2;
-  a2.c2 = (float)(1.0 - hp->beta2);
-  a2.lrf = (float)hp->lr;
-  a2.ef = (float)hp->eps;
+  a2.dec = uc.dec;
+  a2.b1 = uc.b1;
+  a2.c1 = uc.c1;
+  a2.b2 = uc.b2;
+  a2.c2 = uc.c2;
+  a2.lrf = uc.lrf;
+  a2.ef = uc.ef;
   a2.nr = nr;
   // with reduced gradients pass 2 reads grad_shards (mat); the gradient
   // dtype then only names an instantiation
@@ -981,6 +971,11 @@ extern "C" int zf_shard_step(const zf_plan* plan, const zf_hparams* hp,
                     args->params != nullptr, s, a2);
   if (rc != ZF_OK) return rc;
   return record(args->phase_events, 3, s);
+}
+
+extern "C" int zf_shard_step(const zf_plan* plan, const zf_hparams* hp,
+                             const zf_step_args* args, void* stream) {
+  return zf::step_enqueue(plan, hp, args, stream, true);
 }
 
 extern "C" int zf_reduce_scatter(const zf_plan* plan, int32_t grad_dtype,
@@ -1172,5 +1167,7 @@ extern "C" int zf_read_result(const void* d_state, zf_step_result* out, void* st
   out->scale_next = h.loss_scale;
   out->gs = h.gs;
   out->growth_ctr = h.growth_ctr;
+  out->bc1 = h.bc1;
+  out->bc2 = h.bc2;
   return ZF_OK;
 }

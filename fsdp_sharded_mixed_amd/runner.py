@@ -47,14 +47,25 @@ class DeviceRun:
         self.main_grads = ([torch.zeros(n, dtype=torch.float32, device=dev)
                             for _ in range(w.n_ranks)]
                            if w.backward_rs and w.accum_mode == W.ACCUM_NO_SYNC else None)
-        self.master = torch.zeros(n, dtype=torch.float32, device=dev)
-        self.exp_avg = torch.zeros(n, dtype=torch.float32, device=dev)
-        self.exp_avg_sq = torch.zeros(n, dtype=torch.float32, device=dev)
+        # ZeRO-Offload keeps the fp32 state on the host: the master and both
+        # moments in host memory, pinned staging for the sums coming down and
+        # the 16-bit parameters going up
+        sdev = torch.device("cpu") if w.offload else dev
+        self.master = torch.zeros(n, dtype=torch.float32, device=sdev)
+        self.exp_avg = torch.zeros(n, dtype=torch.float32, device=sdev)
+        self.exp_avg_sq = torch.zeros(n, dtype=torch.float32, device=sdev)
+        if w.offload:
+            self.h_grad = torch.empty(n, dtype=torch.float32, pin_memory=True)
+            self.h_params = torch.empty(n, dtype=pdt, pin_memory=True)
+            self.h_state = torch.empty(zf.state_bytes(), dtype=torch.uint8, pin_memory=True)
+        self.n_threads = 0   # CPU-Adam threads (0: every hardware thread)
+        self.n_chunks = 8    # offload pipeline chunks
+        self.last_result = None
         # FSDP2 keeps fp32 parameters (no 16-bit copy) and resident fp32
         # gradient shards; the other layouts keep a 16-bit copy
         self.params = None if w.fp32_params else torch.zeros(n, dtype=pdt, device=dev)
         self.grad_shards = (torch.zeros(n, dtype=torch.float32, device=dev)
-                            if s.policy == 2 or w.backward_rs else None)
+                            if s.policy == 2 or w.backward_rs or w.offload else None)
         self.workspace = torch.empty(max(1, s.workspace_bytes), dtype=torch.uint8, device=dev)
         self.state = torch.empty(zf.state_bytes(), dtype=torch.uint8, device=dev)
         self.unit_buf = (torch.empty(s.max_unit_pad, dtype=pdt, device=dev)
@@ -76,18 +87,23 @@ class DeviceRun:
         """fp32 master from the seeded stream (norm weights 1.0 where the
         workload says so), m = v = 0, 16-bit params = RNE(master), t = 0."""
         w = self.w
-        self.master.zero_()
+        master = (torch.zeros(self.psi_pad, dtype=torch.float32, device=self.device)
+                  if w.offload else self.master)
+        master.zero_()
         for u in self.plan.units:
-            I.fill_normal32(self.master, u.L, w.seed, W.STREAM_MASTER, u.lam, w.master_sigma,
+            I.fill_normal32(master, u.L, w.seed, W.STREAM_MASTER, u.lam, w.master_sigma,
                             offset=u.O)
         if w.norm_weights_one:
             for a, b in w.norm_ranges():
                 pa = self.logical_to_padded(a)
-                self.master[pa:pa + (b - a)] = 1.0
+                master[pa:pa + (b - a)] = 1.0
         self.exp_avg.zero_()
         self.exp_avg_sq.zero_()
         if self.params is not None:
-            self.params.copy_(self.master.to(self.params.dtype))
+            self.params.copy_(master.to(self.params.dtype))
+        if w.offload:
+            self.master.copy_(master.cpu())
+            del master
         zf.state_init(self.state, w.loss_scale, w.dynamic, w.growth_interval)
         self.step_no = 0
         self.loss_scale = w.loss_scale
@@ -150,6 +166,15 @@ class DeviceRun:
     def step(self, stream=None, phase_events=None):
         self.step_no += 1
         reduced = self.w.backward_rs
+        if self.w.offload:
+            self.last_result = zf.offload_step(
+                self.plan, self.hp, self.w.grad_dtype, self.w.param_dtype,
+                None if reduced else self.grads, self.grad_shards, self.params,
+                self.workspace, self.state, self.h_state, self.h_grad, self.master,
+                self.exp_avg, self.exp_avg_sq, self.h_params, stream=stream,
+                grads_reduced=reduced, n_threads=self.n_threads, n_chunks=self.n_chunks,
+                phase_events=phase_events)
+            return
         zf.shard_step(self.plan, self.hp, self.w.grad_dtype, self.w.param_dtype,
                       None if reduced else self.grads, self.master, self.exp_avg,
                       self.exp_avg_sq, self.params, self.workspace, self.state, stream=stream,

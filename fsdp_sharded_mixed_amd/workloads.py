@@ -99,6 +99,9 @@ class Workload:
     # gradient buckets over the segments in the given order (0: the default
     # bucket size max(40M, 1M * N)); each side computes the bucket ids itself
     bucket_numel: Optional[int] = None
+    # ZeRO-Offload: fp32 master / moments and the update on the host
+    # (CPU-Adam), 16-bit parameters on the GPU
+    offload: bool = False
     extra: dict = field(default_factory=dict)
 
     @property
@@ -257,6 +260,19 @@ def llama654m_buckets(mode=ACCUM_REDUCE_EACH) -> Workload:
         n_micro=a, accum_mode=mode, bucket_numel=0)
 
 
+def llama654m_offload() -> Workload:
+    """The 654M decoder under ZeRO-Offload: the GPU keeps the replicas, the
+    reduce-scatter and norm passes and the bf16 parameters; the fp32 state
+    and the AdamW update live on the host (lecture notes 7.1-7.2)."""
+    w = llama654m()
+    w.name = "llama-654m-n2-offload"
+    w.description = ("Llama-style decoder h2048/i8192/32h/8kv/8L/V40960, Psi=654,346,240, "
+                     "one global flat, N=2, bf16 grads (global norm about 3), ZeRO-Offload: "
+                     "fp32 state and CPU-Adam on the host, bf16 params uploaded in chunks")
+    w.offload, w.seed, w.steps = True, 8, 3
+    return w
+
+
 ALL = {
     "tiny": tiny,
     "llama-73m-n8": llama73m,
@@ -266,6 +282,7 @@ ALL = {
     "llama-4.06b-n2": llama4b,
     "llama-654m-n2-buckets-a4": llama654m_buckets,
     "llama-654m-n2-nosync-a4": lambda: llama654m_buckets(ACCUM_NO_SYNC),
+    "llama-654m-n2-offload": llama654m_offload,
 }
 
 

@@ -17,7 +17,7 @@ F16, BF16, F32 = 1, 2, 3
 GLOBAL_FLAT, PER_UNIT, PER_PARAM_DIM0 = 0, 1, 2
 MAX_RANKS = 64
 STATUS = {0: "ZF_OK", -1: "ZF_EINVAL", -2: "ZF_EALIGN", -3: "ZF_EDTYPE", -4: "ZF_ESIZE",
-          -5: "ZF_EHIP", -6: "ZF_ENOMEM"}
+          -5: "ZF_EHIP", -6: "ZF_ENOMEM", -7: "ZF_EUNSUP"}
 
 
 class ZfError(RuntimeError):
@@ -69,7 +69,26 @@ class StepResult(C.Structure):
     _fields_ = [("overflow", C.c_int32), ("skipped", C.c_int32), ("t", C.c_int64),
                 ("sumsq", C.c_double), ("norm", C.c_double), ("coef", C.c_double),
                 ("scale_used", C.c_double), ("scale_next", C.c_double), ("gs", C.c_float),
-                ("growth_ctr", C.c_int32)]
+                ("growth_ctr", C.c_int32), ("bc1", C.c_float), ("bc2", C.c_float)]
+
+
+class CpuAdamArgs(C.Structure):
+    _fields_ = [("n", C.c_int64), ("grad", C.c_void_p), ("master", C.c_void_p),
+                ("exp_avg", C.c_void_p), ("exp_avg_sq", C.c_void_p), ("params", C.c_void_p),
+                ("param_dtype", C.c_int32), ("n_threads", C.c_int32), ("gs", C.c_float),
+                ("bc1", C.c_float), ("bc2", C.c_float), ("reserved", C.c_int32)]
+
+
+class OffloadArgs(C.Structure):
+    _fields_ = [("grad_dtype", C.c_int32), ("param_dtype", C.c_int32),
+                ("grads", C.POINTER(C.c_void_p)), ("grad_shards", C.c_void_p),
+                ("params", C.c_void_p), ("numel", C.c_int64), ("workspace", C.c_void_p),
+                ("workspace_size", C.c_int64), ("state", C.c_void_p), ("h_state", C.c_void_p),
+                ("h_grad", C.c_void_p), ("h_master", C.c_void_p), ("h_exp_avg", C.c_void_p),
+                ("h_exp_avg_sq", C.c_void_p), ("h_params", C.c_void_p),
+                ("grads_reduced", C.c_int32), ("n_threads", C.c_int32),
+                ("n_chunks", C.c_int32), ("reserved", C.c_int32),
+                ("phase_events", C.POINTER(C.c_void_p))]
 
 
 # Every function declared in include/zf.h, with its ctypes signature.
@@ -99,6 +118,9 @@ _SIGNATURES = {
     "zf_accumulate": (C.c_int, [C.c_int32, C.c_void_p, C.c_void_p, C.c_int64, C.c_int32,
                                 C.c_void_p]),
     "zf_read_result": (C.c_int, [C.c_void_p, C.POINTER(StepResult), C.c_void_p]),
+    "zf_cpu_adam": (C.c_int, [C.POINTER(Hparams), C.POINTER(CpuAdamArgs)]),
+    "zf_offload_step": (C.c_int, [C.c_void_p, C.POINTER(Hparams), C.POINTER(OffloadArgs),
+                                  C.c_void_p, C.POINTER(StepResult)]),
     "zf_strerror": (C.c_char_p, [C.c_int]),
 }
 
@@ -318,4 +340,44 @@ def gather_cast(plan, group, dtype, master, out, stream=None, master_numel=None,
 def read_result(state, stream=None):
     out = StepResult()
     _check(lib.zf_read_result(_ptr(state), C.byref(out), _stream(stream)), "zf_read_result")
+    return out
+
+
+def cpu_adam(hp, grad, master, exp_avg, exp_avg_sq, gs, bc1, bc2, params=None,
+             param_dtype=BF16, n_threads=0, n=None):
+    """zf_cpu_adam on host arrays (numpy arrays, CPU tensors or addresses)."""
+    def addr(x):
+        if x is None or isinstance(x, int):
+            return x
+        if hasattr(x, "data_ptr"):
+            return x.data_ptr()
+        return x.ctypes.data
+    if n is None:
+        n = len(master)
+    a = CpuAdamArgs(int(n), addr(grad), addr(master), addr(exp_avg), addr(exp_avg_sq),
+                    addr(params), int(param_dtype), int(n_threads), float(gs), float(bc1),
+                    float(bc2), 0)
+    _check(lib.zf_cpu_adam(C.byref(hp), C.byref(a)), "zf_cpu_adam")
+
+
+def offload_step(plan, hp, grad_dtype, param_dtype, grads, grad_shards, params, workspace,
+                 state, h_state, h_grad, h_master, h_exp_avg, h_exp_avg_sq, h_params,
+                 stream=None, grads_reduced=False, n_threads=0, n_chunks=8, numel=None,
+                 phase_events=None):
+    """zf_offload_step; device tensors for grads/grad_shards/params/workspace/
+    state, host (pinned) tensors for the h_ arrays; phase_events: None or 4
+    raw hipEvent_t handles.  Returns the StepResult."""
+    ev = (C.c_void_p * 4)(*phase_events) if phase_events is not None else None
+    if numel is None:
+        arrays = list(grads or []) + [grad_shards, params]
+        numel = min(t.numel() for t in arrays if t is not None)
+    gp = _ptr_array(grads) if grads is not None else None
+    a = OffloadArgs(int(grad_dtype), int(param_dtype), gp, _ptr(grad_shards), _ptr(params),
+                    int(numel), _ptr(workspace), _nbytes(workspace, None), _ptr(state),
+                    _ptr(h_state), _ptr(h_grad), _ptr(h_master), _ptr(h_exp_avg),
+                    _ptr(h_exp_avg_sq), _ptr(h_params), int(bool(grads_reduced)),
+                    int(n_threads), int(n_chunks), 0, ev)
+    out = StepResult()
+    _check(lib.zf_offload_step(_handle(plan), C.byref(hp), C.byref(a), _stream(stream),
+                               C.byref(out)), "zf_offload_step")
     return out

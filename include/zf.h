@@ -17,7 +17,8 @@
  *   [L13] CMU 15-779 Lecture 13 notes, "Zero Redundancy and PyTorch FSDP":
  *         2.1 Adam, 2.2 fp32 master weights, 3.1-3.3 the three ZeRO stages,
  *         3.4 bit-exactness, 3.6 padding, 4.1 communication, 5.1 FSDP's
- *         per-unit all-gather, 5.2 FlatParameter (flatten, pad, split).
+ *         per-unit all-gather, 5.2 FlatParameter (flatten, pad, split),
+ *         5.6 gradient accumulation, 7.1-7.2 ZeRO-Offload and CPU-Adam.
  *   [F6]  Femtotron dev log #6 (ZeRO-1 and ZeRO-2): the sharding protocol
  *         make_master / reduce_grads / gather_weights / post_step, and the
  *         master as one 1-D vector.
@@ -79,7 +80,8 @@ enum zf_status {
   ZF_EDTYPE = -3,  /* unknown dtype                                            */
   ZF_ESIZE = -4,   /* a size overflows or exceeds a limit                      */
   ZF_EHIP = -5,    /* the HIP runtime reported an error                        */
-  ZF_ENOMEM = -6   /* host allocation for a plan failed                        */
+  ZF_ENOMEM = -6,  /* host allocation for a plan failed                        */
+  ZF_EUNSUP = -7   /* the host CPU lacks an instruction set a call needs        */
 };
 
 /* ZF_F32 is accepted only where a call says so (the fp32 replicas of
@@ -339,11 +341,86 @@ typedef struct {
   double scale_next;    /* loss scale for the next step */
   float gs;             /* binary32 factor applied to the sums */
   int32_t growth_ctr;
+  float bc1, bc2;       /* binary32 bias corrections 1 - beta^t of the update */
 } zf_step_result;
 
 /* Copy the last step's result from a device state block to the host.
  * Synchronises `stream`.  Errors: ZF_EINVAL, ZF_EHIP. */
 int zf_read_result(const void* d_state, zf_step_result* out, void* stream);
+
+/* ---- ZeRO-Offload ([L13] 7.1-7.2) --------------------------------------
+ * The offload partition keeps the 16-bit parameters (and forward/backward)
+ * on the GPU; the fp32 master, exp_avg, exp_avg_sq and the Adam update live
+ * on the CPU.  Gradients go down PCIe, updated 16-bit parameters come back
+ * up in chunks that overlap the CPU update of the next chunk. */
+
+typedef struct {
+  int64_t n;                /* elements */
+  const float* grad;        /* n fp32 reduced gradient sums, still loss-scaled */
+  float* master;            /* n fp32, updated in place */
+  float* exp_avg;           /* n fp32 */
+  float* exp_avg_sq;        /* n fp32 */
+  void* params;             /* NULL, or n 16-bit outputs RNE16(master) */
+  int32_t param_dtype;      /* ZF_F16 or ZF_BF16 (when params is given) */
+  int32_t n_threads;        /* worker threads; <= 0: every hardware thread */
+  float gs, bc1, bc2;       /* the step's scalars, from zf_step_result */
+  int32_t reserved;         /* must be 0 */
+} zf_cpu_adam_args;
+
+/* CPU-Adam ([L13] 7.2: a SIMD, multithreaded Adam on the CPU): the same
+ * element update as zf_shard_step's update pass, in the same binary32
+ * operations and order (so given the same gs, bc1, bc2 it gives the same
+ * bits), on host memory, split over n_threads threads in contiguous ranges
+ * of 8-lane AVX2 vectors; the 16-bit outputs are rounded to nearest-even
+ * (F16C for fp16, integer rounding for bf16).  The caller skips the call
+ * for a skipped step.  Host pointers: 4-byte aligned (params 2-byte).  Runs
+ * on the calling thread plus n_threads - 1 workers and returns when done.
+ * Errors: ZF_EINVAL, ZF_EALIGN, ZF_EDTYPE, ZF_EUNSUP (the CPU lacks AVX2 or
+ * F16C). */
+int zf_cpu_adam(const zf_hparams* hp, const zf_cpu_adam_args* args);
+
+typedef struct {
+  int32_t grad_dtype;         /* as zf_step_args */
+  int32_t param_dtype;        /* dtype of the device 16-bit parameters */
+  const void* const* grads;   /* as zf_step_args (ignored with grads_reduced) */
+  float* grad_shards;         /* device Psi' fp32: pass 1 leaves the sums here
+                                 (or they are already reduced) */
+  void* params;               /* device Psi' 16-bit parameters: the upload's
+                                 destination (padded-flat, as zf_shard_step) */
+  int64_t numel;              /* elements of every per-element array, >= Psi' */
+  void* workspace;            /* device workspace, zf_workspace_bytes(plan) */
+  int64_t workspace_size;
+  void* state;                /* device state block */
+  void* h_state;              /* pinned host, zf_state_bytes() */
+  float* h_grad;              /* pinned host Psi' fp32: the sums come down here */
+  float* h_master;            /* host Psi' fp32 state, padded-flat order */
+  float* h_exp_avg;
+  float* h_exp_avg_sq;
+  void* h_params;             /* pinned host Psi' 16-bit staging of the upload */
+  int32_t grads_reduced;      /* as zf_step_args */
+  int32_t n_threads;          /* CPU-Adam threads (<= 0: every hardware thread) */
+  int32_t n_chunks;           /* pipeline chunks, 1 .. 4096 */
+  int32_t reserved;           /* must be 0 */
+  void* const* phase_events;  /* NULL, or 4 hipEvent_t recorded on `stream`:
+                                 before pass 1, after the finish kernel, after
+                                 the last download, after the last upload */
+} zf_offload_args;
+
+/* One ZeRO-Offload step for all N ranks ([L13] 7.1: only the fp16
+ * parameters stay on the GPU; 7.2: gradients down, CPU-Adam, 16-bit
+ * parameters back up in chunks pipelined with the CPU update):
+ *   GPU   pass 1 (reduce-scatter sums into grad_shards, overflow, norm
+ *         partials), norm reduction, finish -- as zf_shard_step;
+ *   PCIe  the state block and the sums, chunk by chunk, into h_state and
+ *         h_grad;
+ *   CPU   unless the step is skipped, zf_cpu_adam chunk by chunk on
+ *         h_master / h_exp_avg / h_exp_avg_sq, writing RNE16 into h_params;
+ *   PCIe  each chunk of h_params into params as soon as it is ready.
+ * Blocks until the step is complete and fills *result (may be NULL).  The
+ * state and parameters equal zf_shard_step's bit for bit.  Errors:
+ * ZF_EINVAL, ZF_EALIGN, ZF_EDTYPE, ZF_ESIZE, ZF_EHIP, ZF_EUNSUP. */
+int zf_offload_step(const zf_plan* plan, const zf_hparams* hp, const zf_offload_args* args,
+                    void* stream, zf_step_result* result);
 
 /* Text for a status code (static storage). */
 const char* zf_strerror(int status);

@@ -251,6 +251,27 @@ def test_step_argument_errors_enqueue_nothing(zf):
     assert acc(1, ok, ok, -1, 0, None) == -1
     assert acc(1, ok, ok, 10, 5, None) == -1
     assert acc(2, ok + 2, ok + 4, 0, 1, None) == 0  # nothing to do: no launch
+    # the offload step
+    def off(**kw):
+        d = dict(grad_dtype=1, param_dtype=1, grads=grads, grad_shards=ok, params=ok, numel=100,
+                 workspace=ok, workspace_size=need, state=ok, h_state=ok, h_grad=ok,
+                 h_master=ok, h_exp_avg=ok, h_exp_avg_sq=ok, h_params=ok, grads_reduced=0,
+                 n_threads=1, n_chunks=2, reserved=0, phase_events=None)
+        d.update(kw)
+        a = Z.OffloadArgs(*[d[f] for f, _ in Z.OffloadArgs._fields_])
+        return Z.lib.zf_offload_step(plan.handle, C.byref(hp), C.byref(a), None, None)
+    assert off(n_chunks=0) == -1
+    assert off(n_chunks=5000) == -1
+    assert off(reserved=2) == -1
+    assert off(param_dtype=3) == -3
+    assert off(h_grad=None) == -1
+    assert off(params=None) == -1
+    assert off(h_master=ok + 4) == -2
+    assert off(params=ok + 2) == -2
+    assert off(numel=99) == -4
+    assert off(workspace_size=need - 1) == -4
+    assert off(grad_dtype=0) == -3
+    assert Z.lib.zf_offload_step(None, C.byref(hp), None, None, None) == -1
     assert Z.lib.zf_state_init(None, 1.0, 0, 10, None) == -1
     assert Z.lib.zf_state_init(ok, 0.0, 0, 10, None) == -1
     assert Z.lib.zf_state_init(ok + 4, 1.0, 0, 10, None) == -2

@@ -203,3 +203,11 @@ def test_llama654m_bucketed_accumulation(R, name):
     dev, trace = run_workload(R, name, rs_check_step=0)
     assert len(dev.plan.groups) == 12
     assert all(t[1] == 0 and abs(t[5] - 3.0) < 0.1 and t[6] < 1.0 for t in trace)
+
+
+def test_llama654m_offload(R):
+    """654M decoder under ZeRO-Offload: the GPU reduces, the fp32 state and
+    CPU-Adam live on the host, bf16 parameters come back in chunks."""
+    dev, trace = run_workload(R, "llama-654m-n2-offload")
+    assert dev.master.device.type == "cpu"
+    assert all(t[1] == 0 and abs(t[5] - 3.0) < 0.1 and t[6] < 1.0 for t in trace)
