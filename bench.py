@@ -314,6 +314,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--offload-chunks", type=int, default=16,
+                    help="pipeline chunks of an offload step")
+    ap.add_argument("--offload-threads", type=int, default=0,
+                    help="CPU-Adam threads of an offload step (0: every hardware thread)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("DIR", "OUT"))
@@ -355,6 +359,7 @@ def main():
     copy_gbs = 2 * COPY_BYTES * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del src, dst
     dev = runner.DeviceRun(w, device="cuda:0", resident_micro=True)
+    dev.n_chunks, dev.n_threads = args.offload_chunks, args.offload_threads
     dev.init_state()
     if w.backward_rs:
         dev.fill_micro(1, w.loss_scale)

@@ -22,12 +22,17 @@ constexpr uint64_t kPlanMagic = 0x7a665f706c616e31ull;  // "zf_plan1"
 //    shared window.  One 2-quad step per thread for N <= 2 (-6% at 4.06B),
 //    two steps otherwise;
 //  - the update pass uses plain loads; two 2-quad steps per thread on large
-//    recomputing plans, one otherwise (within 1% either way).
+//    recomputing plans, one otherwise (within 1% either way);
+//  - the materialised sums go out with non-temporal stores and the update
+//    pass walks its tiles forward: walking them backward so that the newest
+//    sums might still be in the 256 MB Infinity Cache saved 2% of the update
+//    pass only with temporal stores, which cost pass 1 10% (73M, N = 8).
 // Builds may pin a choice for measurement: ZF_FORCE_UNR1, ZF_FORCE_UNR2 (1|2),
 // ZF_FORCE_MAP1 (0|1), ZF_PASS1_NT_LOADS (0|1).
 #ifndef ZF_PASS1_NT_LOADS
 #define ZF_PASS1_NT_LOADS 1
 #endif
+
 constexpr int kThreads = 256;        // 4 wave64 per block
 constexpr int kQuadsPerUnr = 2;      // quads (4 elements) per thread per tile step
 constexpr int64_t kBigPlan = int64_t(1) << 27;  // padded elements
@@ -97,6 +102,9 @@ inline UpdateConsts update_consts(const zf_hparams* hp) {
   c.ef = (float)hp->eps;
   return c;
 }
+
+// The HIP error code behind the calling thread's last ZF_EHIP (0: none).
+extern thread_local int last_hip_error;
 
 // CPU-Adam (host, AVX2): the update pass's element arithmetic over [0, n)
 // with the given step scalars, split over n_threads threads (<= 0: all).

@@ -10,11 +10,15 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
+#include "zf_hip_status.h"
 #include "zf_internal.h"
 
 namespace {
+
+using zf::hip_ok;
 
 constexpr int64_t kChunkAlign = 16;  // chunk starts: whole CPU-Adam vectors
 
@@ -34,6 +38,22 @@ void fill_result(const zf::DevState& h, zf_step_result* out) {
   out->growth_ctr = h.growth_ctr;
   out->bc1 = h.bc1;
   out->bc2 = h.bc2;
+}
+
+// The uploads run on a stream of their own, so that PCIe carries the
+// parameters up while the sums still come down on the caller's stream.  One
+// stream per device, made on first use (default priority, not blocking the
+// legacy stream) and kept until the process ends.
+hipStream_t upload_stream() {
+  static std::mutex mu;
+  static std::vector<hipStream_t> streams;
+  int dev = 0;
+  if (!hip_ok(hipGetDevice(&dev)) || dev < 0) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((size_t)dev >= streams.size()) streams.resize(dev + 1, nullptr);
+  if (!streams[dev] && !hip_ok(hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking)))
+    streams[dev] = nullptr;
+  return streams[dev];
 }
 
 }  // namespace
@@ -77,7 +97,7 @@ extern "C" int zf_offload_step(const zf_plan* plan, const zf_hparams* hp,
   hipStream_t st = static_cast<hipStream_t>(stream);
   auto record = [&](int i) {
     if (!a->phase_events || !a->phase_events[i]) return true;
-    return hipEventRecord(static_cast<hipEvent_t>(a->phase_events[i]), st) == hipSuccess;
+    return hip_ok(hipEventRecord(static_cast<hipEvent_t>(a->phase_events[i]), st));
   };
   int rc = zf::step_enqueue(plan, hp, &s, stream, false);
   if (rc != ZF_OK) return rc;
@@ -93,16 +113,15 @@ extern "C" int zf_offload_step(const zf_plan* plan, const zf_hparams* hp,
     for (hipEvent_t& ev : down)
       if (ev) (void)hipEventDestroy(ev);
   };
-  if (hipMemcpyAsync(a->h_state, a->state, sizeof(zf::DevState), hipMemcpyDeviceToHost, st) !=
-      hipSuccess)
+  if (!hip_ok(hipMemcpyAsync(a->h_state, a->state, sizeof(zf::DevState), hipMemcpyDeviceToHost, st)))
     return ZF_EHIP;
   for (int64_t c = 0; c < C; ++c) {
     int64_t b, e;
     chunk(c, b, e);
-    if (hipEventCreateWithFlags(&down[c], hipEventDisableTiming) != hipSuccess ||
-        hipMemcpyAsync(a->h_grad + b, a->grad_shards + b, (e - b) * sizeof(float),
-                       hipMemcpyDeviceToHost, st) != hipSuccess ||
-        hipEventRecord(down[c], st) != hipSuccess) {
+    if (!hip_ok(hipEventCreateWithFlags(&down[c], hipEventDisableTiming)) ||
+        !hip_ok(hipMemcpyAsync(a->h_grad + b, a->grad_shards + b, (e - b) * sizeof(float),
+                       hipMemcpyDeviceToHost, st)) ||
+        !hip_ok(hipEventRecord(down[c], st))) {
       cleanup();
       return ZF_EHIP;
     }
@@ -112,19 +131,25 @@ extern "C" int zf_offload_step(const zf_plan* plan, const zf_hparams* hp,
     return ZF_EHIP;
   }
   // the state block arrived with the first chunk (same stream, earlier)
-  if (hipEventSynchronize(down[0]) != hipSuccess) {
+  if (!hip_ok(hipEventSynchronize(down[0]))) {
     cleanup();
     return ZF_EHIP;
   }
   zf::DevState h;
   std::memcpy(&h, a->h_state, sizeof(h));
+  // (`st` may be the legacy stream, whose handle is null)
+  hipStream_t up = st;
+  if (!h.skipped && !(up = upload_stream())) {
+    cleanup();
+    return ZF_EHIP;
+  }
   if (!h.skipped) {
     uint16_t* hp16 = static_cast<uint16_t*>(a->h_params);
     char* dp16 = static_cast<char*>(a->params);
     for (int64_t c = 0; c < C; ++c) {
       int64_t b, e;
       chunk(c, b, e);
-      if (hipEventSynchronize(down[c]) != hipSuccess) {
+      if (!hip_ok(hipEventSynchronize(down[c]))) {
         cleanup();
         return ZF_EHIP;
       }
@@ -132,14 +157,17 @@ extern "C" int zf_offload_step(const zf_plan* plan, const zf_hparams* hp,
                        a->h_exp_avg + b, a->h_exp_avg_sq + b, hp16 + b, a->param_dtype,
                        a->n_threads);
       // up: this chunk's 16-bit parameters while the CPU takes the next one
-      if (hipMemcpyAsync(dp16 + 2 * b, hp16 + b, (e - b) * sizeof(uint16_t),
-                         hipMemcpyHostToDevice, st) != hipSuccess) {
+      if (!hip_ok(hipMemcpyAsync(dp16 + 2 * b, hp16 + b, (e - b) * sizeof(uint16_t),
+                         hipMemcpyHostToDevice, up))) {
         cleanup();
+        (void)hipStreamSynchronize(up);
         return ZF_EHIP;
       }
     }
   }
-  const bool ok = record(3) && hipStreamSynchronize(st) == hipSuccess;
+  // every upload has landed before the caller's stream goes on
+  const bool ok = hip_ok(hipStreamSynchronize(up)) && record(3) &&
+                  hip_ok(hipStreamSynchronize(st));
   cleanup();
   if (!ok) return ZF_EHIP;
   fill_result(h, result);

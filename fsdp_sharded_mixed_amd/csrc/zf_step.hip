@@ -28,9 +28,12 @@
 
 #include <cstdint>
 
+#include "zf_hip_status.h"
 #include "zf_internal.h"
 
 namespace {
+
+using zf::hip_ok;
 
 using zf::kThreads;
 
@@ -760,7 +763,7 @@ int launch_pass1(const zf_plan* plan, int32_t dt, hipStream_t s, const Pass1Args
   const int nr = plan->summary.n_ranks;
   if (plan->unr1 == 2) launch_pass1_u<MAT, NORM, 2>(nr, dt, grid, s, a);
   else launch_pass1_u<MAT, NORM, 1>(nr, dt, grid, s, a);
-  return hipGetLastError() == hipSuccess ? ZF_OK : ZF_EHIP;
+  return hip_ok(hipGetLastError()) ? ZF_OK : ZF_EHIP;
 }
 
 template <int GDT, int PDT, int U, bool OUT16>
@@ -809,7 +812,7 @@ int launch_pass2(const zf_plan* plan, int32_t gdt, int32_t pdt, bool mat, bool o
   const int nr = plan->summary.n_ranks;
   if (plan->unr2 == 2) launch_pass2_u<2>(nr, gdt, pdt, mat, out16, grid, s, a);
   else launch_pass2_u<1>(nr, gdt, pdt, mat, out16, grid, s, a);
-  return hipGetLastError() == hipSuccess ? ZF_OK : ZF_EHIP;
+  return hip_ok(hipGetLastError()) ? ZF_OK : ZF_EHIP;
 }
 
 template <bool ACC, int Q>
@@ -839,10 +842,16 @@ void launch_bucket_nr(int nr, int32_t dt, dim3 grid, hipStream_t s, const Bucket
 
 int record(void* const* ev, int i, hipStream_t s) {
   if (!ev || !ev[i]) return ZF_OK;
-  return hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) == hipSuccess ? ZF_OK : ZF_EHIP;
+  return hip_ok(hipEventRecord(static_cast<hipEvent_t>(ev[i]), s)) ? ZF_OK : ZF_EHIP;
 }
 
 }  // namespace
+
+thread_local int zf::last_hip_error = 0;
+
+extern "C" const char* zf_hip_error_name(void) {
+  return hipGetErrorName(static_cast<hipError_t>(zf::last_hip_error));
+}
 
 extern "C" int64_t zf_state_bytes(void) { return kStateBytes; }
 
@@ -854,7 +863,7 @@ extern "C" int zf_state_init(void* d_state, double loss_scale, int32_t dynamic,
   hipLaunchKernelGGL(zf_state_init_kernel, dim3(1), dim3(64), 0,
                      static_cast<hipStream_t>(stream), static_cast<DevState*>(d_state),
                      loss_scale, dynamic, growth_interval);
-  return hipGetLastError() == hipSuccess ? ZF_OK : ZF_EHIP;
+  return hip_ok(hipGetLastError()) ? ZF_OK : ZF_EHIP;
 }
 
 int zf::step_enqueue(const zf_plan* plan, const zf_hparams* hp, const zf_step_args* args,
@@ -917,7 +926,7 @@ int zf::step_enqueue(const zf_plan* plan, const zf_hparams* hp, const zf_step_ar
       hipLaunchKernelGGL(zf_pass1_reduced<zf::kQuadsPerUnr * 2>, grid, dim3(kThreads), 0, s, a1);
     else
       hipLaunchKernelGGL(zf_pass1_reduced<zf::kQuadsPerUnr>, grid, dim3(kThreads), 0, s, a1);
-    rc = hipGetLastError() == hipSuccess ? ZF_OK : ZF_EHIP;
+    rc = hip_ok(hipGetLastError()) ? ZF_OK : ZF_EHIP;
   } else {
     rc = mat ? launch_pass1<true, true>(plan, args->grad_dtype, s, a1)
              : launch_pass1<false, true>(plan, args->grad_dtype, s, a1);
@@ -931,7 +940,7 @@ int zf::step_enqueue(const zf_plan* plan, const zf_hparams* hp, const zf_step_ar
   a2l.out = partials2;
   a2l.n_in = plan->pass1_tiles;
   hipLaunchKernelGGL(zf_level2, dim3((uint32_t)plan->level2_blocks), dim3(kThreads), 0, s, a2l);
-  if (hipGetLastError() != hipSuccess) return ZF_EHIP;
+  if (!hip_ok(hipGetLastError())) return ZF_EHIP;
 
   FinishArgs af;
   af.partials = partials2;
@@ -942,7 +951,7 @@ int zf::step_enqueue(const zf_plan* plan, const zf_hparams* hp, const zf_step_ar
   af.np = plan->level2_blocks;
   af.n_ranks = nr;
   hipLaunchKernelGGL(zf_finish, dim3(1), dim3(kThreads), 0, s, af);
-  if (hipGetLastError() != hipSuccess) return ZF_EHIP;
+  if (!hip_ok(hipGetLastError())) return ZF_EHIP;
   if ((rc = record(args->phase_events, 2, s)) != ZF_OK) return rc;
   if (!update) return ZF_OK;
 
@@ -1044,7 +1053,7 @@ extern "C" int zf_bucket_reduce_scatter(const zf_plan* plan, int64_t group, int3
   (void)hipGetLastError();
   if (accumulate) launch_bucket_nr<true, Q>(nr, grad_dtype, dim3((uint32_t)bx), s, a);
   else launch_bucket_nr<false, Q>(nr, grad_dtype, dim3((uint32_t)bx), s, a);
-  return hipGetLastError() == hipSuccess ? ZF_OK : ZF_EHIP;
+  return hip_ok(hipGetLastError()) ? ZF_OK : ZF_EHIP;
 }
 
 extern "C" int zf_accumulate(int32_t grad_dtype, const void* grad, float* acc, int64_t n,
@@ -1083,7 +1092,7 @@ extern "C" int zf_accumulate(int32_t grad_dtype, const void* grad, float* acc, i
     if (accumulate) hipLaunchKernelGGL((zf_accumulate_kernel<ZF_F16, true>), grid, dim3(kThreads), 0, s, a);
     else hipLaunchKernelGGL((zf_accumulate_kernel<ZF_F16, false>), grid, dim3(kThreads), 0, s, a);
   }
-  return hipGetLastError() == hipSuccess ? ZF_OK : ZF_EHIP;
+  return hip_ok(hipGetLastError()) ? ZF_OK : ZF_EHIP;
 }
 
 extern "C" int zf_gather(const zf_plan* plan, int64_t unit, int32_t dtype,
@@ -1110,7 +1119,7 @@ extern "C" int zf_gather(const zf_plan* plan, int64_t unit, int32_t dtype,
   (void)hipGetLastError();
   hipLaunchKernelGGL(zf_gather_kernel, dim3((uint32_t)bx, (uint32_t)nr), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), a);
-  return hipGetLastError() == hipSuccess ? ZF_OK : ZF_EHIP;
+  return hip_ok(hipGetLastError()) ? ZF_OK : ZF_EHIP;
 }
 
 extern "C" int zf_gather_cast(const zf_plan* plan, int64_t group, int32_t dtype,
@@ -1145,7 +1154,7 @@ extern "C" int zf_gather_cast(const zf_plan* plan, int64_t group, int32_t dtype,
       hipLaunchKernelGGL(zf_gather_cast_kernel<ZF_BF16>, grid, dim3(kThreads), 0, s, a);
     else
       hipLaunchKernelGGL(zf_gather_cast_kernel<ZF_F16>, grid, dim3(kThreads), 0, s, a);
-    if (hipGetLastError() != hipSuccess) return ZF_EHIP;
+    if (!hip_ok(hipGetLastError())) return ZF_EHIP;
   }
   return ZF_OK;
 }
@@ -1154,9 +1163,9 @@ extern "C" int zf_read_result(const void* d_state, zf_step_result* out, void* st
   if (!d_state || !out) return ZF_EINVAL;
   DevState h;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (hipMemcpyAsync(&h, d_state, sizeof(h), hipMemcpyDeviceToHost, s) != hipSuccess)
+  if (!hip_ok(hipMemcpyAsync(&h, d_state, sizeof(h), hipMemcpyDeviceToHost, s)))
     return ZF_EHIP;
-  if (hipStreamSynchronize(s) != hipSuccess) return ZF_EHIP;
+  if (!hip_ok(hipStreamSynchronize(s))) return ZF_EHIP;
   out->overflow = h.overflow;
   out->skipped = h.skipped;
   out->t = h.t;

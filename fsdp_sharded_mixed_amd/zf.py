@@ -23,7 +23,10 @@ STATUS = {0: "ZF_OK", -1: "ZF_EINVAL", -2: "ZF_EALIGN", -3: "ZF_EDTYPE", -4: "ZF
 class ZfError(RuntimeError):
     def __init__(self, status, where):
         self.status = status
-        super().__init__(f"{where}: {STATUS.get(status, status)} ({strerror(status)})")
+        detail = strerror(status)
+        if status == -5:
+            detail += ": " + lib.zf_hip_error_name().decode()
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({detail})")
 
 
 class Segment(C.Structure):
@@ -122,6 +125,7 @@ _SIGNATURES = {
     "zf_offload_step": (C.c_int, [C.c_void_p, C.POINTER(Hparams), C.POINTER(OffloadArgs),
                                   C.c_void_p, C.POINTER(StepResult)]),
     "zf_strerror": (C.c_char_p, [C.c_int]),
+    "zf_hip_error_name": (C.c_char_p, []),
 }
 
 

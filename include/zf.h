@@ -344,6 +344,10 @@ typedef struct {
   float bc1, bc2;       /* binary32 bias corrections 1 - beta^t of the update */
 } zf_step_result;
 
+/* Name of the HIP runtime error behind the calling thread's last ZF_EHIP
+ * ("hipSuccess" if there was none).  The string is static. */
+const char* zf_hip_error_name(void);
+
 /* Copy the last step's result from a device state block to the host.
  * Synchronises `stream`.  Errors: ZF_EINVAL, ZF_EHIP. */
 int zf_read_result(const void* d_state, zf_step_result* out, void* stream);
@@ -416,8 +420,11 @@ typedef struct {
  *   CPU   unless the step is skipped, zf_cpu_adam chunk by chunk on
  *         h_master / h_exp_avg / h_exp_avg_sq, writing RNE16 into h_params;
  *   PCIe  each chunk of h_params into params as soon as it is ready.
- * Blocks until the step is complete and fills *result (may be NULL).  The
- * state and parameters equal zf_shard_step's bit for bit.  Errors:
+ * The uploads run on a library-owned stream per device (created on first
+ * use, kept until the process ends), so both PCIe directions are busy at
+ * once.  Blocks until the step is complete and fills *result (may be
+ * NULL).  The state and parameters equal zf_shard_step's bit for bit.
+ * Calls that overlap on one device must not share host buffers.  Errors:
  * ZF_EINVAL, ZF_EALIGN, ZF_EDTYPE, ZF_ESIZE, ZF_EHIP, ZF_EUNSUP. */
 int zf_offload_step(const zf_plan* plan, const zf_hparams* hp, const zf_offload_args* args,
                     void* stream, zf_step_result* result);
