@@ -113,6 +113,44 @@ def traffic_for(workload, kernel="zf_pass2", per="launch"):
     return d[kernel]["hbm_bytes_per_" + per]
 
 
+def counted_bytes_per_step(w):
+    """HBM bytes per step of every kernel of the step, from the committed
+    counter summary of these kernel sources, or None."""
+    path = os.path.join(PROFILES, f"zf_step_{w.name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return sum(v["hbm_bytes_per_step"] for v in d.values()
+               if isinstance(v, dict) and "hbm_bytes_per_step" in v)
+
+
+def skipped_step_ms(w, dev, one_step, reps=3):
+    """Median time of a step whose gradients hold a +inf (the step is
+    skipped: pass 1, the reduction and the finish run, the update exits).
+    Runs after the timed region; the state is left as it was except the
+    dynamic loss scale, which halves per skipped step."""
+    import torch
+    grads = dev.micro_grads[0][0]
+    p = dev.plan.units[0].O  # a real element of the first unit
+    keep = grads[p].clone()
+    grads[p] = float("inf")
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        one_step()
+        e1.record()
+        torch.cuda.synchronize()
+        assert dev.result().skipped == 1
+        times.append(e0.elapsed_time(e1))
+    grads[p] = keep
+    torch.cuda.synchronize()
+    return round(sorted(times)[len(times) // 2], 5)
+
+
 def backward_traffic(w):
     """Measured HBM bytes of one step's backward-side launches, or None."""
     parts = [traffic_for(w.name, k, "step") for k in
@@ -204,6 +242,29 @@ def summarize_pmc(fetch_dir, write_dir, workload, out, commands):
     print(json.dumps(res, indent=1))
 
 
+def host_info():
+    """CPU model, logical CPUs and RAM of the host the oracle ran on."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    ram = None
+    try:
+        with open("/proc/meminfo") as f:
+            for ln in f:
+                if ln.startswith("MemTotal"):
+                    ram = round(int(ln.split()[1]) / 2 ** 20, 1)
+                    break
+    except OSError:
+        pass
+    return {"cpu": model, "cpus": os.cpu_count(), "ram_gib": ram}
+
+
 def cpu_baseline(w, min_seconds=10.0, max_steps=40):
     """The CPU oracle as it stands, single thread, on a slice of the workload:
     its first segments up to ~19M parameters (for the Llama workloads: the
@@ -228,13 +289,24 @@ def cpu_baseline(w, min_seconds=10.0, max_steps=40):
                  for a in range(ws.n_micro)]
     else:
         grads = OI.replicas(ws, units, psi_pad, 1, ws.loss_scale)
-    steps, t0 = 0, time.perf_counter()
-    while steps < max_steps and (time.perf_counter() - t0) < min_seconds:
-        run.step(grads)
-        steps += 1
-    dt = time.perf_counter() - t0
+    # one core, as the oracle is single-threaded by design
+    try:
+        saved = os.sched_getaffinity(0)
+        os.sched_setaffinity(0, {min(saved)})
+    except (AttributeError, OSError):
+        saved = None
+    try:
+        steps, t0 = 0, time.perf_counter()
+        while steps < max_steps and (time.perf_counter() - t0) < min_seconds:
+            run.step(grads)
+            steps += 1
+        dt = time.perf_counter() - t0
+    finally:
+        if saved is not None:
+            os.sched_setaffinity(0, saved)
     gbs = algorithmic_bytes_per_param(ws) * psi * steps / dt / 1e9
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "host": host_info(),
             "params_per_s": round(psi * steps / dt, 1),
             "sample": f"first {len(segs)} parameter tensors ({psi:,} params) of {w.name}, "
                       f"N={ws.n_ranks}, {steps} steps over one batch"
@@ -404,16 +476,18 @@ def main():
 
     # per-kernel durations: a second run of K steps with HIP events recorded
     # by the library between its kernels, on the step's stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     for row in evs:
         for e in row:
             e.record()
     torch.cuda.synchronize()
     for row in evs:
-        one_step(phase_events=[e.cuda_event for e in row[1:]], backward_event=row[0])
+        one_step(phase_events=[e.cuda_event for e in row[1:5]], backward_event=row[0])
+        row[5].record()  # after the unit gathers
     torch.cuda.synchronize()
+    per_step = sorted((r[0] if w.backward_rs else r[1]).elapsed_time(r[5]) for r in evs)
     evs_b = [r[0] for r in evs]
-    evs = [r[1:] for r in evs]
+    evs = [r[1:5] for r in evs]
     bw = (sum(b.elapsed_time(r[0]) for b, r in zip(evs_b, evs)) / args.steps
           if w.backward_rs else 0.0)
     p1 = sum(r[0].elapsed_time(r[1]) for r in evs) / args.steps
@@ -477,13 +551,26 @@ def main():
         "kernels_ms": kernels,
         "roofline": roof,
     }
+    line["ms_per_step_median"] = round(per_step[len(per_step) // 2], 5)
+    line["ms_per_step_min"] = round(per_step[0], 5)
+    counted = counted_bytes_per_step(w)
+    if counted is not None:
+        # HBM bytes the counters saw per step (committed summaries of these
+        # kernel sources) over the step time
+        cg = counted / (ms * 1e-3) / 1e9
+        line["hbm_gbs_counted"] = round(cg, 2)
+        line["pct_hbm_peak_counted"] = round(100 * cg / PEAK_HBM_GBS, 2)
+        line["pct_device_copy_counted"] = round(100 * cg / copy_gbs, 2)
+    line["skipped_step_ms"] = skipped_step_ms(w, dev, one_step)
     if w.backward_rs:
         line["config"]["micro_batches"] = w.n_micro
         line["config"]["accumulation"] = ["reduce-scatter every micro-batch",
                                           "no_sync fp32 local, one reduce-scatter"][w.accum_mode]
         line["config"]["buckets"] = s.n_groups
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w)
+        cb = cpu_baseline(w)
+        cb["gpu_over_oracle"] = round(line["value"] / cb["value"], 1)
+        line["cpu_baseline"] = cb
     print(json.dumps(line), flush=True)
 
 

@@ -870,3 +870,28 @@ def test_regen_accum_matches_direct(orc, mode):
     one = O.regen_accum_acc(w.grad_dtype, n, 1, mode, w.seed, 2, w.sigma, w.loss_scale, idx)
     assert np.array_equal(one, O.regen_acc(w.grad_dtype, n, w.seed, 2, w.sigma, w.loss_scale,
                                            idx))
+
+
+def test_clipped_gradient_norm(orc):
+    """[L13] via torchtitan's clip ([MDT] 五.7): when the norm exceeds
+    max_norm, the gradient the update sees, g = acc * gs, has L2 norm
+    max_norm * norm / (norm + 1e-6), to within binary32 rounding of gs
+    (relative 1e-6); and with clipping off (max_norm <= 0) the factor is the
+    plain unscale-and-average 1/(S*N)."""
+    for n, gdt in ((4, W.F16), (8, W.BF16), (3, W.BF16)):
+        w = _small_workload(n, W.PER_UNIT, grad_dtype=gdt, lens=(4001, 37, 999),
+                            dynamic=(gdt == W.F16), scale=1024.0 if gdt == W.F16 else 1.0,
+                            sigma=0.05, max_norm=0.25)
+        units, psi, psi_pad = OI.plan(w)
+        grads = OI.replicas(w, units, psi_pad, 1, w.loss_scale)
+        acc = np.concatenate(O.reduce_scatter(w.grad_dtype, n, units, grads))
+        ss = float(np.sum(acc.astype(np.float64) ** 2))
+        sc, res = O.finish(ss, 0, n, OI.hparams(w), OI.scale_state(w))
+        assert res.norm > w.max_norm and res.coef < 1.0
+        g = (acc * np.float32(sc.gs)).astype(np.float64)
+        want = w.max_norm * res.norm / (res.norm + 1e-6)
+        assert abs(math.sqrt(float(np.sum(g * g))) - want) <= 1e-6 * want
+        hp = OI.hparams(w)
+        hp.max_norm = 0.0
+        sc0, res0 = O.finish(ss, 0, n, hp, OI.scale_state(w))
+        assert res0.coef == 1.0 and sc0.gs == np.float32(1.0 / (w.loss_scale * n))
