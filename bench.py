@@ -242,6 +242,34 @@ def summarize_pmc(fetch_dir, write_dir, workload, out, commands):
     print(json.dumps(res, indent=1))
 
 
+PROBE_FLOATS = 1 << 28  # 1 GiB per array
+
+
+def stream_probes(reps=10):
+    """GB/s of the box for streams in the step kernels' access pattern
+    (zfi_stream_probe): a copy (1 read, 1 write), the update pass's mix of
+    4 reads and 4 writes, and 8 reads + 1 write (pass 1 at N = 8)."""
+    import torch
+    from fsdp_sharded_mixed_amd import inputs as I
+    bufs = [torch.ones(PROBE_FLOATS, dtype=torch.float32, device="cuda:0") for _ in range(9)]
+    out = {}
+    for name, r, wr in (("1r1w", 1, 1), ("4r4w", 4, 4), ("8r1w", 8, 1)):
+        src, dst = bufs[:r], bufs[r:r + wr]
+        for _ in range(3):
+            I.stream_probe(src, dst)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            I.stream_probe(src, dst)
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = round((r + wr) * 4 * PROBE_FLOATS * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9,
+                          1)
+    del bufs
+    torch.cuda.empty_cache()
+    return out
+
+
 def host_info():
     """CPU model, logical CPUs and RAM of the host the oracle ran on."""
     model = ""
@@ -430,6 +458,7 @@ def main():
     torch.cuda.synchronize()
     copy_gbs = 2 * COPY_BYTES * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del src, dst
+    probe = stream_probes()
     dev = runner.DeviceRun(w, device="cuda:0", resident_micro=True)
     dev.n_chunks, dev.n_threads = args.offload_chunks, args.offload_threads
     dev.init_state()
@@ -469,6 +498,7 @@ def main():
 
     if w.offload:
         line = offload_line(args, w, dev, ms, wall, copy_gbs)
+        line["stream_probe_gbs"] = probe
         if not args.no_cpu_baseline:
             line["cpu_baseline"] = cpu_baseline(w)
         print(json.dumps(line), flush=True)
@@ -551,6 +581,9 @@ def main():
         "kernels_ms": kernels,
         "roofline": roof,
     }
+    line["stream_probe_gbs"] = probe
+    if roof["kernel"].startswith("zf_pass2"):
+        roof["frac_of_4r4w_probe"] = round(roof["achieved"] / probe["4r4w"], 4)
     line["ms_per_step_median"] = round(per_step[len(per_step) // 2], 5)
     line["ms_per_step_min"] = round(per_step[0], 5)
     counted = counted_bytes_per_step(w)

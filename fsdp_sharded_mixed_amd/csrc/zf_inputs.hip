@@ -93,3 +93,85 @@ extern "C" int zfi_fill_normal32(float* dst, int64_t n, uint64_t seed, uint64_t 
 extern "C" uint64_t zfi_stream_output(uint64_t seed, uint64_t stream, uint64_t j) {
   return mix64(stream_state(seed, stream) + (j + 1ull) * kGamma);
 }
+
+// ---------------------------------------------------------------------------
+// Bandwidth probe.
+namespace {
+
+typedef float f32x4p __attribute__((ext_vector_type(4)));
+
+struct ProbeArgs {
+  const float* src[8];
+  float* dst[8];
+  int64_t nq;
+};
+
+template <int R, int W>
+__global__ __launch_bounds__(256) void stream_probe(ProbeArgs a) {
+  constexpr int Q = 2;
+  const int64_t q0 = (int64_t)blockIdx.x * 256 * Q + threadIdx.x;
+  f32x4p x[Q];
+#pragma unroll
+  for (int h = 0; h < Q; ++h) {
+    const int64_t q = q0 + (int64_t)h * 256;
+    f32x4p t = {0, 0, 0, 0};
+    if (q < a.nq) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) t = t + reinterpret_cast<const f32x4p*>(a.src[r])[q];
+    }
+    x[h] = t;
+  }
+#pragma unroll
+  for (int h = 0; h < Q; ++h) {
+    const int64_t q = q0 + (int64_t)h * 256;
+    if (q >= a.nq) continue;
+#pragma unroll
+    for (int k = 0; k < W; ++k)
+      __builtin_nontemporal_store(x[h], reinterpret_cast<f32x4p*>(a.dst[k]) + q);
+  }
+}
+
+template <int R>
+void launch_probe_w(int w, dim3 g, hipStream_t s, const ProbeArgs& a) {
+  switch (w) {
+    case 1: hipLaunchKernelGGL((stream_probe<R, 1>), g, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((stream_probe<R, 2>), g, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((stream_probe<R, 4>), g, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((stream_probe<R, 8>), g, dim3(256), 0, s, a); break;
+  }
+}
+
+}  // namespace
+
+extern "C" int zfi_stream_probe(const float* const* src, int32_t n_src, float* const* dst,
+                                int32_t n_dst, int64_t n, void* stream_handle) {
+  if (!src || !dst || n <= 0 || n % 4 != 0) return -1;
+  if (!(n_src == 1 || n_src == 2 || n_src == 4 || n_src == 8)) return -1;
+  if (!(n_dst == 1 || n_dst == 2 || n_dst == 4 || n_dst == 8)) return -1;
+  ProbeArgs a;
+  for (int k = 0; k < 8; ++k) {
+    a.src[k] = nullptr;
+    a.dst[k] = nullptr;
+  }
+  for (int k = 0; k < n_src; ++k) {
+    if (!src[k] || (reinterpret_cast<uintptr_t>(src[k]) & 15u)) return -1;
+    a.src[k] = src[k];
+  }
+  for (int k = 0; k < n_dst; ++k) {
+    if (!dst[k] || (reinterpret_cast<uintptr_t>(dst[k]) & 15u)) return -1;
+    a.dst[k] = dst[k];
+  }
+  a.nq = n / 4;
+  const int64_t blocks = (a.nq + 511) / 512;
+  if (blocks > 0x7FFFFFFF) return -1;
+  const dim3 g((uint32_t)blocks);
+  hipStream_t s = static_cast<hipStream_t>(stream_handle);
+  (void)hipGetLastError();
+  switch (n_src) {
+    case 1: launch_probe_w<1>(n_dst, g, s, a); break;
+    case 2: launch_probe_w<2>(n_dst, g, s, a); break;
+    case 4: launch_probe_w<4>(n_dst, g, s, a); break;
+    default: launch_probe_w<8>(n_dst, g, s, a); break;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}

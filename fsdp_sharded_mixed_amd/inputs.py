@@ -23,6 +23,9 @@ def _load():
     lib.zfi_fill_normal32.restype = C.c_int
     lib.zfi_fill_normal32.argtypes = [C.c_void_p, C.c_int64, C.c_uint64, C.c_uint64, C.c_int64,
                                       C.c_double, C.c_void_p]
+    lib.zfi_stream_probe.restype = C.c_int
+    lib.zfi_stream_probe.argtypes = [C.POINTER(C.c_void_p), C.c_int32, C.POINTER(C.c_void_p),
+                                     C.c_int32, C.c_int64, C.c_void_p]
     lib.zfi_stream_output.restype = C.c_uint64
     lib.zfi_stream_output.argtypes = [C.c_uint64, C.c_uint64, C.c_uint64]
     return lib
@@ -64,3 +67,13 @@ def inject_index(w, psi):
     """Logical index that receives a workload's injected +inf: output 0 of
     the inject stream, modulo Psi."""
     return stream_output(w.seed, W.STREAM_INJECT, 0) % psi
+
+
+def stream_probe(srcs, dsts, n=None, stream=None):
+    """zfi_stream_probe: dst[k] = sum of srcs, with the step's access pattern."""
+    n = min(t.numel() for t in list(srcs) + list(dsts)) if n is None else n
+    sp = (C.c_void_p * len(srcs))(*[t.data_ptr() for t in srcs])
+    dp = (C.c_void_p * len(dsts))(*[t.data_ptr() for t in dsts])
+    rc = lib.zfi_stream_probe(sp, len(srcs), dp, len(dsts), int(n), _stream(stream))
+    if rc != 0:
+        raise RuntimeError(f"zfi_stream_probe failed ({rc})")

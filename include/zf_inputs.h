@@ -40,6 +40,17 @@ int zfi_fill_normal32(float* dst, int64_t n, uint64_t seed, uint64_t stream,
 /* Output j of `stream`'s splitmix64 generator (host computation). */
 uint64_t zfi_stream_output(uint64_t seed, uint64_t stream, uint64_t j);
 
+/* Bandwidth probe for the bench (no arithmetic of the step): dst[k][i] =
+ * src[0][i] + ... + src[n_src-1][i] for every destination k < n_dst and
+ * i < n, in the access pattern of the step's kernels (16-byte loads and
+ * non-temporal 16-byte stores per lane, 4-element quads 256 apart per lane,
+ * one tile of 512 quads per block), so that a plain copy (1 source, 1
+ * destination) and the update pass's mix (4 and 4) can be timed on the
+ * box that runs the step.  n_src and n_dst in 1..8; every pointer 16-byte
+ * aligned; n a multiple of 4.  Returns 0, -1 (bad argument) or -5. */
+int zfi_stream_probe(const float* const* src, int32_t n_src, float* const* dst, int32_t n_dst,
+                     int64_t n, void* stream_handle);
+
 #ifdef __cplusplus
 }
 #endif

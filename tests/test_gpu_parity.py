@@ -333,3 +333,20 @@ def test_phase_events_and_no_sync(R):
     t = [evs[0].elapsed_time(evs[i]) for i in (1, 2, 3)]
     assert 0 <= t[0] <= t[1] <= t[2]
     assert dev.result().t == 1
+
+
+def test_stream_probe_sums(R):
+    """The bench's bandwidth probe computes what it claims (dst = sum of the
+    sources), so its timing measures real loads and stores."""
+    from fsdp_sharded_mixed_amd import inputs as I
+    g = torch.Generator(device="cpu").manual_seed(3)
+    for r, wr in ((1, 1), (4, 4), (8, 1), (2, 2)):
+        n = 4 * 5000
+        src = [torch.randn(n, generator=g).cuda() for _ in range(r)]
+        dst = [torch.zeros(n, device="cuda") for _ in range(wr)]
+        I.stream_probe(src, dst)
+        want = src[0].clone()
+        for t in src[1:]:
+            want = want + t
+        for d in dst:
+            assert torch.equal(d, want)
