@@ -104,6 +104,7 @@ def lib():
                                           C.POINTER(Result)]),
             "or_rs_accumulate": (C.c_int, [i32, i32, vp, i64, i64, vp, vp, i32]),
             "or_local_accumulate": (C.c_int, [i32, i64, vp, vp, i32]),
+            "or_reshard": (C.c_int, [vp, i64, i32, vp, vp, i64, i32, vp, i32]),
             "or_bucket_assign": (C.c_int, [vp, i64, i32, i64, vp, C.POINTER(i64)]),
             "or_regen_accum_sumsq": (C.c_int, [i32, i32, i32, i32, u64, i64, dbl, dbl, i64, i64,
                                                C.POINTER(Inject), C.POINTER(dbl),
@@ -312,6 +313,22 @@ def local_accumulate(grad_dtype, grad, acc, accumulate):
     assert acc.dtype == np.float32 and acc.flags.c_contiguous and acc.size == grad.size
     _check(lib().or_local_accumulate(grad_dtype, grad.size, _p(grad), _p(acc), int(accumulate)),
            "local_accumulate")
+
+
+def reshard(units_a, n_a, shards_a, units_b, n_b):
+    """Rank shard buffers under layout A -> new ones under layout B (same
+    dtype), by logical index; B's padding is zero."""
+    ua = np.ascontiguousarray(units_a, UNIT_DTYPE)
+    ub = np.ascontiguousarray(units_b, UNIT_DTYPE)
+    shards_a = [np.ascontiguousarray(x) for x in shards_a]
+    dt = shards_a[0].dtype
+    s_tot = int(ub["S"].sum())
+    out = [np.empty(s_tot, dt) for _ in range(n_b)]
+    for x in out:  # every byte set, so that padding left unwritten shows
+        x.view(np.uint8)[:] = 0xFF
+    _check(lib().or_reshard(_p(ua), len(ua), n_a, _ptrs(shards_a), _p(ub), len(ub), n_b,
+                            _ptrs(out), dt.itemsize), "reshard")
+    return out
 
 
 def bucket_assign(numel, n_ranks, bucket_numel=0):

@@ -674,6 +674,53 @@ int or_fsdp2_gather(const or_unit* units, int64_t n_units, int32_t n_ranks, int6
   return 0;
 }
 
+/* Resharding by logical index ([F5]: when the DP size changes between save
+ * and load, the shard offsets lose their meaning and the state has to be
+ * redistributed for the new parallelism; [MDT] 六.4: DeepSpeed converts its
+ * per-rank ZeRO checkpoints to a universal one, torchtitan's DCP reshards
+ * natively).  Every real element keeps its value
+ * and moves from its place under layout A (N_a ranks) to its place under
+ * layout B (N_b ranks); every padding element of B is zero.  Rank r's real
+ * part of unit u is the logical run [lam_u + r*S_u, lam_u + r*S_u +
+ * clamp(L_u - r*S_u, 0, S_u)) in every layout, so the element is found by
+ * walking both layouts' (unit, rank) runs in logical order.  elem_bytes is
+ * 2 or 4; a[r] / b[r] are the ranks' shard buffers (unit u at M_u). */
+int or_reshard(const or_unit* ua, int64_t nua, int32_t na, const void* const* a,
+               const or_unit* ub, int64_t nub, int32_t nb, void* const* b, int32_t elem_bytes) {
+  int64_t psi_a = 0, psi_b = 0, u, i;
+  int32_t r;
+  char* logical;
+  if (!ua || !ub || !a || !b || na < 1 || nb < 1 || (elem_bytes != 2 && elem_bytes != 4))
+    return -1;
+  for (u = 0; u < nua; ++u) psi_a += ua[u].L;
+  for (u = 0; u < nub; ++u) psi_b += ub[u].L;
+  if (psi_a != psi_b) return -1;
+  logical = (char*)malloc((size_t)(psi_a > 0 ? psi_a : 1) * (size_t)elem_bytes);
+  if (!logical) return -2;
+  /* A's runs into logical order */
+  for (u = 0; u < nua; ++u)
+    for (r = 0; r < na; ++r)
+      for (i = 0; i < ua[u].S; ++i) {
+        int64_t e = (int64_t)r * ua[u].S + i;
+        if (e >= ua[u].L) break;
+        memcpy(logical + (ua[u].lam + e) * elem_bytes,
+               (const char*)a[r] + (ua[u].M + i) * elem_bytes, (size_t)elem_bytes);
+      }
+  /* logical order into B's runs, zeros in B's padding */
+  for (u = 0; u < nub; ++u)
+    for (r = 0; r < nb; ++r)
+      for (i = 0; i < ub[u].S; ++i) {
+        int64_t e = (int64_t)r * ub[u].S + i;
+        char* dst = (char*)b[r] + (ub[u].M + i) * elem_bytes;
+        if (e < ub[u].L)
+          memcpy(dst, logical + (ub[u].lam + e) * elem_bytes, (size_t)elem_bytes);
+        else
+          memset(dst, 0, (size_t)elem_bytes);
+      }
+  free(logical);
+  return 0;
+}
+
 /* Plain data-parallel reference on one unpadded buffer of Psi elements: the
  * same N replicas are summed in the same rank order, and the whole array is
  * updated at once.  ZeRO-1/2 must reproduce it bit for bit ([L13] 3.4: the

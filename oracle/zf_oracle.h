@@ -17,6 +17,8 @@
  *         3.4 (bit-exactness conditions), 3.5 (memory), 3.6 (padding),
  *         4.1-4.2 (communication volume), 5.2 (FlatParameter), 5.6 (the two
  *         gradient-accumulation schemes), exercises 1-5.
+ *  [F5]   Femtotron dev log #5 (Data Parallelism): gradient accumulation with
+ *         no_sync, resharding when the DP size changes.
  *  [F6]   Femtotron dev log #6 (ZeRO-1 and ZeRO-2): the master as one 1-D vector.
  *  [F7]   Femtotron dev log #7 (ZeRO-3): the ZeRO-2 gradient hook (pad, then
  *         reduce-scatter with AVG), ZeRO-3 is not bit-exact (reduction tree).
@@ -27,7 +29,8 @@
  *         fp32 shard is the parameter, cast at all-gather time, fp32
  *         reduce-scatter), 六.2 (Stage 3 vs FSDP1 vs FSDP2), 三.3 (Megatron
  *         gradient buckets, fp32 gradient accumulation) and 五.7
- *         (gradient-norm clipping and accumulation on the shard).
+ *         (gradient-norm clipping and accumulation on the shard), 六.4
+ *         (checkpoint formats and resharding).
  *
  * Where the pages leave a step open, the reading taken is stated at the
  * function that takes it.  Parity status: every function is pinned by a
@@ -140,6 +143,8 @@ int or_fsdp2_step(int32_t grad_dtype, int32_t n_ranks, const or_unit* units, int
                   or_scale_state* st, or_result* res);
 int or_fsdp2_gather(const or_unit* units, int64_t n_units, int32_t n_ranks, int64_t first,
                     int64_t count, int32_t dtype, const float* const* master, uint16_t* out);
+int or_reshard(const or_unit* ua, int64_t nua, int32_t na, const void* const* a,
+               const or_unit* ub, int64_t nub, int32_t nb, void* const* b, int32_t elem_bytes);
 int or_dp_step(int32_t grad_dtype, int32_t param_dtype, int32_t n_ranks, int64_t psi,
                const uint16_t* const* grads, float* master, float* exp_avg, float* exp_avg_sq,
                uint16_t* params, const or_hparams* hp, or_scale_state* st, or_result* res);

@@ -94,6 +94,12 @@ MUTANTS = [
     ("no_sync regeneration sums ranks before micro-batches",
      "  if (mode == 0) {\n    for (a = 0; a < n_micro; ++a) {",
      "  if (mode == 0 || mode == 1) {\n    for (a = 0; a < n_micro; ++a) {"),
+    ("reshard leaves the new padding unwritten",
+     "        else\n          memset(dst, 0, (size_t)elem_bytes);",
+     "        else\n          (void)dst;"),
+    ("reshard places later ranks one element early",
+     "memcpy(dst, logical + (ub[u].lam + e) * elem_bytes, (size_t)elem_bytes);",
+     "memcpy(dst, logical + (ub[u].lam + e - (r > 0)) * elem_bytes, (size_t)elem_bytes);"),
     ("ring traffic without the (N-1)/N factor",
      "return passes * ((double)(n_ranks - 1) / (double)n_ranks) * 2.0 * (double)psi_pad;",
      "return passes * 2.0 * (double)psi_pad;"),

@@ -895,3 +895,76 @@ def test_clipped_gradient_norm(orc):
         hp.max_norm = 0.0
         sc0, res0 = O.finish(ss, 0, n, hp, OI.scale_state(w))
         assert res0.coef == 1.0 and sc0.gs == np.float32(1.0 / (w.loss_scale * n))
+
+
+# ------------------------------------------------------------- resharding ----
+def _layouts(numel, rows, n):
+    unit_ids, u = [], 0
+    for i in range(len(numel)):
+        if i and i % 2 == 0:
+            u += 1
+        unit_ids.append(u)
+    return {"flat": O.layout(numel, unit_ids, n, W.GLOBAL_FLAT),
+            "units": O.layout(numel, unit_ids, n, W.PER_UNIT),
+            "dim0": O.layout_dim0(numel, rows, n)}
+
+
+def test_reshard_by_logical_index(orc):
+    """[F5]: a change of DP size needs the state re-laid out.  Resharding
+    from any layout and N to any other keeps every real element (checked
+    against an independent logical-order rebuild), zeroes the new padding,
+    and a round trip returns the original bits."""
+    rows = [7, 1, 16, 3, 5, 1, 33]
+    cols = [6, 9, 4, 1, 1, 64, 8]
+    numel = [r * c for r, c in zip(rows, cols)]
+    rng = np.random.default_rng(8)
+    for na, nb in ((4, 3), (1, 8), (5, 2), (3, 3)):
+        la, lb = _layouts(numel, rows, na), _layouts(numel, rows, nb)
+        for ka in la:
+            for kb in lb:
+                ua, psi, _ = la[ka]
+                ub, _, _ = lb[kb]
+                logical = rng.standard_normal(psi).astype(np.float32)
+                a = OI.to_rank_shards(ua, na, logical)
+                b = O.reshard(ua, na, a, ub, nb)
+                assert np.array_equal(OI.rank_shards_to_logical(ub, b).view(np.uint32),
+                                      logical.view(np.uint32))
+                ref_pad = OI.to_rank_shards(ub, nb, logical)
+                assert all(np.array_equal(x.view(np.uint32), y.view(np.uint32))
+                           for x, y in zip(b, ref_pad)), (ka, kb)
+                back = O.reshard(ub, nb, b, ua, na)
+                assert all(np.array_equal(x.view(np.uint32), y.view(np.uint32))
+                           for x, y in zip(back, a))
+                b16 = O.reshard(ua, na, [O.narrow(W.BF16, x) for x in a], ub, nb)
+                assert all(np.array_equal(x, O.narrow(W.BF16, y)) for x, y in zip(b16, ref_pad))
+
+
+@pytest.mark.parametrize("na,nb", [(4, 3), (2, 8), (3, 1)])
+def test_switching_rank_count_equals_dp(orc, na, nb):
+    """Three steps at N_a ranks, the state resharded, two steps at N_b: the
+    state and the 16-bit parameters equal plain data parallelism that runs
+    N_a replicas for three steps and N_b after, bit for bit."""
+    wa = _small_workload(na, W.PER_UNIT, grad_dtype=W.BF16, dynamic=False, scale=1.0)
+    wb = _small_workload(nb, W.GLOBAL_FLAT, grad_dtype=W.BF16, dynamic=False, scale=1.0)
+    run = OI.OracleRun(wa)
+    p = OI.master_logical(wa, run.psi)
+    m, v = np.zeros_like(p), np.zeros_like(p)
+    prm = O.narrow(W.BF16, p)
+    st, hp = OI.scale_state(wa), OI.hparams(wa)
+    for step in range(1, 6):
+        if step == 4:  # switch: re-lay the rank shards for N_b, same scale state
+            new = OI.OracleRun(wb)
+            for name in ("master", "m", "v"):
+                setattr(new, name, O.reshard(run.units, na, getattr(run, name), new.units, nb))
+            new.st, new.step_no = run.st, run.step_no
+            run = new
+        w = wa if step < 4 else wb
+        grads = OI.replicas(w, run.units, run.psi_pad, step, 1.0)
+        r1 = run.step(grads)
+        r2 = O.dp_step(W.BF16, W.BF16, w.n_ranks, [OI.padded_to_logical(run.units, g) for g in grads],
+                       p, m, v, prm, hp, st)
+        assert r1.sumsq == r2.sumsq and r1.t == r2.t
+        for mine, ref in ((run.master, p), (run.m, m), (run.v, v)):
+            assert np.array_equal(OI.rank_shards_to_logical(run.units, mine).view(np.uint32),
+                                  ref.view(np.uint32))
+        assert np.array_equal(OI.padded_to_logical(run.units, run.full), prm)
