@@ -26,7 +26,10 @@
 // -ffp-contract=off and correctly rounded division and square root.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
+#include <new>
+#include <vector>
 
 #include "zf_hip_status.h"
 #include "zf_internal.h"
@@ -695,8 +698,38 @@ __global__ __launch_bounds__(kThreads) void zf_accumulate_kernel(AccArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Resharding: copy (or zero) a batch of element runs.  blockIdx.y = run;
+// the blocks of grid.x stride over the run's elements.
+constexpr int kReshardMax = 64;
+struct ReshardRun {
+  int64_t src;  // element offset in the source, or -1: write zeros
+  int64_t dst;  // element offset in the destination
+  int64_t len;
+};
+struct ReshardArgs {
+  const void* src;
+  void* dst;
+  ReshardRun r[kReshardMax];
+};
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void zf_reshard_kernel(ReshardArgs a) {
+  const ReshardRun run = a.r[blockIdx.y];
+  const T* s = static_cast<const T*>(a.src);
+  T* d = static_cast<T*>(a.dst) + run.dst;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < run.len; i += stride)
+    d[i] = run.src < 0 ? T(0) : s[run.src + i];
+}
+
+// ---------------------------------------------------------------------------
 // State initialisation.
+// 64 threads: every byte of the 256-byte block is written (the struct's
+// fields, then zeros), so a copied block is fully defined.
 __global__ void zf_state_init_kernel(DevState* s, double S, int32_t dynamic, int32_t growth) {
+  static_assert(kStateBytes == 64 * sizeof(uint32_t), "one word per thread");
+  reinterpret_cast<uint32_t*>(s)[threadIdx.x] = 0u;
+  __syncthreads();
   if (threadIdx.x != 0 || blockIdx.x != 0) return;
   s->loss_scale = S;
   s->beta1_pow = 1.0;
@@ -1093,6 +1126,87 @@ extern "C" int zf_accumulate(int32_t grad_dtype, const void* grad, float* acc, i
     else hipLaunchKernelGGL((zf_accumulate_kernel<ZF_F16, false>), grid, dim3(kThreads), 0, s, a);
   }
   return hip_ok(hipGetLastError()) ? ZF_OK : ZF_EHIP;
+}
+
+namespace {
+
+// Real runs of a plan in logical order: (logical start, padded offset, len),
+// plus the padding runs (offset, len).
+struct Run {
+  int64_t lam, off, len;
+};
+void plan_runs(const zf_plan* p, std::vector<Run>& real, std::vector<Run>& pad) {
+  const int nr = p->summary.n_ranks;
+  for (const zf_unit_info& u : p->units)
+    for (int r = 0; r < nr; ++r) {
+      int64_t len = u.L - (int64_t)r * u.S;
+      if (len < 0) len = 0;
+      if (len > u.S) len = u.S;
+      const int64_t off = u.O + (int64_t)r * u.S;
+      if (len > 0) real.push_back(Run{u.lam + (int64_t)r * u.S, off, len});
+      if (len < u.S) pad.push_back(Run{-1, off + len, u.S - len});
+    }
+}
+
+}  // namespace
+
+extern "C" int zf_reshard(const zf_plan* from, const zf_plan* to, const void* src,
+                          int64_t src_numel, void* dst, int64_t dst_numel, int32_t elem_bytes,
+                          void* stream) {
+  if (!valid_plan(from) || !valid_plan(to) || !src || !dst) return ZF_EINVAL;
+  if (elem_bytes != 2 && elem_bytes != 4) return ZF_EINVAL;
+  if (from->summary.psi != to->summary.psi) return ZF_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) &
+      (uintptr_t)(elem_bytes - 1))
+    return ZF_EALIGN;
+  if (src_numel < from->summary.psi_pad || dst_numel < to->summary.psi_pad) return ZF_ESIZE;
+  const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
+  const uintptr_t s1 = s0 + (uintptr_t)from->summary.psi_pad * elem_bytes;
+  const uintptr_t d1 = d0 + (uintptr_t)to->summary.psi_pad * elem_bytes;
+  if (s0 < d1 && d0 < s1) return ZF_EINVAL;  // overlapping arrays
+  std::vector<ReshardRun> runs;
+  try {
+    std::vector<Run> ra, rb, pa, pb;
+    plan_runs(from, ra, pa);
+    plan_runs(to, rb, pb);
+    // merge the two logical orders: each overlap of a source run and a
+    // destination run is one copy
+    size_t i = 0, j = 0;
+    while (i < ra.size() && j < rb.size()) {
+      const int64_t lo = std::max(ra[i].lam, rb[j].lam);
+      const int64_t hi = std::min(ra[i].lam + ra[i].len, rb[j].lam + rb[j].len);
+      if (lo < hi)
+        runs.push_back(ReshardRun{ra[i].off + (lo - ra[i].lam), rb[j].off + (lo - rb[j].lam),
+                                  hi - lo});
+      if (ra[i].lam + ra[i].len < rb[j].lam + rb[j].len) ++i;
+      else ++j;
+    }
+    for (const Run& p : pb) runs.push_back(ReshardRun{-1, p.off, p.len});
+  } catch (const std::bad_alloc&) {
+    return ZF_ENOMEM;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  for (size_t first = 0; first < runs.size(); first += kReshardMax) {
+    ReshardArgs a;
+    a.src = src;
+    a.dst = dst;
+    const size_t count = std::min<size_t>(kReshardMax, runs.size() - first);
+    int64_t longest = 0;
+    for (size_t k = 0; k < count; ++k) {
+      a.r[k] = runs[first + k];
+      longest = std::max(longest, a.r[k].len);
+    }
+    int64_t bx = (longest + (int64_t)kThreads * 8 - 1) / ((int64_t)kThreads * 8);
+    bx = std::min<int64_t>(std::max<int64_t>(bx, 1), 4096);
+    const dim3 grid((uint32_t)bx, (uint32_t)count);
+    if (elem_bytes == 4)
+      hipLaunchKernelGGL(zf_reshard_kernel<uint32_t>, grid, dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL(zf_reshard_kernel<uint16_t>, grid, dim3(kThreads), 0, s, a);
+    if (!hip_ok(hipGetLastError())) return ZF_EHIP;
+  }
+  return ZF_OK;
 }
 
 extern "C" int zf_gather(const zf_plan* plan, int64_t unit, int32_t dtype,

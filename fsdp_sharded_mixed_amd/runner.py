@@ -184,6 +184,39 @@ class DeviceRun:
     def result(self):
         return zf.read_result(self.state)
 
+    # ---- resharding and checkpoints ------------------------------------------
+    def replan(self, w_new):
+        """A DeviceRun for workload w_new (same model, another layout or rank
+        count) holding this run's state, re-laid out by logical index with
+        zf_reshard; the state block (loss scale, t, beta powers) is copied."""
+        assert not (self.w.offload or w_new.offload), "reshards device-resident state"
+        new = DeviceRun(w_new, device=self.device)
+        for name in ("master", "exp_avg", "exp_avg_sq"):
+            zf.reshard(self.plan, new.plan, getattr(self, name), getattr(new, name))
+        if self.params is not None and new.params is not None:
+            zf.reshard(self.plan, new.plan, self.params, new.params)
+        elif new.params is not None:  # fp32 parameters before: cast them
+            new.params.copy_(new.master.to(new.params.dtype))
+        new.state.copy_(self.state)
+        new.step_no, new.loss_scale = self.step_no, self.loss_scale
+        return new
+
+    def checkpoint(self):
+        """Host copies of everything a resumed run needs: the fp32 state, the
+        16-bit parameters and the state block (no file format)."""
+        keep = {n: getattr(self, n).detach().cpu().clone()
+                for n in ("master", "exp_avg", "exp_avg_sq", "state")}
+        if self.params is not None:
+            keep["params"] = self.params.detach().cpu().clone()
+        keep["step_no"], keep["loss_scale"] = self.step_no, self.loss_scale
+        return keep
+
+    def restore(self, ckpt):
+        for n in ("master", "exp_avg", "exp_avg_sq", "state", "params"):
+            if n in ckpt:
+                getattr(self, n).copy_(ckpt[n])
+        self.step_no, self.loss_scale = ckpt["step_no"], ckpt["loss_scale"]
+
     def unit_shards(self, u):
         """Rank r's 16-bit shard of unit u: params[O_u + r*S_u : +S_u]."""
         info = self.plan.units[u]

@@ -124,6 +124,8 @@ _SIGNATURES = {
     "zf_cpu_adam": (C.c_int, [C.POINTER(Hparams), C.POINTER(CpuAdamArgs)]),
     "zf_offload_step": (C.c_int, [C.c_void_p, C.POINTER(Hparams), C.POINTER(OffloadArgs),
                                   C.c_void_p, C.POINTER(StepResult)]),
+    "zf_reshard": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p,
+                             C.c_int64, C.c_int32, C.c_void_p]),
     "zf_strerror": (C.c_char_p, [C.c_int]),
     "zf_hip_error_name": (C.c_char_p, []),
 }
@@ -385,3 +387,14 @@ def offload_step(plan, hp, grad_dtype, param_dtype, grads, grad_shards, params, 
     _check(lib.zf_offload_step(_handle(plan), C.byref(hp), C.byref(a), _stream(stream),
                                C.byref(out)), "zf_offload_step")
     return out
+
+
+def reshard(plan_from, plan_to, src, dst, stream=None, elem_bytes=None, src_numel=None,
+            dst_numel=None):
+    """zf_reshard of one per-element array (tensors, or addresses with the
+    counts and elem_bytes)."""
+    eb = elem_bytes if elem_bytes is not None else src.element_size()
+    sn = src_numel if src_numel is not None else src.numel()
+    dn = dst_numel if dst_numel is not None else dst.numel()
+    _check(lib.zf_reshard(_handle(plan_from), _handle(plan_to), _ptr(src), int(sn), _ptr(dst),
+                          int(dn), int(eb), _stream(stream)), "zf_reshard")

@@ -19,6 +19,8 @@
  *         3.4 bit-exactness, 3.6 padding, 4.1 communication, 5.1 FSDP's
  *         per-unit all-gather, 5.2 FlatParameter (flatten, pad, split),
  *         5.6 gradient accumulation, 7.1-7.2 ZeRO-Offload and CPU-Adam.
+ *   [F5]  Femtotron dev log #5 (Data Parallelism): resharding when the DP
+ *         size changes.
  *   [F6]  Femtotron dev log #6 (ZeRO-1 and ZeRO-2): the sharding protocol
  *         make_master / reduce_grads / gather_weights / post_step, and the
  *         master as one 1-D vector.
@@ -32,7 +34,8 @@
  *         五.6 (FSDP2: per-parameter dim-0 shards, the fp32 shard is the
  *         parameter, fp32 reduce-scatter into the shard's gradient, cast to
  *         the parameter dtype at all-gather time), 六.2 (Stage 3 vs FSDP1 vs
- *         FSDP2), 三.3 (Megatron's gradient buffer and buckets, no_sync
+ *         FSDP2), 六.4 (checkpoint formats and resharding), 三.3 (Megatron's
+ *         gradient buffer and buckets, no_sync
  *         accumulation in fp32) and 五.7 (global gradient-norm clipping;
  *         gradient accumulation on the shard).
  *
@@ -188,7 +191,11 @@ int64_t zf_state_bytes(void);
 /* Initialise a state block (device memory, zf_state_bytes() bytes, 16-byte
  * aligned): loss scale S > 0, dynamic scaling on/off (halve on overflow;
  * double after growth_interval applied steps in a row, never if <= 0),
- * t = 0.  Enqueued on `stream`.  Errors: ZF_EINVAL, ZF_EALIGN, ZF_EHIP. */
+ * t = 0; every byte of the block is written.  The block is plain data with
+ * no pointers and does not depend on N or the layout: copying it to the
+ * host and back (a checkpoint) or to another plan's run (zf_reshard)
+ * resumes the step sequence exactly.  Enqueued on `stream`.  Errors:
+ * ZF_EINVAL, ZF_EALIGN, ZF_EHIP. */
 int zf_state_init(void* d_state, double loss_scale, int32_t dynamic, int32_t growth_interval,
                   void* stream);
 
@@ -343,6 +350,22 @@ typedef struct {
   int32_t growth_ctr;
   float bc1, bc2;       /* binary32 bias corrections 1 - beta^t of the update */
 } zf_step_result;
+
+/* Resharding ([F5]: a checkpoint saved at one DP size loaded at another
+ * needs the state redistributed; [MDT] 六.4: universal checkpoints, DCP):
+ * re-lay one per-element array from plan `from` to plan `to` by logical
+ * index.  Every real element moves from its padded-flat place under `from`
+ * to its place under `to`; every padding element of `dst` becomes zero.
+ * The plans may differ in layout and rank count but must describe the same
+ * model (the same segments in the same order; Psi is checked).  Rank r's
+ * real part of unit u is the logical run [lam_u + r*S_u, +clamp(L_u -
+ * r*S_u, 0, S_u)) in every layout.  src / dst: device arrays of src_numel
+ * >= Psi'(from) and dst_numel >= Psi'(to) elements of elem_bytes (2: 16-bit
+ * parameters, 4: fp32 master / moments), aligned to elem_bytes, not
+ * overlapping.  The device state block needs no change (it does not depend
+ * on N).  Errors: ZF_EINVAL, ZF_EALIGN, ZF_ESIZE, ZF_ENOMEM, ZF_EHIP. */
+int zf_reshard(const zf_plan* from, const zf_plan* to, const void* src, int64_t src_numel,
+               void* dst, int64_t dst_numel, int32_t elem_bytes, void* stream);
 
 /* Name of the HIP runtime error behind the calling thread's last ZF_EHIP
  * ("hipSuccess" if there was none).  The string is static. */

@@ -35,7 +35,8 @@ def test_headers_declare_the_calls():
     names = _declared("zf.h")
     for required in ("zf_plan_flat", "zf_shard_step", "zf_gather"):
         assert required in names
-    assert len(_declared("zf_inputs.h")) == 3
+    assert _declared("zf_inputs.h") == ["zfi_fill_normal16", "zfi_fill_normal32", "zfi_stream_output",
+                                        "zfi_stream_probe"]
 
 
 @pytest.mark.parametrize("header,lib", [("zf.h", "libzf.so"), ("zf_inputs.h", "libzf_inputs.so")])
@@ -272,6 +273,20 @@ def test_step_argument_errors_enqueue_nothing(zf):
     assert off(workspace_size=need - 1) == -4
     assert off(grad_dtype=0) == -3
     assert Z.lib.zf_offload_step(None, C.byref(hp), None, None, None) == -1
+    # resharding: plans of the same model only, sizes, alignment, no overlap
+    rs = Z.lib.zf_reshard
+    p3 = Z.plan_flat([(100, 0)], 3, W.GLOBAL_FLAT, 2)
+    p_other = Z.plan_flat([(99, 0)], 3, W.GLOBAL_FLAT, 2)
+    far = ok + (1 << 20)
+    assert rs(plan.handle, p3.handle, ok, 100, far, 102, 3, None) == -1
+    assert rs(plan.handle, p_other.handle, ok, 100, far, 102, 4, None) == -1
+    assert rs(plan.handle, None, ok, 100, far, 102, 4, None) == -1
+    assert rs(plan.handle, p3.handle, None, 100, far, 102, 4, None) == -1
+    assert rs(plan.handle, p3.handle, ok + 2, 100, far, 102, 4, None) == -2
+    assert rs(plan.handle, p3.handle, ok, 100, far + 1, 102, 2, None) == -2
+    assert rs(plan.handle, p3.handle, ok, 99, far, 102, 4, None) == -4
+    assert rs(plan.handle, p3.handle, ok, 100, far, 101, 4, None) == -4
+    assert rs(plan.handle, p3.handle, ok, 100, ok + 200, 102, 4, None) == -1  # overlap
     assert Z.lib.zf_state_init(None, 1.0, 0, 10, None) == -1
     assert Z.lib.zf_state_init(ok, 0.0, 0, 10, None) == -1
     assert Z.lib.zf_state_init(ok + 4, 1.0, 0, 10, None) == -2
