@@ -270,6 +270,29 @@ def stream_probes(reps=10):
     return out
 
 
+def apply_overrides(w, items):
+    """Apply FIELD=VALUE overrides to a workload (typed like the field)."""
+    done = {}
+    for item in items:
+        key, _, val = item.partition("=")
+        if not hasattr(w, key) or key in ("segments", "extra"):
+            raise SystemExit(f"bench.py: unknown workload field {key!r}")
+        cur = getattr(w, key)
+        if isinstance(cur, bool):
+            new = val.lower() in ("1", "true", "yes")
+        elif isinstance(cur, int) or cur is None and key in ("inject_step", "bucket_numel"):
+            new = int(val)
+        elif isinstance(cur, float):
+            new = float(val)
+        else:
+            new = val
+        setattr(w, key, new)
+        done[key] = new
+    if done:
+        w.name = w.name + "+" + ",".join(f"{k}={v}" for k, v in done.items())
+    return done
+
+
 def host_info():
     """CPU model, logical CPUs and RAM of the host the oracle ran on."""
     model = ""
@@ -414,6 +437,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--set", action="append", default=[], metavar="FIELD=VALUE",
+                    help="override a workload field (seed, n_ranks, stage, lr, n_micro, "
+                         "max_norm, ...); the line's config records every override")
+    ap.add_argument("--per-step-log", metavar="FILE",
+                    help="also write one JSON line per timed step (result and time)")
     ap.add_argument("--offload-chunks", type=int, default=16,
                     help="pipeline chunks of an offload step")
     ap.add_argument("--offload-threads", type=int, default=0,
@@ -440,6 +468,7 @@ def main():
     from fsdp_sharded_mixed_amd import runner, workloads as W
 
     w = W.get(args.workload)
+    overrides = apply_overrides(w, args.set)
     torch.cuda.set_device(0)
     print(f"bench: {w.name} Psi={w.psi:,} N={w.n_ranks} stage={w.stage}", file=sys.stderr,
           flush=True)
@@ -515,7 +544,8 @@ def main():
         one_step(phase_events=[e.cuda_event for e in row[1:5]], backward_event=row[0])
         row[5].record()  # after the unit gathers
     torch.cuda.synchronize()
-    per_step = sorted((r[0] if w.backward_rs else r[1]).elapsed_time(r[5]) for r in evs)
+    step_ms = [(r[0] if w.backward_rs else r[1]).elapsed_time(r[5]) for r in evs]
+    per_step = sorted(step_ms)
     evs_b = [r[0] for r in evs]
     evs = [r[1:5] for r in evs]
     bw = (sum(b.elapsed_time(r[0]) for b, r in zip(evs_b, evs)) / args.steps
@@ -581,6 +611,17 @@ def main():
         "kernels_ms": kernels,
         "roofline": roof,
     }
+    if overrides:
+        line["config"]["overrides"] = overrides
+    if args.per_step_log:
+        res = dev.result()
+        with open(args.per_step_log, "w") as f:
+            for k, t_ms in enumerate(step_ms):
+                f.write(json.dumps({"workload": w.name, "step": k, "ms": round(t_ms, 5),
+                                    "n_ranks": w.n_ranks, "stage": w.stage}) + "\n")
+            f.write(json.dumps({"workload": w.name, "last_result": {
+                "skipped": res.skipped, "t": res.t, "loss_scale": res.scale_next,
+                "norm": res.norm, "clip_coef": res.coef}}) + "\n")
     line["stream_probe_gbs"] = probe
     if roof["kernel"].startswith("zf_pass2"):
         roof["frac_of_4r4w_probe"] = round(roof["achieved"] / probe["4r4w"], 4)

@@ -22,7 +22,8 @@ constexpr uint64_t kPlanMagic = 0x7a665f706c616e31ull;  // "zf_plan1"
 //    shared window.  One 2-quad step per thread for N <= 2 (-6% at 4.06B),
 //    two steps otherwise;
 //  - the update pass uses plain loads; two 2-quad steps per thread on large
-//    recomputing plans, one otherwise (within 1% either way);
+//    recomputing plans, one otherwise (within 1% either way); its tiles
+//    walk in block order (the XCD-contiguous walk costs +3% there);
 //  - the materialised sums go out with non-temporal stores and the update
 //    pass walks its tiles forward: walking them backward so that the newest
 //    sums might still be in the 256 MB Infinity Cache saved 2% of the update
