@@ -88,12 +88,18 @@ COPY_BYTES = 1 << 30  # calibration copy: 1 GiB read + 1 GiB written
 
 
 def kernel_source_hash():
-    """Fingerprint of the step library's sources (kernels, tiling, planner)."""
+    """Fingerprint of the step library's code (kernels, tiling, planner):
+    the sources with comments removed and whitespace collapsed, so that a
+    comment does not invalidate measured counters but any code change does."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for path in KERNEL_SOURCES:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

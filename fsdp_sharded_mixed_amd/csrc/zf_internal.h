@@ -16,7 +16,9 @@ constexpr uint64_t kPlanMagic = 0x7a665f706c616e31ull;  // "zf_plan1"
 // block finishes.  The tiling depends only on the plan, so the norm's
 // rounding does not depend on the device or the run.
 // Tiling (measured on MI355X, in-process A/B over builds on one box):
-//  - pass 1 streams the N replicas with the non-temporal load hint.  With
+//  - pass 1 streams the N replicas with the non-temporal load hint, one
+//    8-byte quad per lane per replica (16-byte loads of quad pairs cost
+//    +50% at N = 8, where the sums' stores become strided, and +8% at N = 2).  With
 //    N <= 4 it walks the tiles XCD-contiguously (N = 2: -6%, 3: -5%,
 //    4: -5%); at N = 8 that walk costs +4%, so many replicas keep one
 //    shared window.  One 2-quad step per thread for N <= 2 (-6% at 4.06B),

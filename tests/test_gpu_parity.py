@@ -350,3 +350,41 @@ def test_stream_probe_sums(R):
             want = want + t
         for d in dst:
             assert torch.equal(d, want)
+
+
+@pytest.mark.parametrize("dtype", [W.F16, W.BF16])
+def test_rs_pair_sweep(R, dtype):
+    """The N = 2 reduce-scatter over every 16-bit value of replica 0 against
+    512 values of replica 1 that cover every exponent with edge mantissas
+    (33.5M pairs: rounding ties, cancellation, overflow to inf, NaN
+    propagation), and N = 1 over all 65,536 values: bit-exact against the
+    oracle (NaN positions equal)."""
+    from fsdp_sharded_mixed_amd import zf
+    allv = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    man_bits = 10 if dtype == W.F16 else 7
+    exps = np.arange(1 << (15 - man_bits), dtype=np.uint32) << man_bits
+    top = (1 << man_bits) - 1
+    half = 1 << (man_bits - 1)
+    mans = np.array([0, 1, 2, top, top - 1, half, half - 1, half + 1], np.uint32)
+    other = (exps[:, None] | mans[None, :]).ravel()
+    other = np.concatenate([other, other | 0x8000]).astype(np.uint16)
+    assert other.size >= 512
+    other = other[np.linspace(0, other.size - 1, 512).astype(np.int64)]
+    r0 = np.repeat(allv, other.size)
+    r1 = np.tile(other, allv.size)
+    n = r0.size
+    for reps in ([r0, r1], [allv]):
+        nr = len(reps)
+        w = small(nr, W.GLOBAL_FLAT, [reps[0].size], gdt=dtype)
+        plan = R.plan_workload(w)
+        tdt = torch.float16 if dtype == W.F16 else torch.bfloat16
+        dev_g = [torch.from_numpy(x.view(np.int16)).cuda().view(tdt) for x in reps]
+        out = torch.empty(plan.psi_pad, dtype=torch.float32, device="cuda")
+        zf.reduce_scatter(plan, dtype, dev_g, out)
+        units, _, _ = OI.plan(w)
+        ref = OI.rank_shards_to_padded(units, O.reduce_scatter(dtype, nr, units, reps))
+        got = G.f32(out)
+        nan = np.isnan(ref)
+        assert np.array_equal(np.isnan(got), nan)
+        assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+    assert n == (1 << 16) * 512
