@@ -217,12 +217,18 @@ def summarize_pmc(fetch_dir, write_dir, workload, out, commands):
         return sum(xs), len(xs)
 
     fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
-    copy_key = next(k for k in fetch if "copy" in k.lower() and "zf_" not in k)
-    f_scale = COPY_BYTES / (pick(fetch, copy_key) * 1024.0)
-    w_scale = COPY_BYTES / (pick(write, copy_key) * 1024.0)
+    # the calibration copy: the bench's own 1-read/1-write probe kernel,
+    # whose every dispatch reads and writes exactly PROBE_FLOATS * 4 bytes
+    def median_of(vals, name):
+        xs = sorted(vals[name])
+        return xs[len(xs) // 2]
+
+    copy_key = next(k for k in fetch if "stream_probe<1, 1>" in k)
+    f_scale = 4 * PROBE_FLOATS / (median_of(fetch, copy_key) * 1024.0)
+    w_scale = 4 * PROBE_FLOATS / (median_of(write, copy_key) * 1024.0)
     w = W.get(workload)
     res = {"workload": workload, "kernel_source_sha256_16": kernel_source_hash(),
-           "calibration": {"kernel": copy_key, "bytes_each_way": COPY_BYTES,
+           "calibration": {"kernel": copy_key, "bytes_each_way": 4 * PROBE_FLOATS,
                            "fetch_scale": f_scale, "write_scale": w_scale},
            "commands": commands}
     # one finish kernel per step: the step count of the run
@@ -443,6 +449,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-skip-probe", action="store_true",
+                    help="do not time skipped steps (profiled runs: keeps every launch of "
+                         "the step kernels an applied step's)")
     ap.add_argument("--set", action="append", default=[], metavar="FIELD=VALUE",
                     help="override a workload field (seed, n_ranks, stage, lr, n_micro, "
                          "max_norm, ...); the line's config records every override")
@@ -641,7 +650,8 @@ def main():
         line["hbm_gbs_counted"] = round(cg, 2)
         line["pct_hbm_peak_counted"] = round(100 * cg / PEAK_HBM_GBS, 2)
         line["pct_device_copy_counted"] = round(100 * cg / copy_gbs, 2)
-    line["skipped_step_ms"] = skipped_step_ms(w, dev, one_step)
+    if not args.no_skip_probe:
+        line["skipped_step_ms"] = skipped_step_ms(w, dev, one_step)
     if w.backward_rs:
         line["config"]["micro_batches"] = w.n_micro
         line["config"]["accumulation"] = ["reduce-scatter every micro-batch",
