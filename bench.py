@@ -404,7 +404,8 @@ def offload_line(args, w, dev, ms, wall, copy_gbs):
     for _ in range(reps):
         zf.cpu_adam(dev.hp, dev.h_grad, dev.master, dev.exp_avg, dev.exp_avg_sq, res.gs,
                     res.bc1, res.bc2, params=dev.h_params, param_dtype=w.param_dtype,
-                    n_threads=dev.n_threads)
+                    n_threads=dev.n_threads,
+                    grad_dtype=w.grad_dtype if w.offload_down16 else zf.F32)
     cpu_s = (time.perf_counter() - t0) / reps
     threads = dev.n_threads if dev.n_threads > 0 else (os.cpu_count() or 1)
     s = dev.plan.summary
@@ -422,7 +423,8 @@ def offload_line(args, w, dev, ms, wall, copy_gbs):
                 "random-init weights)",
         "config": {"workload": w.name, "psi": w.psi, "psi_padded": s.psi_pad,
                    "virtual_ranks": w.n_ranks, "zero_stage": w.stage,
-                   "offload": "fp32 state + CPU-Adam on the host",
+                   "offload": "fp32 state + CPU-Adam on the host, "
+                              + ("16-bit" if w.offload_down16 else "fp32") + " sums down",
                    "cpu_adam_threads": threads, "pipeline_chunks": dev.n_chunks},
         "params_updated_per_s": round(w.psi / (ms * 1e-3), 1),
         "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
@@ -430,9 +432,10 @@ def offload_line(args, w, dev, ms, wall, copy_gbs):
         "device_copy_gbs": round(copy_gbs, 1),
         "phases_ms": {"gpu_reduce": round(red, 4), "download": round(down, 4),
                       "cpu_adam_and_upload": round(upd, 4)},
-        "pcie_down_gbs": round(4 * n / (down * 1e-3) / 1e9, 2),
+        "pcie_down_gbs": round((2 if w.offload_down16 else 4) * n / (down * 1e-3) / 1e9, 2),
         "cpu_adam": {"ms": round(cpu_s * 1e3, 3), "params_per_s": round(n / cpu_s, 1),
-                     "host_gbs": round(30 * n / cpu_s / 1e9, 2), "threads": threads,
+                     "host_gbs": round((28 if w.offload_down16 else 30) * n / cpu_s / 1e9, 2),
+                     "threads": threads,
                      "host_cpus": os.cpu_count()},
         "roofline": {"bound": "hbm", "achieved": round(p1_gbs, 2), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(p1_gbs / PEAK_HBM_GBS, 4),

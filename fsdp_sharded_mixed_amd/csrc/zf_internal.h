@@ -86,9 +86,11 @@ constexpr int64_t kStateBytes = 256;
 // Validates `args` and enqueues the step on `stream`: pass 1, the norm
 // reduction and the finish kernel, then (update == true) the update pass.
 // With update == false the fp32 state and params are neither needed nor
-// touched and grad_shards must be given (pass 1 leaves the sums there).
+// touched and grad_shards must be given (pass 1 leaves the sums there, in
+// fp32, or with down16 rounded to the gradient dtype in its first Psi'*2
+// bytes, the norm and overflow then taken on the rounded values).
 int step_enqueue(const zf_plan* plan, const zf_hparams* hp, const zf_step_args* args,
-                 void* stream, bool update);
+                 void* stream, bool update, bool down16);
 
 // Binary32 hyperparameters of the update, each rounded once from its double.
 struct UpdateConsts {
@@ -112,9 +114,11 @@ extern thread_local int last_hip_error;
 // CPU-Adam (host, AVX2): the update pass's element arithmetic over [0, n)
 // with the given step scalars, split over n_threads threads (<= 0: all).
 bool host_simd_ok();
+// grad_dtype: ZF_F32 (grad points to binary32) or ZF_F16 / ZF_BF16 (16-bit
+// gradients, widened exactly).
 void cpu_adam_run(const zf_hparams* hp, float gs, float bc1, float bc2, int64_t n,
-                  const float* grad, float* master, float* exp_avg, float* exp_avg_sq,
-                  uint16_t* params, int32_t param_dtype, int32_t n_threads);
+                  const void* grad, int32_t grad_dtype, float* master, float* exp_avg,
+                  float* exp_avg_sq, uint16_t* params, int32_t param_dtype, int32_t n_threads);
 
 }  // namespace zf
 

@@ -61,7 +61,12 @@ hipStream_t upload_stream() {
 extern "C" int zf_offload_step(const zf_plan* plan, const zf_hparams* hp,
                                const zf_offload_args* a, void* stream, zf_step_result* result) {
   if (!plan || plan->magic != zf::kPlanMagic || !hp || !a) return ZF_EINVAL;
-  if (a->reserved != 0 || a->n_chunks < 1 || a->n_chunks > 4096) return ZF_EINVAL;
+  if ((a->down16 != 0 && a->down16 != 1) || a->n_chunks < 1 || a->n_chunks > 4096)
+    return ZF_EINVAL;
+  const bool down16 = a->down16 == 1;
+  // bytes per downloaded element: the fp32 sums, or the sums rounded to the
+  // gradient dtype
+  const int64_t eb = down16 ? 2 : 4;
   if (a->param_dtype != ZF_F16 && a->param_dtype != ZF_BF16) return ZF_EDTYPE;
   if (!a->params || !a->grad_shards || !a->h_state || !a->h_grad || !a->h_master ||
       !a->h_exp_avg || !a->h_exp_avg_sq || !a->h_params)
@@ -99,7 +104,7 @@ extern "C" int zf_offload_step(const zf_plan* plan, const zf_hparams* hp,
     if (!a->phase_events || !a->phase_events[i]) return true;
     return hip_ok(hipEventRecord(static_cast<hipEvent_t>(a->phase_events[i]), st));
   };
-  int rc = zf::step_enqueue(plan, hp, &s, stream, false);
+  int rc = zf::step_enqueue(plan, hp, &s, stream, false, down16);
   if (rc != ZF_OK) return rc;
   const int64_t C = std::min<int64_t>(a->n_chunks, (n + kChunkAlign - 1) / kChunkAlign);
   auto chunk = [&](int64_t c, int64_t& b, int64_t& e) {
@@ -119,8 +124,9 @@ extern "C" int zf_offload_step(const zf_plan* plan, const zf_hparams* hp,
     int64_t b, e;
     chunk(c, b, e);
     if (!hip_ok(hipEventCreateWithFlags(&down[c], hipEventDisableTiming)) ||
-        !hip_ok(hipMemcpyAsync(a->h_grad + b, a->grad_shards + b, (e - b) * sizeof(float),
-                       hipMemcpyDeviceToHost, st)) ||
+        !hip_ok(hipMemcpyAsync(reinterpret_cast<char*>(a->h_grad) + b * eb,
+                               reinterpret_cast<const char*>(a->grad_shards) + b * eb,
+                               (e - b) * eb, hipMemcpyDeviceToHost, st)) ||
         !hip_ok(hipEventRecord(down[c], st))) {
       cleanup();
       return ZF_EHIP;
@@ -153,9 +159,10 @@ extern "C" int zf_offload_step(const zf_plan* plan, const zf_hparams* hp,
         cleanup();
         return ZF_EHIP;
       }
-      zf::cpu_adam_run(hp, h.gs, h.bc1, h.bc2, e - b, a->h_grad + b, a->h_master + b,
-                       a->h_exp_avg + b, a->h_exp_avg_sq + b, hp16 + b, a->param_dtype,
-                       a->n_threads);
+      zf::cpu_adam_run(hp, h.gs, h.bc1, h.bc2, e - b,
+                       reinterpret_cast<const char*>(a->h_grad) + b * eb,
+                       down16 ? a->grad_dtype : ZF_F32, a->h_master + b, a->h_exp_avg + b,
+                       a->h_exp_avg_sq + b, hp16 + b, a->param_dtype, a->n_threads);
       // up: this chunk's 16-bit parameters while the CPU takes the next one
       if (!hip_ok(hipMemcpyAsync(dp16 + 2 * b, hp16 + b, (e - b) * sizeof(uint16_t),
                          hipMemcpyHostToDevice, up))) {

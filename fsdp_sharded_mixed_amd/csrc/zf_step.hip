@@ -215,13 +215,18 @@ __device__ __forceinline__ void block_reduce(double& ss, uint32_t& bad) {
 struct Pass1Args {
   GradPtrs g;
   int64_t n;          // Psi'
-  float* rs;          // fp32 sums (MAT) or unused
+  float* rs;          // fp32 sums (OUT == 1) or unused
+  uint16_t* rs16;     // 16-bit sums (OUT == 2) or unused
   Partial* partials;  // one per tile (NORM) or unused
   int32_t nr;
   int32_t tile_map;   // see tile_of_block
 };
 
-template <int NR, int DT, bool MAT, bool NORM, int Q>
+// OUT: 0 the sums stay in registers; 1 they are stored in fp32; 2 they are
+// rounded to the gradient dtype and stored in 16 bits, and the overflow flag
+// and the norm are taken on the rounded values (the 16-bit gradients an
+// offloaded optimizer receives).
+template <int NR, int DT, int OUT, bool NORM, int Q>
 __global__ __launch_bounds__(kThreads) void zf_pass1(Pass1Args a) {
   const int nr = NR > 0 ? NR : a.nr;
   const int64_t nq = a.n / kQuad;
@@ -241,7 +246,12 @@ __global__ __launch_bounds__(kThreads) void zf_pass1(Pass1Args a) {
 #pragma unroll
   for (int h = 0; h < Q; ++h) {
     if (!ok[h]) continue;
-    if constexpr (MAT) stq32_nt(a.rs, qi[h], acc[h]);
+    if constexpr (OUT == 1) stq32_nt(a.rs, qi[h], acc[h]);
+    if constexpr (OUT == 2) {
+      const u32x2 w = (u32x2){pack2<DT>(acc[h].x, acc[h].y), pack2<DT>(acc[h].z, acc[h].w)};
+      stq16_nt(a.rs16, qi[h], w);
+      acc[h] = widen4<DT>(w);
+    }
     if constexpr (NORM) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -253,8 +263,13 @@ __global__ __launch_bounds__(kThreads) void zf_pass1(Pass1Args a) {
   const int64_t tail0 = nq * kQuad;
   if (tile == gridDim.x - 1 && (int64_t)threadIdx.x < a.n - tail0) {
     const int64_t p = tail0 + threadIdx.x;
-    const float t = sum1<DT>(a.g, nr, p);
-    if constexpr (MAT) a.rs[p] = t;
+    float t = sum1<DT>(a.g, nr, p);
+    if constexpr (OUT == 1) a.rs[p] = t;
+    if constexpr (OUT == 2) {
+      const uint16_t q = narrow1<DT>(t);
+      a.rs16[p] = q;
+      t = widen1<DT>(q);
+    }
     if constexpr (NORM) {
       bad |= nonfinite(t) ? 1u : 0u;
       ss = ss + (double)t * (double)t;
@@ -769,10 +784,10 @@ int grads_ok(const zf_plan* plan, const void* const* grads, GradPtrs& out) {
   return ZF_OK;
 }
 
-template <bool MAT, bool NORM, int U>
+template <int OUT, bool NORM, int U>
 void launch_pass1_u(int nr, int32_t dt, dim3 grid, hipStream_t s, const Pass1Args& a) {
 #define ZF_P1(NRV, DTV) \
-  hipLaunchKernelGGL((zf_pass1<NRV, DTV, MAT, NORM, zf::kQuadsPerUnr * U>), grid, dim3(kThreads), 0, s, a)
+  hipLaunchKernelGGL((zf_pass1<NRV, DTV, OUT, NORM, zf::kQuadsPerUnr * U>), grid, dim3(kThreads), 0, s, a)
 #define ZF_P1_DT(NRV) \
   do { if (dt == ZF_BF16) ZF_P1(NRV, ZF_BF16); else ZF_P1(NRV, ZF_F16); } while (0)
   switch (nr) {
@@ -790,12 +805,12 @@ void launch_pass1_u(int nr, int32_t dt, dim3 grid, hipStream_t s, const Pass1Arg
 #undef ZF_P1
 }
 
-template <bool MAT, bool NORM>
+template <int OUT, bool NORM>
 int launch_pass1(const zf_plan* plan, int32_t dt, hipStream_t s, const Pass1Args& a) {
   const dim3 grid((uint32_t)plan->pass1_tiles);
   const int nr = plan->summary.n_ranks;
-  if (plan->unr1 == 2) launch_pass1_u<MAT, NORM, 2>(nr, dt, grid, s, a);
-  else launch_pass1_u<MAT, NORM, 1>(nr, dt, grid, s, a);
+  if (plan->unr1 == 2) launch_pass1_u<OUT, NORM, 2>(nr, dt, grid, s, a);
+  else launch_pass1_u<OUT, NORM, 1>(nr, dt, grid, s, a);
   return hip_ok(hipGetLastError()) ? ZF_OK : ZF_EHIP;
 }
 
@@ -900,7 +915,7 @@ extern "C" int zf_state_init(void* d_state, double loss_scale, int32_t dynamic,
 }
 
 int zf::step_enqueue(const zf_plan* plan, const zf_hparams* hp, const zf_step_args* args,
-                     void* stream, bool update) {
+                     void* stream, bool update, bool down16) {
   if (!valid_plan(plan) || !hp || !args) return ZF_EINVAL;
   const zf_plan_summary& sm = plan->summary;
   if (args->grads_reduced != 0 && args->grads_reduced != 1) return ZF_EINVAL;
@@ -924,6 +939,7 @@ int zf::step_enqueue(const zf_plan* plan, const zf_hparams* hp, const zf_step_ar
     if (!aligned16(bufs[i])) return ZF_EALIGN;
   }
   if (!update && !args->grad_shards) return ZF_EINVAL;
+  if (down16 && (update || reduced)) return ZF_EINVAL;
   if (args->params && !aligned16(args->params)) return ZF_EALIGN;
   if (args->grad_shards && !aligned16(args->grad_shards)) return ZF_EALIGN;
   if (sm.policy == 2 && !args->grad_shards) return ZF_EINVAL;
@@ -950,6 +966,7 @@ int zf::step_enqueue(const zf_plan* plan, const zf_hparams* hp, const zf_step_ar
   a1.g = gp;
   a1.n = sm.psi_pad;
   a1.rs = rs;
+  a1.rs16 = down16 ? reinterpret_cast<uint16_t*>(args->grad_shards) : nullptr;
   a1.partials = partials;
   a1.nr = nr;
   a1.tile_map = plan->pass1_map;
@@ -961,8 +978,9 @@ int zf::step_enqueue(const zf_plan* plan, const zf_hparams* hp, const zf_step_ar
       hipLaunchKernelGGL(zf_pass1_reduced<zf::kQuadsPerUnr>, grid, dim3(kThreads), 0, s, a1);
     rc = hip_ok(hipGetLastError()) ? ZF_OK : ZF_EHIP;
   } else {
-    rc = mat ? launch_pass1<true, true>(plan, args->grad_dtype, s, a1)
-             : launch_pass1<false, true>(plan, args->grad_dtype, s, a1);
+    if (down16) rc = launch_pass1<2, true>(plan, args->grad_dtype, s, a1);
+    else if (mat) rc = launch_pass1<1, true>(plan, args->grad_dtype, s, a1);
+    else rc = launch_pass1<0, true>(plan, args->grad_dtype, s, a1);
   }
   if (rc != ZF_OK) return rc;
   if ((rc = record(args->phase_events, 1, s)) != ZF_OK) return rc;
@@ -1017,7 +1035,7 @@ int zf::step_enqueue(const zf_plan* plan, const zf_hparams* hp, const zf_step_ar
 
 extern "C" int zf_shard_step(const zf_plan* plan, const zf_hparams* hp,
                              const zf_step_args* args, void* stream) {
-  return zf::step_enqueue(plan, hp, args, stream, true);
+  return zf::step_enqueue(plan, hp, args, stream, true, false);
 }
 
 extern "C" int zf_reduce_scatter(const zf_plan* plan, int32_t grad_dtype,
@@ -1038,7 +1056,8 @@ extern "C" int zf_reduce_scatter(const zf_plan* plan, int32_t grad_dtype,
   a1.nr = plan->summary.n_ranks;
   a1.tile_map = plan->pass1_map;
   (void)hipGetLastError();
-  return launch_pass1<true, false>(plan, grad_dtype, static_cast<hipStream_t>(stream), a1);
+  a1.rs16 = nullptr;
+  return launch_pass1<1, false>(plan, grad_dtype, static_cast<hipStream_t>(stream), a1);
 }
 
 extern "C" int zf_bucket_reduce_scatter(const zf_plan* plan, int64_t group, int32_t grad_dtype,

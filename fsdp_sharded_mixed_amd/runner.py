@@ -173,7 +173,7 @@ class DeviceRun:
                 self.workspace, self.state, self.h_state, self.h_grad, self.master,
                 self.exp_avg, self.exp_avg_sq, self.h_params, stream=stream,
                 grads_reduced=reduced, n_threads=self.n_threads, n_chunks=self.n_chunks,
-                phase_events=phase_events)
+                phase_events=phase_events, down16=self.w.offload_down16)
             return
         zf.shard_step(self.plan, self.hp, self.w.grad_dtype, self.w.param_dtype,
                       None if reduced else self.grads, self.master, self.exp_avg,

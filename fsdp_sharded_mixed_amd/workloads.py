@@ -102,6 +102,9 @@ class Workload:
     # ZeRO-Offload: fp32 master / moments and the update on the host
     # (CPU-Adam), 16-bit parameters on the GPU
     offload: bool = False
+    # ZeRO-Offload with 16-bit gradients down (the sums rounded to the
+    # gradient dtype; norm and overflow on the rounded values)
+    offload_down16: bool = False
     extra: dict = field(default_factory=dict)
 
     @property
@@ -273,6 +276,16 @@ def llama654m_offload() -> Workload:
     return w
 
 
+def llama654m_offload16() -> Workload:
+    """The offload workload with the pages' 16-bit gradient edge: the
+    reduce-scatter sums go down PCIe rounded to bf16 (2 B per parameter)."""
+    w = llama654m_offload()
+    w.name = "llama-654m-n2-offload16"
+    w.description = w.description.replace("ZeRO-Offload:", "ZeRO-Offload with bf16 sums down:")
+    w.offload_down16, w.seed = True, 9
+    return w
+
+
 ALL = {
     "tiny": tiny,
     "llama-73m-n8": llama73m,
@@ -283,6 +296,7 @@ ALL = {
     "llama-654m-n2-buckets-a4": llama654m_buckets,
     "llama-654m-n2-nosync-a4": lambda: llama654m_buckets(ACCUM_NO_SYNC),
     "llama-654m-n2-offload": llama654m_offload,
+    "llama-654m-n2-offload16": llama654m_offload16,
 }
 
 

@@ -79,7 +79,7 @@ class CpuAdamArgs(C.Structure):
     _fields_ = [("n", C.c_int64), ("grad", C.c_void_p), ("master", C.c_void_p),
                 ("exp_avg", C.c_void_p), ("exp_avg_sq", C.c_void_p), ("params", C.c_void_p),
                 ("param_dtype", C.c_int32), ("n_threads", C.c_int32), ("gs", C.c_float),
-                ("bc1", C.c_float), ("bc2", C.c_float), ("reserved", C.c_int32)]
+                ("bc1", C.c_float), ("bc2", C.c_float), ("grad_dtype", C.c_int32)]
 
 
 class OffloadArgs(C.Structure):
@@ -90,7 +90,7 @@ class OffloadArgs(C.Structure):
                 ("h_grad", C.c_void_p), ("h_master", C.c_void_p), ("h_exp_avg", C.c_void_p),
                 ("h_exp_avg_sq", C.c_void_p), ("h_params", C.c_void_p),
                 ("grads_reduced", C.c_int32), ("n_threads", C.c_int32),
-                ("n_chunks", C.c_int32), ("reserved", C.c_int32),
+                ("n_chunks", C.c_int32), ("down16", C.c_int32),
                 ("phase_events", C.POINTER(C.c_void_p))]
 
 
@@ -350,8 +350,9 @@ def read_result(state, stream=None):
 
 
 def cpu_adam(hp, grad, master, exp_avg, exp_avg_sq, gs, bc1, bc2, params=None,
-             param_dtype=BF16, n_threads=0, n=None):
-    """zf_cpu_adam on host arrays (numpy arrays, CPU tensors or addresses)."""
+             param_dtype=BF16, n_threads=0, n=None, grad_dtype=F32):
+    """zf_cpu_adam on host arrays (numpy arrays, CPU tensors or addresses);
+    grad_dtype F32, or F16 / BF16 for 16-bit gradient sums."""
     def addr(x):
         if x is None or isinstance(x, int):
             return x
@@ -362,14 +363,14 @@ def cpu_adam(hp, grad, master, exp_avg, exp_avg_sq, gs, bc1, bc2, params=None,
         n = len(master)
     a = CpuAdamArgs(int(n), addr(grad), addr(master), addr(exp_avg), addr(exp_avg_sq),
                     addr(params), int(param_dtype), int(n_threads), float(gs), float(bc1),
-                    float(bc2), 0)
+                    float(bc2), int(grad_dtype))
     _check(lib.zf_cpu_adam(C.byref(hp), C.byref(a)), "zf_cpu_adam")
 
 
 def offload_step(plan, hp, grad_dtype, param_dtype, grads, grad_shards, params, workspace,
                  state, h_state, h_grad, h_master, h_exp_avg, h_exp_avg_sq, h_params,
                  stream=None, grads_reduced=False, n_threads=0, n_chunks=8, numel=None,
-                 phase_events=None):
+                 phase_events=None, down16=False):
     """zf_offload_step; device tensors for grads/grad_shards/params/workspace/
     state, host (pinned) tensors for the h_ arrays; phase_events: None or 4
     raw hipEvent_t handles.  Returns the StepResult."""
@@ -382,7 +383,7 @@ def offload_step(plan, hp, grad_dtype, param_dtype, grads, grad_shards, params, 
                     int(numel), _ptr(workspace), _nbytes(workspace, None), _ptr(state),
                     _ptr(h_state), _ptr(h_grad), _ptr(h_master), _ptr(h_exp_avg),
                     _ptr(h_exp_avg_sq), _ptr(h_params), int(bool(grads_reduced)),
-                    int(n_threads), int(n_chunks), 0, ev)
+                    int(n_threads), int(n_chunks), int(bool(down16)), ev)
     out = StepResult()
     _check(lib.zf_offload_step(_handle(plan), C.byref(hp), C.byref(a), _stream(stream),
                                C.byref(out)), "zf_offload_step")

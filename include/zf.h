@@ -383,7 +383,8 @@ int zf_read_result(const void* d_state, zf_step_result* out, void* stream);
 
 typedef struct {
   int64_t n;                /* elements */
-  const float* grad;        /* n fp32 reduced gradient sums, still loss-scaled */
+  const void* grad;         /* n reduced gradient sums, still loss-scaled, of
+                               grad_dtype */
   float* master;            /* n fp32, updated in place */
   float* exp_avg;           /* n fp32 */
   float* exp_avg_sq;        /* n fp32 */
@@ -391,7 +392,9 @@ typedef struct {
   int32_t param_dtype;      /* ZF_F16 or ZF_BF16 (when params is given) */
   int32_t n_threads;        /* worker threads; <= 0: every hardware thread */
   float gs, bc1, bc2;       /* the step's scalars, from zf_step_result */
-  int32_t reserved;         /* must be 0 */
+  int32_t grad_dtype;       /* 0 or ZF_F32: binary32 sums (4-byte aligned);
+                               ZF_F16 / ZF_BF16: 16-bit sums (2-byte aligned),
+                               widened exactly */
 } zf_cpu_adam_args;
 
 /* CPU-Adam ([L13] 7.2: a SIMD, multithreaded Adam on the CPU): the same
@@ -427,7 +430,15 @@ typedef struct {
   int32_t grads_reduced;      /* as zf_step_args */
   int32_t n_threads;          /* CPU-Adam threads (<= 0: every hardware thread) */
   int32_t n_chunks;           /* pipeline chunks, 1 .. 4096 */
-  int32_t reserved;           /* must be 0 */
+  int32_t down16;             /* 0: the fp32 sums go down (4 B per element;
+                                 the result equals zf_shard_step's bit for
+                                 bit).  1: the sums are rounded to the
+                                 gradient dtype on the GPU and go down in 16
+                                 bits (2 B per element, the pages' fp16
+                                 gradient edge); the overflow check and the
+                                 norm are taken on the rounded values, as
+                                 the host would see them.  1 needs
+                                 grads_reduced = 0. */
   void* const* phase_events;  /* NULL, or 4 hipEvent_t recorded on `stream`:
                                  before pass 1, after the finish kernel, after
                                  the last download, after the last upload */
@@ -446,7 +457,8 @@ typedef struct {
  * The uploads run on a library-owned stream per device (created on first
  * use, kept until the process ends), so both PCIe directions are busy at
  * once.  Blocks until the step is complete and fills *result (may be
- * NULL).  The state and parameters equal zf_shard_step's bit for bit.
+ * NULL).  With down16 = 0 the state and parameters equal zf_shard_step's
+ * bit for bit; with down16 = 1 they follow the 16-bit gradients.
  * Calls that overlap on one device must not share host buffers.  Errors:
  * ZF_EINVAL, ZF_EALIGN, ZF_EDTYPE, ZF_ESIZE, ZF_EHIP, ZF_EUNSUP. */
 int zf_offload_step(const zf_plan* plan, const zf_hparams* hp, const zf_offload_args* args,

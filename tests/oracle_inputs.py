@@ -182,6 +182,14 @@ class OracleRun:
             grads = replicas(self.w, self.units, self.psi_pad, self.step_no, self.st.loss_scale)
             if self.w.inject_step == self.step_no:
                 inject_inf(self.w, self.units, grads)
+        if self.w.offload and self.w.offload_down16:
+            # the sums rounded to the gradient dtype, then the step from them
+            w = self.w
+            acc = O.reduce_scatter(w.grad_dtype, w.n_ranks, self.units, grads)
+            acc = [O.widen(w.grad_dtype, O.narrow(w.grad_dtype, a)) for a in acc]
+            return O.step_reduced(w.param_dtype, w.n_ranks, self.units, w.stage, acc,
+                                  self.master, self.m, self.v, self.full, self.shards, self.hp,
+                                  self.st)
         if self.w.fp32_params:
             return O.fsdp2_step(self.w.grad_dtype, self.w.n_ranks, self.units, grads,
                                 self.master, self.m, self.v, self.grad_shards, self.hp, self.st)

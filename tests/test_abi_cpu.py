@@ -257,13 +257,14 @@ def test_step_argument_errors_enqueue_nothing(zf):
         d = dict(grad_dtype=1, param_dtype=1, grads=grads, grad_shards=ok, params=ok, numel=100,
                  workspace=ok, workspace_size=need, state=ok, h_state=ok, h_grad=ok,
                  h_master=ok, h_exp_avg=ok, h_exp_avg_sq=ok, h_params=ok, grads_reduced=0,
-                 n_threads=1, n_chunks=2, reserved=0, phase_events=None)
+                 n_threads=1, n_chunks=2, down16=0, phase_events=None)
         d.update(kw)
         a = Z.OffloadArgs(*[d[f] for f, _ in Z.OffloadArgs._fields_])
         return Z.lib.zf_offload_step(plan.handle, C.byref(hp), C.byref(a), None, None)
     assert off(n_chunks=0) == -1
     assert off(n_chunks=5000) == -1
-    assert off(reserved=2) == -1
+    assert off(down16=2) == -1
+    assert off(down16=1, grads_reduced=1, grads=None) == -1
     assert off(param_dtype=3) == -3
     assert off(h_grad=None) == -1
     assert off(params=None) == -1

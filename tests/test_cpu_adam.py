@@ -126,7 +126,7 @@ def test_argument_errors(zf):
 
     def call(**kw):
         d = dict(n=16, grad=a, master=a, exp_avg=a, exp_avg_sq=a, params=None, param_dtype=2,
-                 n_threads=1, gs=1.0, bc1=0.1, bc2=0.001, reserved=0)
+                 n_threads=1, gs=1.0, bc1=0.1, bc2=0.001, grad_dtype=0)
         d.update(kw)
         args = zf.CpuAdamArgs(*[d[f] for f, _ in zf.CpuAdamArgs._fields_])
         return zf.lib.zf_cpu_adam(C.byref(hp), C.byref(args))
@@ -134,9 +134,35 @@ def test_argument_errors(zf):
     assert call() == 0
     assert call(n=-1) == -1
     assert call(grad=None) == -1
-    assert call(reserved=1) == -1
+    assert call(grad_dtype=5) == -3
+    assert call(grad_dtype=1, grad=a + 2) == 0     # 16-bit sums: 2-byte alignment
+    assert call(grad_dtype=3, grad=a + 2) == -2
     assert call(params=a, param_dtype=3) == -3
     assert call(master=a + 2) == -2
     assert call(params=a + 1, param_dtype=1) == -2
     assert call(n=0, grad=None) == 0
     assert zf.lib.zf_cpu_adam(None, None) == -1
+
+
+@pytest.mark.parametrize("gdt", [W.F16, W.BF16])
+def test_16bit_gradients(zf, gdt):
+    """16-bit gradient sums (the offload step's 16-bit download): the host
+    update equals the oracle's on the exactly widened values."""
+    rng = np.random.default_rng(11)
+    n = 40003
+    acc32, p, m, v = _state(rng, n)
+    g16 = O.narrow(gdt, acc32)
+    acc = O.widen(gdt, g16)
+    acc[~np.isfinite(acc)] = 0.0
+    g16 = O.narrow(gdt, acc)
+    hp = _hp()
+    sc = _scalars(acc, 3, hp)
+    ref = [p.copy(), m.copy(), v.copy()]
+    O.adamw_array(acc, sc, *ref)
+    got = [p.copy(), m.copy(), v.copy()]
+    out = np.empty(n, np.uint16)
+    zf.cpu_adam(_zhp(zf, hp), g16, *got, sc.gs, sc.bc1, sc.bc2, params=out, param_dtype=W.BF16,
+                n_threads=5, grad_dtype=gdt)
+    for g, r in zip(got, ref):
+        assert np.array_equal(_bits(g), _bits(r))
+    assert np.array_equal(out, O.narrow(W.BF16, ref[0]))

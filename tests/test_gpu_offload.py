@@ -120,3 +120,61 @@ def test_offload_against_oracle(R):
         G.assert_state_close("exp_avg_sq", dev.exp_avg_sq.numpy(), vo)
         po = G.oracle_padded_params(orc)
         assert G.ulp16_distance(G.bits16(dev.params), po).max() <= 1
+
+
+@pytest.mark.parametrize("gdt,n", [(W.BF16, 2), (W.F16, 3), (W.BF16, 8)])
+def test_offload16_against_oracle(R, gdt, n):
+    """The 16-bit download (the pages' fp16 gradient edge): the sums are
+    rounded to the gradient dtype on the GPU, the norm and overflow check use
+    the rounded values, CPU-Adam widens them.  Against the oracle doing the
+    same: the downloaded sums bit-exact, state within 4 ulp, params within
+    1 ulp, norm within 1e-5, over five steps (a fp16 loss scale that halves)."""
+    w = wl(n, W.PER_UNIT, [37, 5, 101, 64001, 3, 9000], gdt=gdt, offload_down16=True)
+    dev = R.DeviceRun(w)
+    dev.init_state()
+    orc = OI.OracleRun(w)
+    for k in range(1, 6):
+        scale = orc.st.loss_scale
+        grads = OI.replicas(w, orc.units, orc.psi_pad, k, scale)
+        if k == 3:
+            grads[0][orc.units[3]["O"] + 7] = OI.inf_bits(gdt)
+        dev.fill_grads(k, scale)
+        if k == 3:
+            dev.grads[0].view(torch.int16)[orc.units[3]["O"] + 7] = \
+                int(np.array(OI.inf_bits(gdt), np.uint16).view(np.int16))
+        res_o = orc.step(grads)
+        dev.step()
+        res_d = dev.last_result
+        dev.loss_scale = res_d.scale_next
+        G.assert_result_matches(res_d, res_o, f"step {k}")
+        assert res_d.skipped == (k == 3)
+        if not res_d.skipped:
+            sums = O.reduce_scatter(gdt, n, orc.units, grads)
+            ref16 = OI.rank_shards_to_padded(orc.units, [O.narrow(gdt, a) for a in sums])
+            got16 = dev.h_grad.view(torch.int16)[:orc.psi_pad].numpy().view(np.uint16)
+            assert np.array_equal(got16, ref16)
+        mo, mmo, vo = G.oracle_padded_state(orc)
+        G.assert_state_close("master", dev.master.numpy(), mo)
+        G.assert_state_close("exp_avg", dev.exp_avg.numpy(), mmo)
+        G.assert_state_close("exp_avg_sq", dev.exp_avg_sq.numpy(), vo)
+        assert G.ulp16_distance(G.bits16(dev.params), G.oracle_padded_params(orc)).max() <= 1
+
+
+def test_offload16_overflow_only_in_16_bits(R):
+    """fp16 replicas whose fp32 sum is finite but beyond fp16's range: the
+    plain step applies, the 16-bit download sees +inf and skips (and the
+    dynamic loss scale halves), exactly as the oracle doing the same."""
+    lens = [4096]
+    results = {}
+    for down16 in (False, True):
+        w = wl(2, W.GLOBAL_FLAT, lens, gdt=W.F16, offload_down16=down16)
+        dev = R.DeviceRun(w)
+        dev.init_state()
+        dev.fill_grads(1, w.loss_scale)
+        big = int(np.array(0x7BFF, np.uint16).view(np.int16))  # 65504, the largest fp16
+        for q in range(2):
+            dev.grads[q].view(torch.int16)[10] = big
+        dev.step()
+        results[down16] = dev.last_result
+    assert results[False].skipped == 0
+    assert results[True].skipped == 1 and results[True].scale_next == 512.0
