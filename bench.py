@@ -83,7 +83,8 @@ def backward_kernel_bytes_per_elem(w):
 
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "fsdp_sharded_mixed_amd", "csrc", f)
-                  for f in ("zf_step.hip", "zf_internal.h", "zf_plan.cpp")]
+                  for f in ("zf_step.hip", "zf_backward.hip", "zf_gather.hip", "zf_device.h",
+                            "zf_internal.h", "zf_plan.cpp")]
 COPY_BYTES = 1 << 30  # calibration copy: 1 GiB read + 1 GiB written
 
 

@@ -45,7 +45,8 @@ def _hipcc(out, sources, host_sources=()):
 
 def build():
     """Build both libraries; returns their paths."""
-    zf = _hipcc(LIB_ZF, [os.path.join(CSRC, f) for f in ("zf_step.hip", "zf_offload.hip")],
+    zf = _hipcc(LIB_ZF, [os.path.join(CSRC, f) for f in
+                         ("zf_step.hip", "zf_backward.hip", "zf_gather.hip", "zf_offload.hip")],
                 [os.path.join(CSRC, f) for f in ("zf_plan.cpp", "zf_cpu_adam.cpp")])
     inputs = _hipcc(LIB_INPUTS, [os.path.join(CSRC, "zf_inputs.hip")])
     return zf, inputs
