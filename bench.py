@@ -412,7 +412,9 @@ def offload_line(args, w, dev, ms, wall, copy_gbs):
     s = dev.plan.summary
     alg = algorithmic_bytes_per_param(w) * w.psi
     gbs = alg / (ms * 1e-3) / 1e9
-    p1_bytes = (2 * w.n_ranks + 4) * s.psi_pad
+    # pass 1 reads N 16-bit replicas and writes the sums: fp32, or rounded
+    # to the gradient dtype for a 16-bit download
+    p1_bytes = (2 * w.n_ranks + (2 if w.offload_down16 else 4)) * s.psi_pad
     p1_gbs = p1_bytes / (red * 1e-3) / 1e9
     return {
         "metric": "ZeRO step GB/s (algorithmic bytes) and % of HBM peak; params updated/s",
