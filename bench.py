@@ -455,6 +455,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the second timing of the K steps replayed from a HIP graph")
+    ap.add_argument("--graph-steps", type=int, default=10,
+                    help="steps captured per graph (1 when it does not divide --steps)")
     ap.add_argument("--no-skip-probe", action="store_true",
                     help="do not time skipped steps (profiled runs: keeps every launch of "
                          "the step kernels an applied step's)")
@@ -575,6 +579,28 @@ def main():
     fin = sum(r[1].elapsed_time(r[2]) for r in evs) / args.steps
     p2 = sum(r[2].elapsed_time(r[3]) for r in evs) / args.steps
 
+    # the same K steps replayed from a HIP graph of G steps (the step only
+    # enqueues kernels, so it captures whole; t and the loss scale advance on
+    # the device from one replay to the next)
+    graph_ms = None
+    if not args.no_graph:
+        gsteps = args.graph_steps if args.steps % args.graph_steps == 0 else 1
+        graph = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            for _ in range(gsteps):
+                one_step()
+        graph.replay()
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(args.steps // gsteps):
+            graph.replay()
+        end.record()
+        torch.cuda.synchronize()
+        graph_ms = start.elapsed_time(end) / args.steps
+        assert dev.result().skipped == 0
+        del graph
+
     s = dev.plan.summary
     materialized = s.policy != 0
     alg = algorithmic_bytes_per_param(w) * w.psi
@@ -632,6 +658,10 @@ def main():
         "kernels_ms": kernels,
         "roofline": roof,
     }
+    if graph_ms is not None:
+        line["graph_replay"] = {"steps_per_graph": gsteps, "ms_per_step": round(graph_ms, 5),
+                                "value": round(alg / (graph_ms * 1e-3) / 1e9, 2),
+                                "params_updated_per_s": round(w.psi / (graph_ms * 1e-3), 1)}
     if overrides:
         line["config"]["overrides"] = overrides
     if args.per_step_log:
