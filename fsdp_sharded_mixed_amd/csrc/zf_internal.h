@@ -30,8 +30,17 @@ constexpr uint64_t kPlanMagic = 0x7a665f706c616e31ull;  // "zf_plan1"
 //    pass walks its tiles forward: walking them backward so that the newest
 //    sums might still be in the 256 MB Infinity Cache saved 2% of the update
 //    pass only with temporal stores, which cost pass 1 10% (73M, N = 8).
+//  - occupancy: the update pass runs at most 2 blocks (8 waves) per CU:
+//    73M -8%, 654M -3%, 2.1B FSDP2 -10% against the register-limited 8
+//    blocks; 1 block per CU is slower again (+10% at 73M).  Pass 1 runs at
+//    most 4 blocks per CU when it streams 8 or more replicas and writes the
+//    sums (-3% at 73M, N = 8); with 2 replicas, read-only or writing, it
+//    needs every block it can get (a cap of 4 costs +13% to +90%).
+//    The cap is dynamic LDS that the kernel never touches, sized so that no
+//    more blocks fit in a CU's 160 KiB.
 // Builds may pin a choice for measurement: ZF_FORCE_UNR1, ZF_FORCE_UNR2 (1|2),
-// ZF_FORCE_MAP1 (0|1), ZF_PASS1_NT_LOADS (0|1).
+// ZF_FORCE_MAP1 (0|1), ZF_PASS1_NT_LOADS (0|1), ZF_FORCE_OCC1, ZF_FORCE_OCC2
+// (blocks per CU, 0: no cap).
 #ifndef ZF_PASS1_NT_LOADS
 #define ZF_PASS1_NT_LOADS 1
 #endif
@@ -66,6 +75,33 @@ inline int unr_pass2(int n_ranks, int64_t psi_pad, bool materialize) {
 #endif
 }
 constexpr int kMaxLevel2Blocks = 1024;
+
+// Resident-block caps (blocks per CU, 0: none) and the dynamic LDS per block
+// that enforces one: k blocks fit in the CU's LDS, k + 1 do not (the margin
+// covers the kernels' own few hundred bytes of static LDS).
+constexpr int64_t kLdsPerCU = 160 * 1024;
+inline int occ_pass1(int n_ranks, bool writes_sums) {
+#ifdef ZF_FORCE_OCC1
+  (void)n_ranks;
+  (void)writes_sums;
+  return ZF_FORCE_OCC1;
+#else
+  return (writes_sums && n_ranks >= 8) ? 4 : 0;
+#endif
+}
+inline int occ_pass2() {
+#ifdef ZF_FORCE_OCC2
+  return ZF_FORCE_OCC2;
+#else
+  return 2;
+#endif
+}
+inline uint32_t occupancy_lds(int blocks_per_cu) {
+  if (blocks_per_cu <= 0) return 0;
+  return (uint32_t)(kLdsPerCU / (blocks_per_cu + 1) + 1024);
+}
+static_assert(kLdsPerCU / (kLdsPerCU / 3 + 1024) == 2, "two blocks per CU");
+static_assert(kLdsPerCU / (kLdsPerCU / 5 + 1024) == 4, "four blocks per CU");
 
 // The device state block (the caller's zf_state_bytes() buffer), also read
 // on the host by the offload step.

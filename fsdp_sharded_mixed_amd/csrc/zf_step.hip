@@ -61,6 +61,10 @@ struct Pass1Args {
 // offloaded optimizer receives).
 template <int NR, int DT, int OUT, bool NORM, int Q>
 __global__ __launch_bounds__(kThreads) void zf_pass1(Pass1Args a) {
+  // the occupancy cap: dynamic LDS (see occupancy_lds) that no lane touches
+  // (n is never negative)
+  extern __shared__ uint32_t zf_occupancy_lds[];
+  if (a.n < 0) zf_occupancy_lds[threadIdx.x] = 0u;
   const int nr = NR > 0 ? NR : a.nr;
   const int64_t nq = a.n / kQuad;
   const int64_t tile = tile_of_block(a.tile_map);
@@ -273,6 +277,10 @@ __device__ __forceinline__ void adamw1(const Coef& c, float acc, float& p, float
 
 template <int NR, int GDT, int PDT, bool MAT, int Q, bool OUT16>
 __global__ __launch_bounds__(kThreads) void zf_pass2(Pass2Args a) {
+  // the occupancy cap: dynamic LDS (see occupancy_lds) that no lane touches
+  // (n is never negative)
+  extern __shared__ uint32_t zf_occupancy_lds[];
+  if (a.n < 0) zf_occupancy_lds[threadIdx.x] = 0u;
   if (a.st->skipped) return;  // the whole grid leaves at once
   Coef c;
   c.gs = a.st->gs;
@@ -366,9 +374,11 @@ __global__ void zf_state_init_kernel(DevState* s, double S, int32_t dynamic, int
 // Host side.
 
 template <int OUT, bool NORM, int U>
-void launch_pass1_u(int nr, int32_t dt, dim3 grid, hipStream_t s, const Pass1Args& a) {
+void launch_pass1_u(int nr, int32_t dt, dim3 grid, uint32_t lds, hipStream_t s,
+                    const Pass1Args& a) {
 #define ZF_P1(NRV, DTV) \
-  hipLaunchKernelGGL((zf_pass1<NRV, DTV, OUT, NORM, zf::kQuadsPerUnr * U>), grid, dim3(kThreads), 0, s, a)
+  hipLaunchKernelGGL((zf_pass1<NRV, DTV, OUT, NORM, zf::kQuadsPerUnr * U>), grid, dim3(kThreads), \
+                     lds, s, a)
 #define ZF_P1_DT(NRV) \
   do { if (dt == ZF_BF16) ZF_P1(NRV, ZF_BF16); else ZF_P1(NRV, ZF_F16); } while (0)
   switch (nr) {
@@ -390,20 +400,22 @@ template <int OUT, bool NORM>
 int launch_pass1(const zf_plan* plan, int32_t dt, hipStream_t s, const Pass1Args& a) {
   const dim3 grid((uint32_t)plan->pass1_tiles);
   const int nr = plan->summary.n_ranks;
-  if (plan->unr1 == 2) launch_pass1_u<OUT, NORM, 2>(nr, dt, grid, s, a);
-  else launch_pass1_u<OUT, NORM, 1>(nr, dt, grid, s, a);
+  const uint32_t lds = zf::occupancy_lds(zf::occ_pass1(nr, OUT != 0));
+  if (plan->unr1 == 2) launch_pass1_u<OUT, NORM, 2>(nr, dt, grid, lds, s, a);
+  else launch_pass1_u<OUT, NORM, 1>(nr, dt, grid, lds, s, a);
   return hip_ok(hipGetLastError()) ? ZF_OK : ZF_EHIP;
 }
 
 template <int GDT, int PDT, int U, bool OUT16>
 void launch_pass2_nr(int nr, bool mat, dim3 grid, hipStream_t s, const Pass2Args& a) {
   constexpr int Q = zf::kQuadsPerUnr * U;
+  const uint32_t lds = zf::occupancy_lds(zf::occ_pass2());
   if (mat) {
-    hipLaunchKernelGGL((zf_pass2<0, GDT, PDT, true, Q, OUT16>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((zf_pass2<0, GDT, PDT, true, Q, OUT16>), grid, dim3(kThreads), lds, s, a);
     return;
   }
 #define ZF_P2(NRV) \
-  hipLaunchKernelGGL((zf_pass2<NRV, GDT, PDT, false, Q, OUT16>), grid, dim3(kThreads), 0, s, a)
+  hipLaunchKernelGGL((zf_pass2<NRV, GDT, PDT, false, Q, OUT16>), grid, dim3(kThreads), lds, s, a)
   switch (nr) {
     case 1: ZF_P2(1); break;
     case 2: ZF_P2(2); break;
