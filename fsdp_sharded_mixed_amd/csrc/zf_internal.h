@@ -23,9 +23,10 @@ constexpr uint64_t kPlanMagic = 0x7a665f706c616e31ull;  // "zf_plan1"
 //    4: -5%); at N = 8 that walk costs +4%, so many replicas keep one
 //    shared window.  One 2-quad step per thread for N <= 2 (-6% at 4.06B),
 //    two steps otherwise;
-//  - the update pass uses plain loads; two 2-quad steps per thread on large
-//    recomputing plans, one otherwise (within 1% either way); its tiles
-//    walk in block order (the XCD-contiguous walk costs +3% there);
+//  - the update pass uses plain loads and one 2-quad step per thread (with
+//    the occupancy cap below, two steps cost +5% at 4.06B, +6% at 73M and
+//    +9% for FSDP2 2.1B); its tiles walk in block order (the
+//    XCD-contiguous walk costs +3% there);
 //  - the materialised sums go out with non-temporal stores and the update
 //    pass walks its tiles forward: walking them backward so that the newest
 //    sums might still be in the 256 MB Infinity Cache saved 2% of the update
@@ -47,7 +48,6 @@ constexpr uint64_t kPlanMagic = 0x7a665f706c616e31ull;  // "zf_plan1"
 
 constexpr int kThreads = 256;        // 4 wave64 per block
 constexpr int kQuadsPerUnr = 2;      // quads (4 elements) per thread per tile step
-constexpr int64_t kBigPlan = int64_t(1) << 27;  // padded elements
 inline int unr_pass1(int n_ranks) {
 #ifdef ZF_FORCE_UNR1
   (void)n_ranks;
@@ -66,12 +66,12 @@ inline int map_pass1(int n_ranks) {
 }
 inline int unr_pass2(int n_ranks, int64_t psi_pad, bool materialize) {
   (void)n_ranks;
-#ifdef ZF_FORCE_UNR2
   (void)psi_pad;
   (void)materialize;
+#ifdef ZF_FORCE_UNR2
   return ZF_FORCE_UNR2;
 #else
-  return (!materialize && psi_pad >= kBigPlan) ? 2 : 1;
+  return 1;
 #endif
 }
 constexpr int kMaxLevel2Blocks = 1024;
