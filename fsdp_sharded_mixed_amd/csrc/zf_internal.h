@@ -34,9 +34,13 @@ constexpr uint64_t kPlanMagic = 0x7a665f706c616e31ull;  // "zf_plan1"
 //  - occupancy: the update pass runs at most 2 blocks (8 waves) per CU:
 //    73M -8%, 654M -3%, 2.1B FSDP2 -10% against the register-limited 8
 //    blocks; 1 block per CU is slower again (+10% at 73M).  Pass 1 runs at
-//    most 4 blocks per CU when it streams 8 or more replicas and writes the
-//    sums (-3% at 73M, N = 8); with 2 replicas, read-only or writing, it
-//    needs every block it can get (a cap of 4 costs +13% to +90%).
+//    most 3 blocks per CU when it streams 6 or more replicas and writes the
+//    sums (73M at N = 6 and N = 8: -2% to -3% against no cap or a cap of
+//    4); with 2 replicas, read-only or writing, it needs every block it can
+//    get (a cap of 4 costs +13% to +90%).
+//  - pass 1 splits full tiles from the last one: a full tile's loads carry
+//    no range check and issue back to back (-2% at N = 8; the update pass
+//    measured within 1% either way and keeps one code path).
 //    The cap is dynamic LDS that the kernel never touches, sized so that no
 //    more blocks fit in a CU's 160 KiB.
 // Builds may pin a choice for measurement: ZF_FORCE_UNR1, ZF_FORCE_UNR2 (1|2),
@@ -86,7 +90,7 @@ inline int occ_pass1(int n_ranks, bool writes_sums) {
   (void)writes_sums;
   return ZF_FORCE_OCC1;
 #else
-  return (writes_sums && n_ranks >= 8) ? 4 : 0;
+  return (writes_sums && n_ranks >= 6) ? 3 : 0;
 #endif
 }
 inline int occ_pass2() {

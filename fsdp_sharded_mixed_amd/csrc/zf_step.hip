@@ -59,27 +59,22 @@ struct Pass1Args {
 // rounded to the gradient dtype and stored in 16 bits, and the overflow flag
 // and the norm are taken on the rounded values (the 16-bit gradients an
 // offloaded optimizer receives).
-template <int NR, int DT, int OUT, bool NORM, int Q>
-__global__ __launch_bounds__(kThreads) void zf_pass1(Pass1Args a) {
-  // the occupancy cap: dynamic LDS (see occupancy_lds) that no lane touches
-  // (n is never negative)
-  extern __shared__ uint32_t zf_occupancy_lds[];
-  if (a.n < 0) zf_occupancy_lds[threadIdx.x] = 0u;
-  const int nr = NR > 0 ? NR : a.nr;
-  const int64_t nq = a.n / kQuad;
-  const int64_t tile = tile_of_block(a.tile_map);
-  const int64_t q0 = tile * kThreads * Q + threadIdx.x;
+//
+// The quads of one tile.  FULL: every quad of the tile lies below nq (all
+// tiles but the last), so no load or store carries a range check: the loads
+// issue back to back instead of one predicated branch each.
+template <int NR, int DT, int OUT, bool NORM, int Q, bool FULL>
+__device__ __forceinline__ void pass1_quads(const Pass1Args& a, int nr, int64_t nq, int64_t q0,
+                                            double& ss, uint32_t& bad) {
   int64_t qi[Q];
   bool ok[Q];
 #pragma unroll
   for (int h = 0; h < Q; ++h) {
     qi[h] = q0 + (int64_t)h * kThreads;
-    ok[h] = qi[h] < nq;
+    ok[h] = FULL || qi[h] < nq;
   }
   f32x4 acc[Q];
   sum_quads<NR, DT, ZF_PASS1_NT_LOADS != 0, Q>(a.g, nr, qi, ok, acc);
-  double ss = 0.0;
-  uint32_t bad = 0;
 #pragma unroll
   for (int h = 0; h < Q; ++h) {
     if (!ok[h]) continue;
@@ -97,6 +92,24 @@ __global__ __launch_bounds__(kThreads) void zf_pass1(Pass1Args a) {
       }
     }
   }
+}
+
+template <int NR, int DT, int OUT, bool NORM, int Q>
+__global__ __launch_bounds__(kThreads) void zf_pass1(Pass1Args a) {
+  // the occupancy cap: dynamic LDS (see occupancy_lds) that no lane touches
+  // (n is never negative)
+  extern __shared__ uint32_t zf_occupancy_lds[];
+  if (a.n < 0) zf_occupancy_lds[threadIdx.x] = 0u;
+  const int nr = NR > 0 ? NR : a.nr;
+  const int64_t nq = a.n / kQuad;
+  const int64_t tile = tile_of_block(a.tile_map);
+  const int64_t q0 = tile * kThreads * Q + threadIdx.x;
+  double ss = 0.0;
+  uint32_t bad = 0;
+  if ((tile + 1) * kThreads * Q <= nq)
+    pass1_quads<NR, DT, OUT, NORM, Q, true>(a, nr, nq, q0, ss, bad);
+  else
+    pass1_quads<NR, DT, OUT, NORM, Q, false>(a, nr, nq, q0, ss, bad);
   const int64_t tail0 = nq * kQuad;
   if (tile == gridDim.x - 1 && (int64_t)threadIdx.x < a.n - tail0) {
     const int64_t p = tail0 + threadIdx.x;
