@@ -63,8 +63,11 @@ __global__ __launch_bounds__(kThreads) void zf_gather_kernel(GatherArgs a) {
 // FSDP2 unshard: cast each parameter's fp32 shards (padded-flat [O_u,
 // O_u + L_u): the N ranks' chunks side by side, padding rows excluded) to
 // 16 bits into the group buffer at the parameter's unpadded offset.
-// blockIdx.y = parameter of this launch; blockIdx.x = 2048-element tile.
+// One block per 2048-element tile; the launch's parameters own consecutive
+// runs of tiles (parameter k: tiles [first_tile[k], first_tile[k+1])), so
+// a short parameter costs no idle blocks beside a long one.
 constexpr int kCastMax = 32;  // parameters per launch
+constexpr int64_t kCastTile = (int64_t)kThreads * 8;
 struct CastEntry {
   int64_t src;  // O_u in the fp32 array
   int64_t dst;  // offset in the group buffer
@@ -74,12 +77,17 @@ struct CastArgs {
   const float* master;
   uint16_t* out;
   CastEntry e[kCastMax];
+  int64_t first_tile[kCastMax];  // nondecreasing; INT64_MAX past the last parameter
 };
 
 template <int DT>
 __global__ __launch_bounds__(kThreads) void zf_gather_cast_kernel(CastArgs a) {
-  const CastEntry e = a.e[blockIdx.y];
-  const int64_t t0 = (int64_t)blockIdx.x * kThreads * 8;
+  const int64_t b = blockIdx.x;
+  int k = 0;  // the block's parameter: how many later parameters start at or before b
+#pragma unroll
+  for (int j = 1; j < kCastMax; ++j) k += a.first_tile[j] <= b ? 1 : 0;
+  const CastEntry e = a.e[k];
+  const int64_t t0 = (b - a.first_tile[k]) * kCastTile;
   if (t0 >= e.len) return;
   const float* src = a.master + e.src;
   uint16_t* dst = a.out + e.dst;
@@ -249,6 +257,13 @@ extern "C" int zf_gather_cast(const zf_plan* plan, int64_t group, int32_t dtype,
   if (!aligned16(master) || (reinterpret_cast<uintptr_t>(out) & 1u) != 0) return ZF_EALIGN;
   const zf_group_info& g = plan->groups[group];
   if (master_numel < plan->summary.psi_pad || out_numel < g.numel) return ZF_ESIZE;
+  // every launch's tiles fit one grid dimension (checked before any launch)
+  for (int64_t first = 0; first < g.n_units; first += kCastMax) {
+    int64_t tiles = 0;
+    for (int64_t k = first; k < g.n_units && k < first + kCastMax; ++k)
+      tiles += (plan->units[g.first_unit + k].L + kCastTile - 1) / kCastTile;
+    if (tiles > 0x7FFFFFFF) return ZF_ESIZE;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   int64_t dst = 0;
@@ -256,18 +271,24 @@ extern "C" int zf_gather_cast(const zf_plan* plan, int64_t group, int32_t dtype,
     CastArgs a;
     a.master = master;
     a.out = static_cast<uint16_t*>(out);
-    int64_t count = g.n_units - first, max_len = 0;
+    int64_t count = g.n_units - first, tiles = 0;
     if (count > kCastMax) count = kCastMax;
-    for (int64_t k = 0; k < count; ++k) {
+    for (int64_t k = 0; k < kCastMax; ++k) {
+      if (k >= count) {
+        a.e[k] = CastEntry{0, 0, 0};
+        a.first_tile[k] = INT64_MAX;
+        continue;
+      }
       const zf_unit_info& u = plan->units[g.first_unit + first + k];
       a.e[k].src = u.O;
       a.e[k].dst = dst;
       a.e[k].len = u.L;
+      a.first_tile[k] = tiles;
       dst += u.L;
-      if (u.L > max_len) max_len = u.L;
+      tiles += (u.L + kCastTile - 1) / kCastTile;
     }
-    const int64_t bx = (max_len + kThreads * 8 - 1) / (kThreads * 8);
-    const dim3 grid((uint32_t)(bx < 1 ? 1 : bx), (uint32_t)count);
+    if (tiles < 1) tiles = 1;  // only empty parameters: one block that finds nothing to do
+    const dim3 grid((uint32_t)tiles);
     if (dtype == ZF_BF16)
       hipLaunchKernelGGL(zf_gather_cast_kernel<ZF_BF16>, grid, dim3(kThreads), 0, s, a);
     else
