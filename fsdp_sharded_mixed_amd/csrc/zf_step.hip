@@ -136,7 +136,8 @@ __global__ __launch_bounds__(kThreads) void zf_pass1(Pass1Args a) {
 
 // Pass 1 over gradients that are already reduced (and accumulated): the
 // fp32 gradient shards are only read, for the overflow flag and the
-// squared-norm partials, over the same tiles as zf_pass1.
+// squared-norm partials, over the same tiles as zf_pass1.  Non-temporal
+// loads, as in zf_pass1 (654M bucketed: -14% against plain loads).
 template <int Q>
 __global__ __launch_bounds__(kThreads) void zf_pass1_reduced(Pass1Args a) {
   const int64_t nq = a.n / kQuad;
@@ -148,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void zf_pass1_reduced(Pass1Args a) {
   for (int h = 0; h < Q; ++h) {
     const int64_t q = q0 + (int64_t)h * kThreads;
     ok[h] = q < nq;
-    acc[h] = ok[h] ? ldq32(a.rs, q) : (f32x4){0, 0, 0, 0};
+    acc[h] = ok[h] ? ldq32<true>(a.rs, q) : (f32x4){0, 0, 0, 0};
   }
   double ss = 0.0;
   uint32_t bad = 0;
