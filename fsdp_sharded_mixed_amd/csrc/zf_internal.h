@@ -23,10 +23,13 @@ constexpr uint64_t kPlanMagic = 0x7a665f706c616e31ull;  // "zf_plan1"
 //    4: -5%); at N = 8 that walk costs +4%, so many replicas keep one
 //    shared window.  One 2-quad step per thread for N <= 2 (-6% at 4.06B),
 //    two steps otherwise;
-//  - the update pass uses plain loads and one 2-quad step per thread (with
-//    the occupancy cap below, two steps cost +5% at 4.06B, +6% at 73M and
-//    +9% for FSDP2 2.1B); its tiles walk in block order (the
-//    XCD-contiguous walk costs +3% there);
+//  - the update pass reads master, m and v with the non-temporal hint (under
+//    the occupancy cap: 73M -4%, 654M -7%, 4.06B -2%, FSDP2 2.1B -2%; before
+//    the cap the same hint had cost +15%) and the materialised sums with
+//    plain loads (the hint there: neutral at 73M, +6% for FSDP2); it runs
+//    one 2-quad step per thread (under the occupancy cap two steps cost +5%
+//    at 4.06B, +6% at 73M and +9% for FSDP2 2.1B); its tiles walk in block
+//    order (the XCD-contiguous walk costs +3% there);
 //  - the materialised sums go out with non-temporal stores and the update
 //    pass walks its tiles forward: walking them backward so that the newest
 //    sums might still be in the 256 MB Infinity Cache saved 2% of the update

@@ -323,9 +323,9 @@ __global__ __launch_bounds__(kThreads) void zf_pass2(Pass2Args a) {
 #pragma unroll
   for (int h = 0; h < Q; ++h) {
     if (ok[h]) {
-      p[h] = ldq32(a.master, qi[h]);
-      m[h] = ldq32(a.m, qi[h]);
-      v[h] = ldq32(a.v, qi[h]);
+      p[h] = ldq32<true>(a.master, qi[h]);
+      m[h] = ldq32<true>(a.m, qi[h]);
+      v[h] = ldq32<true>(a.v, qi[h]);
     }
   }
 #pragma unroll
