@@ -485,7 +485,7 @@ def main():
                       args.summarize_pmc[2], args.command)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the step runs on one GPU; --gpus {args.gpus} is not supported "
               "(N data-parallel ranks are emulated on a single device)", file=sys.stderr)
         sys.exit(2)
 
