@@ -1,0 +1,88 @@
+"""The bench's contract and byte accounting, on the CPU (no GPU call).
+
+* `bench.py --gpus N` with N > 1 exits with status 2 and says why (one GPU;
+  the N ranks are emulated on it), before touching a device.
+* Algorithmic bytes per parameter: the step reads each rank's 16-bit
+  gradient replica once (2N), reads and writes the fp32 master, exp_avg
+  and exp_avg_sq (12 + 12) and writes the 16-bit parameter (2); a ZeRO-3
+  unit gather reads and writes 16-bit values once more (4).  The backward
+  side and FSDP2 add their own terms.  The expected values below are
+  written out per workload, and the counter summaries measured the same
+  bytes per parameter per kernel (the update pass's 30, the bucket launches'
+  44, the no_sync launches' 72 + 12).
+* Counter traffic is reported only while the summaries were taken on the
+  current kernel code.
+"""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bench
+from fsdp_sharded_mixed_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+@pytest.mark.parametrize("name,expected", [
+    ("tiny", 2 * 4 + 26),                  # N = 4, stage 2
+    ("llama-73m-n8", 2 * 8 + 26),          # 42
+    ("llama-654m-n2", 2 * 2 + 26),         # 30
+    ("llama-2.1b-n2-zero3", 2 * 2 + 30),   # stage 3: + unit gather
+    ("llama-4.06b-n2", 2 * 2 + 26),        # 30
+    # FSDP2: replicas in, fp32 gradient shard out and back, state in and
+    # out, then the cast-gather reads fp32 and writes 16 bits
+    ("llama-2.1b-n2-fsdp2", 4 + 4 + 4 + 24 + 6),
+    # 4 micro-batches, each bucket reduced every micro-batch: 4 x 2N read,
+    # 4 shard writes, 3 shard reads; then the norm pass and the update pass
+    # read the shard (4 + 4), the state (24), and the 16-bit param (2)
+    ("llama-654m-n2-buckets-a4", (4 * 4 + 4 * 4 + 3 * 4) + 4 + 4 + 24 + 2),
+    # no_sync: 4 x 2N replica reads, 4 x N fp32 main_grad writes, 3 x N
+    # main_grad reads, one reduction reading N main_grads and writing the
+    # shard; then the same step
+    ("llama-654m-n2-nosync-a4", (4 * 4 + 4 * 4 * 2 + 3 * 4 * 2 + 4 * 2 + 4) + 4 + 4 + 24 + 2),
+])
+def test_algorithmic_bytes(name, expected):
+    assert bench.algorithmic_bytes_per_param(W.get(name)) == expected
+
+
+def test_kernel_bytes_match_counter_figures():
+    """The per-element figures the roofline uses for each launch."""
+    assert bench.update_kernel_bytes_per_elem(W.get("llama-73m-n8"), True) == 30
+    assert bench.update_kernel_bytes_per_elem(W.get("llama-4.06b-n2"), False) == 30
+    assert bench.update_kernel_bytes_per_elem(W.get("llama-2.1b-n2-fsdp2"), True) == 28
+    assert bench.backward_kernel_bytes_per_elem(W.get("llama-654m-n2-buckets-a4")) == 44
+    assert bench.backward_kernel_bytes_per_elem(W.get("llama-654m-n2-nosync-a4")) == 72 + 12
+
+
+def test_kernel_hash_ignores_comments_only(tmp_path, monkeypatch):
+    src = tmp_path / "k.hip"
+    src.write_text("int f(int x) { return x + 1; }  // add one\n")
+    monkeypatch.setattr(bench, "KERNEL_SOURCES", [str(src)])
+    h0 = bench.kernel_source_hash()
+    src.write_text("/* a comment */\nint f(int x)   {\n  return x + 1;  // one more\n}\n")
+    assert bench.kernel_source_hash() == h0
+    src.write_text("int f(int x) { return x + 2; }\n")
+    assert bench.kernel_source_hash() != h0
+
+
+def test_traffic_only_for_current_code(tmp_path, monkeypatch):
+    summary = {"workload": "llama-73m-n8", "kernel_source_sha256_16": "0123456789abcdef",
+               "zf_pass2": {"launches_per_step": 1.0, "hbm_bytes_per_launch": 123.0,
+                            "hbm_bytes_per_step": 123.0, "per_param_per_step": 30.0}}
+    (tmp_path / "zf_step_llama-73m-n8_traffic.json").write_text(json.dumps(summary))
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0123456789abcdef")
+    assert bench.traffic_for("llama-73m-n8") == 123.0
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "fedcba9876543210")
+    assert bench.traffic_for("llama-73m-n8") is None
+    assert bench.traffic_for("no-such-workload") is None
