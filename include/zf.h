@@ -51,6 +51,16 @@
  *     reported as ZF_EHIP (the stream may then hold part of the step).
  *   - An overflow (skipped step) is a result, not an error.
  *   - No call aborts or throws.
+ *   - HIP graphs: zf_shard_step, zf_reduce_scatter, zf_gather,
+ *     zf_gather_cast, zf_bucket_reduce_scatter, zf_accumulate and
+ *     zf_state_init enqueue kernels only (no memset, copy, allocation or
+ *     synchronisation; every pointer travels by value in the kernel
+ *     arguments), so a caller may capture them on a stream and replay the
+ *     graph.  The state block carries t, the loss scale and the skip
+ *     decision from one replay to the next.  The hyperparameters (and every
+ *     pointer) are those of the capture, so a learning-rate schedule needs a
+ *     new capture.  zf_read_result and zf_offload_step synchronise and
+ *     cannot be captured.
  *
  * Device data layout (the padded flat index p):
  *   A plan's units are laid end to end, unit u at offset O_u with P_u =
