@@ -100,6 +100,22 @@ MUTANTS = [
     ("reshard places later ranks one element early",
      "memcpy(dst, logical + (ub[u].lam + e) * elem_bytes, (size_t)elem_bytes);",
      "memcpy(dst, logical + (ub[u].lam + e - (r > 0)) * elem_bytes, (size_t)elem_bytes);"),
+    ("first moment decays with beta2",
+     "float mm = sc->b1 * m[i] + sc->c1 * g;", "float mm = sc->b2 * m[i] + sc->c1 * g;"),
+    ("gradient neither unscaled nor clipped",
+     "float g = acc[i] * sc->gs;", "float g = acc[i];"),
+    ("clip coefficient not capped at 1",
+     "if (coef > 1.0) coef = 1.0;", "if (coef > 2.0) coef = 1.0;"),
+    ("dynamic loss scale never grows",
+     "st->loss_scale = S * 2.0;", "st->loss_scale = S;"),
+    ("growth counter kept after the scale doubles",
+     "    st->loss_scale = S * 2.0;\n    st->growth_ctr = 0;",
+     "    st->loss_scale = S * 2.0;"),
+    ("weight decay not scaled by the learning rate",
+     "sc->dec = (float)(1.0 - hp->lr * hp->weight_decay);",
+     "sc->dec = (float)(1.0 - hp->weight_decay);"),
+    ("bias correction uses beta^t instead of 1 - beta^t",
+     "sc->bc1 = (float)(1.0 - B1);", "sc->bc1 = (float)B1;"),
     ("ring traffic without the (N-1)/N factor",
      "return passes * ((double)(n_ranks - 1) / (double)n_ranks) * 2.0 * (double)psi_pad;",
      "return passes * 2.0 * (double)psi_pad;"),

@@ -895,6 +895,13 @@ def test_clipped_gradient_norm(orc):
         hp.max_norm = 0.0
         sc0, res0 = O.finish(ss, 0, n, hp, OI.scale_state(w))
         assert res0.coef == 1.0 and sc0.gs == np.float32(1.0 / (w.loss_scale * n))
+        # clipping never scales up (torch's clip_grad_norm_ clamps its
+        # coefficient at 1): with max_norm between the norm and twice it,
+        # the factor is still the plain 1/(S*N)
+        for ratio in (1.01, 1.6, 1.99):
+            hp.max_norm = ratio * res.norm
+            sc1, res1 = O.finish(ss, 0, n, hp, OI.scale_state(w))
+            assert res1.coef == 1.0 and sc1.gs == sc0.gs
 
 
 # ------------------------------------------------------------- resharding ----
