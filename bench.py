@@ -34,6 +34,17 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, vendor figure
 DEFAULT_WORKLOAD = "llama-73m-n8"
 
 
+def formats(w):
+    """The workload's storage formats.  The path computes in binary32 (the
+    reduce-scatter sums and AdamW), with the squared norm accumulated in
+    binary64; gradients and parameters are stored in 16 bits."""
+    from fsdp_sharded_mixed_amd import workloads as W
+    name = {W.BF16: "bf16", W.F16: "f16"}
+    return {"grad_dtype": name[w.grad_dtype],
+            "param_dtype": "f32" if w.fp32_params else name[w.param_dtype],
+            "state_dtype": "f32", "norm_accumulate": "f64"}
+
+
 def backward_bytes_per_param(w):
     """Bytes of the backward-side reduction per parameter per step, over its
     n_micro micro-batches (A): every micro-batch reads the N 16-bit replicas
@@ -421,11 +432,11 @@ def offload_line(args, w, dev, ms, wall, copy_gbs):
         "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32 state, " + ("bf16" if w.grad_dtype == W.BF16 else "f16") + " grads",
+        "dtype": "f32",
         "data": "synthetic (seeded splitmix64/Irwin-Hall normal grads and master init, "
                 "random-init weights)",
         "config": {"workload": w.name, "psi": w.psi, "psi_padded": s.psi_pad,
-                   "virtual_ranks": w.n_ranks, "zero_stage": w.stage,
+                   "virtual_ranks": w.n_ranks, "zero_stage": w.stage, **formats(w),
                    "offload": "fp32 state + CPU-Adam on the host, "
                               + ("16-bit" if w.offload_down16 else "fp32") + " sums down",
                    "cpu_adam_threads": threads, "pipeline_chunks": dev.n_chunks},
@@ -643,11 +654,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32 state, " + ("bf16" if w.grad_dtype == W.BF16 else "f16") + " grads",
+        "dtype": "f32",
         "data": "synthetic (seeded splitmix64/Irwin-Hall normal grads and master init, "
                 "random-init weights)",
         "config": {"workload": w.name, "psi": w.psi, "psi_padded": s.psi_pad,
-                   "virtual_ranks": w.n_ranks, "zero_stage": w.stage,
+                   "virtual_ranks": w.n_ranks, "zero_stage": w.stage, **formats(w),
                    "layout": ["global flat", "per-unit FlatParameter",
                               "per-parameter dim-0 (FSDP2)"][w.layout],
                    "rs_policy": ["recompute", "materialize", "fp32 grad shard"][s.policy]},

@@ -86,3 +86,13 @@ def test_traffic_only_for_current_code(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "fedcba9876543210")
     assert bench.traffic_for("llama-73m-n8") is None
     assert bench.traffic_for("no-such-workload") is None
+
+
+def test_formats_in_config():
+    """The line's dtype is the arithmetic type (binary32); the storage
+    formats go into config."""
+    assert bench.formats(W.get("llama-73m-n8")) == {
+        "grad_dtype": "bf16", "param_dtype": "bf16", "state_dtype": "f32",
+        "norm_accumulate": "f64"}
+    assert bench.formats(W.get("llama-4.06b-n2"))["grad_dtype"] == "f16"
+    assert bench.formats(W.get("llama-2.1b-n2-fsdp2"))["param_dtype"] == "f32"
