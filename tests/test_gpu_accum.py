@@ -184,6 +184,38 @@ def test_bucket_order_and_second_stream(R):
     assert torch.equal(ref.view(torch.int32), dev.grad_shards.view(torch.int32))
 
 
+def test_buckets_on_two_concurrent_streams(R):
+    """Even buckets on one stream, odd buckets on another, both in flight at
+    once, over two accumulating micro-batches: the same shards bit for bit
+    as one stream in order."""
+    from fsdp_sharded_mixed_amd import zf
+    w = bucketed(4, [5003, 77, 20000, 1, 3333, 9000, 12, 4096], bucket=3000, n_micro=2)
+    dev = R.DeviceRun(w)
+    dev.init_state()
+    ng = len(dev.plan.groups)
+    assert ng >= 4
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    out = []
+    for split in (False, True):
+        dev.grad_shards.fill_(float("nan"))  # every bucket must overwrite it
+        for micro in range(2):
+            dev.fill_grads(1, 1.0, micro=micro)
+            ready = torch.cuda.Event()
+            ready.record()
+            for s in streams:
+                s.wait_event(ready)
+            for g in range(ng):
+                s = streams[g % 2] if split else streams[0]
+                zf.bucket_reduce_scatter(dev.plan, g, w.grad_dtype, dev.grads,
+                                         dev.grad_shards, micro > 0, stream=s)
+            for s in streams:
+                torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        out.append(dev.grad_shards.clone())
+    assert not torch.isnan(out[0]).any()
+    assert torch.equal(out[0].view(torch.int32), out[1].view(torch.int32))
+
+
 def test_fsdp2_accumulation(R):
     """FSDP2 with torchtitan's default accumulation: every FSDP unit
     reduce-scattered each micro-batch into the fp32 gradient shards
