@@ -188,7 +188,8 @@ def _csv_rows(directory, suffix):
 
 
 def summarize_trace(directory, out, command):
-    """Text summary of a rocprofv3 --kernel-trace --stats run."""
+    """Text summary of a rocprofv3 --kernel-trace --stats run (with the roctx
+    ranges' host times when the run also had --marker-trace and --roctx)."""
     rows = _csv_rows(directory, "kernel_stats.csv")
     lines = [f"command: {command}", "",
              f"{'kernel':<70} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}"]
@@ -198,6 +199,15 @@ def summarize_trace(directory, out, command):
         lines.append(f"{name:<70} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>10.2f} "
                      f"{float(r['MinNs']) / 1e3:>10.2f} {float(r['MaxNs']) / 1e3:>10.2f} "
                      f"{float(r['Percentage']):>6.2f}")
+    import glob
+    if glob.glob(os.path.join(directory, "**", "*marker_api_stats.csv"), recursive=True):
+        lines += ["", "roctx ranges (host time from push to pop; the enqueue waits once the "
+                      "launch queue is full, so it follows the device's pace):",
+                  f"{'range':<70} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10}"]
+        for r in _csv_rows(directory, "marker_api_stats.csv"):
+            lines.append(f"{r['Name']:<70} {int(r['Calls']):>6} "
+                         f"{float(r['AverageNs']) / 1e3:>10.2f} {float(r['MinNs']) / 1e3:>10.2f} "
+                         f"{float(r['MaxNs']) / 1e3:>10.2f}")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -468,6 +478,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the second timing of the K steps replayed from a HIP graph")
+    ap.add_argument("--roctx", action="store_true",
+                    help="roctx ranges around backward, step and gathers (rocprofv3 "
+                         "--marker-trace)")
     ap.add_argument("--graph-steps", type=int, default=10,
                     help="steps captured per graph (1 when it does not divide --steps)")
     ap.add_argument("--no-skip-probe", action="store_true",
@@ -501,8 +514,10 @@ def main():
         sys.exit(2)
 
     import torch
-    from fsdp_sharded_mixed_amd import runner, workloads as W
+    from fsdp_sharded_mixed_amd import runner, trace, workloads as W
 
+    if args.roctx:
+        trace.enable()
     w = W.get(args.workload)
     overrides = apply_overrides(w, args.set)
     torch.cuda.set_device(0)
@@ -537,9 +552,12 @@ def main():
         if w.backward_rs:
             if backward_event is not None:
                 backward_event.record()
-            dev.backward_all()
-        dev.step(phase_events=phase_events)
-        dev.gather_all()
+            with trace.span("backward buckets"):
+                dev.backward_all()
+        with trace.span("step"):
+            dev.step(phase_events=phase_events)
+        with trace.span("gathers"):
+            dev.gather_all()
 
     for _ in range(args.warmup):
         one_step()

@@ -96,3 +96,22 @@ def test_formats_in_config():
         "norm_accumulate": "f64"}
     assert bench.formats(W.get("llama-4.06b-n2"))["grad_dtype"] == "f16"
     assert bench.formats(W.get("llama-2.1b-n2-fsdp2"))["param_dtype"] == "f32"
+
+
+def test_roctx_spans():
+    """Ranges are no-ops until enabled; enabled, they push and pop through
+    the roctx library (no profiler attached: the calls just return)."""
+    from fsdp_sharded_mixed_amd import trace
+    with trace.span("off"):
+        pass
+    if not os.path.exists(os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "lib",
+                                       "librocprofiler-sdk-roctx.so")):
+        pytest.skip("no roctx library in this ROCm")
+    trace.enable()
+    try:
+        with trace.span("outer"):
+            with trace.span("inner"):
+                pass
+        assert trace.enabled()
+    finally:
+        trace._lib = None
