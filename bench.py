@@ -14,12 +14,21 @@ same batch (the state evolves).
 
 Prints one JSON line:
   value        algorithmic GB/s = (2N + 26) B per parameter (+ 4 for the
-               ZeRO-3 unit gathers) x Psi / step time
-  roofline     the dominant kernel (the fused update pass): its algorithmic
-               bytes per launch / its mean duration from HIP events recorded
-               around it on its stream, against 8 TB/s
+               ZeRO-3 unit gathers; FSDP2, backward-side and offload terms in
+               algorithmic_bytes_per_param) x Psi / step time
+  dtype        the arithmetic type (f32; the norm accumulates in f64); the
+               gradient, parameter and state formats are in config
+  roofline     the dominant kernel (the fused update pass, or the bucket
+               launches when they move more): its algorithmic bytes per
+               launch / its mean duration from HIP events recorded around it
+               on its stream, against 8 TB/s; traffic = counted HBM bytes
+               per launch from the committed counter summaries of the same
+               kernel code (null otherwise)
+  graph_replay the same K steps replayed from a HIP graph of --graph-steps
+               captured steps
   cpu_baseline the single-threaded CPU oracle on a bounded slice of the
                same workload (rank 0, one GPU only)
+--roctx adds named host ranges for rocprofv3 --marker-trace.
 """
 import argparse
 import json
