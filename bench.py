@@ -483,7 +483,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    from fsdp_sharded_mixed_amd import workloads as _W
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(_W.ALL),
+                    help=f"default {DEFAULT_WORKLOAD}")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the second timing of the K steps replayed from a HIP graph")
