@@ -84,16 +84,26 @@ def test_layout_workload_units(orc):
 
 
 # ---------------------------------------------------------------- ledger ----
+def _golden_rows(name, kind):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return [l.split()[1:] for l in f
+                if l.strip() and not l.startswith("#") and l.split()[0] == kind]
+
+
+L13_STATES = "l13_model_state_bytes.txt"
+
+
 def test_ledger_simulator_table(orc):
     """[L13] 3.5 and exercise 5, the simulator's 5-layer MLP (Psi = 32,656,
-    units [3168, 9312, 9312, 9312, 1552], N = 4): 16 -> 7 -> 5.5 -> 4 bytes per
-    parameter; ZeRO-3 steady 130,624 B and peak 161,632 B, the peak being
-    16,328 + 97,968 + 10,088 + 37,248."""
+    units [3168, 9312, 9312, 9312, 1552], N = 4): bytes per parameter per
+    stage and the ZeRO-3 steady and peak bytes, as printed (golden file);
+    the peak is 16,328 + 97,968 + 10,088 + 37,248."""
     units, psi, _ = O.layout([3168, 9312, 9312, 9312, 1552], [0, 1, 2, 3, 4], 4, O.PER_UNIT)
-    got = [O.ledger(units, 4, s)[0] for s in range(4)]
-    assert got == [16 * psi, 7 * psi, int(5.5 * psi), 4 * psi]
-    assert got[3] == 130624
-    assert O.ledger(units, 4, 3)[1] == 161632 == 16328 + 97968 + 10088 + 37248
+    for stage, per_param in _golden_rows(L13_STATES, "sim"):
+        assert O.ledger(units, 4, int(stage))[0] == float(per_param) * psi
+    (steady, peak), = _golden_rows(L13_STATES, "sim3")
+    assert O.ledger(units, 4, 3)[0] == int(steady)
+    assert O.ledger(units, 4, 3)[1] == int(peak) == 16328 + 97968 + 10088 + 37248
 
 
 def _gb(units, n, s):
@@ -101,27 +111,27 @@ def _gb(units, n, s):
 
 
 def test_ledger_paper_examples(orc):
-    """[L13] 2.4 (ZeRO table 1) and exercise 1: 7.5B on 64 GPUs 120 / 31.4 /
-    16.6 / 1.88 GB; 1T on 1024 GPUs 15.6 GB at stage 3; 13B on 64 GPUs 208 /
-    54.4 / 28.8 / 3.25 GB."""
-    u75, _, _ = O.layout([7_500_000_000], [0], 64, O.GLOBAL_FLAT)
-    assert [round(_gb(u75, 64, s), 2) for s in range(4)] == [120.0, 31.41, 16.64, 1.88]
-    u1t, _, _ = O.layout([1_000_000_000_000], [0], 1024, O.GLOBAL_FLAT)
-    assert round(_gb(u1t, 1024, 3), 1) == 15.6
-    u13, _, _ = O.layout([13_000_000_000], [0], 64, O.GLOBAL_FLAT)
-    assert [round(_gb(u13, 64, s), 1) for s in range(3)] == [208.0, 54.4, 28.8]
-    assert _gb(u13, 64, 3) == 3.25
+    """[L13] 2.4 (ZeRO table 1) and exercise 1: 7.5B on 64 GPUs, 1T on 1024
+    GPUs at stage 3, 13B on 64 GPUs -- every printed GB figure (golden file)
+    equals the ledger rounded to the printed digits."""
+    rows = _golden_rows(L13_STATES, "gb")
+    assert len(rows) == 9
+    for params, n, stage, printed, digits in rows:
+        u, _, _ = O.layout([int(params)], [0], int(n), O.GLOBAL_FLAT)
+        assert round(_gb(u, int(n), int(stage)), int(digits)) == float(printed), (params, stage)
 
 
 def test_ledger_largest_model_table2(orc):
     """[L13] 2.5 (ZeRO table 2): the largest model whose states fit 32 GB at
-    64-way data parallelism is 2B / 7.6B / 14.4B / 128B for stages 0-3, and
-    2T at stage 3 with 16-way model parallelism on 1024 GPUs (64-way DP)."""
+    64-way data parallelism, per stage (golden file), and 2T at stage 3 with
+    16-way model parallelism on 1024 GPUs (64-way DP)."""
     probe = 64 * 10**9
     u, _, _ = O.layout([probe], [0], 64, O.GLOBAL_FLAT)
     per_param = [O.ledger(u, 64, s)[0] / probe for s in range(4)]
-    biggest = [32e9 / b / 1e9 for b in per_param]
-    assert [round(x, 1) for x in biggest] == [2.0, 7.6, 14.4, 128.0]
+    rows = _golden_rows(L13_STATES, "fit")
+    assert len(rows) == 4
+    for stage, billions in rows:
+        assert round(32e9 / per_param[int(stage)] / 1e9, 1) == float(billions)
     assert round(16 * 32e9 / per_param[3] / 1e12, 1) == 2.0
 
 
