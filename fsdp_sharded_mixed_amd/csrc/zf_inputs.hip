@@ -175,3 +175,52 @@ extern "C" int zfi_stream_probe(const float* const* src, int32_t n_src, float* c
   }
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
+
+// ---------------------------------------------------------------------------
+// Lowering probes: binary32 square root and division as this compiler emits
+// them under the step library's flags (correctly rounded divide and sqrt,
+// no contraction), for tests that compare them with IEEE results.
+namespace {
+
+__global__ __launch_bounds__(256) void sqrt_probe(float* out, int64_t n, uint32_t first) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x; k < n; k += stride)
+    out[k] = sqrtf(__uint_as_float(first + (uint32_t)k));
+}
+
+__global__ __launch_bounds__(256) void div_probe(const float* a, const float* b, float* out,
+                                                 int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x; k < n; k += stride)
+    out[k] = a[k] / b[k];
+}
+
+uint32_t probe_blocks(int64_t n) {
+  const int64_t b = (n + 255) / 256;
+  return (uint32_t)(b < 8192 ? (b < 1 ? 1 : b) : 8192);
+}
+
+}  // namespace
+
+extern "C" int zfi_sqrt_probe(float* out, int64_t n, uint32_t first_bits, void* stream_handle) {
+  if (!out || n < 0 || n > (int64_t)0x100000000LL - (int64_t)first_bits) return -1;
+  if (reinterpret_cast<uintptr_t>(out) & 3u) return -1;
+  if (n == 0) return 0;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(sqrt_probe, dim3(probe_blocks(n)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream_handle), out, n, first_bits);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+extern "C" int zfi_div_probe(const float* a, const float* b, float* out, int64_t n,
+                             void* stream_handle) {
+  if (!a || !b || !out || n < 0) return -1;
+  const uintptr_t mis = reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b) |
+                        reinterpret_cast<uintptr_t>(out);
+  if (mis & 3u) return -1;
+  if (n == 0) return 0;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(div_probe, dim3(probe_blocks(n)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream_handle), a, b, out, n);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}

@@ -28,6 +28,10 @@ def _load():
                                      C.c_int32, C.c_int64, C.c_void_p]
     lib.zfi_stream_output.restype = C.c_uint64
     lib.zfi_stream_output.argtypes = [C.c_uint64, C.c_uint64, C.c_uint64]
+    lib.zfi_sqrt_probe.restype = C.c_int
+    lib.zfi_sqrt_probe.argtypes = [C.c_void_p, C.c_int64, C.c_uint32, C.c_void_p]
+    lib.zfi_div_probe.restype = C.c_int
+    lib.zfi_div_probe.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p]
     return lib
 
 
@@ -77,3 +81,19 @@ def stream_probe(srcs, dsts, n=None, stream=None):
     rc = lib.zfi_stream_probe(sp, len(srcs), dp, len(dsts), int(n), _stream(stream))
     if rc != 0:
         raise RuntimeError(f"zfi_stream_probe failed ({rc})")
+
+
+def sqrt_probe(out, first_bits, n=None, stream=None):
+    """zfi_sqrt_probe: out[i] = sqrtf of the binary32 with bits first_bits + i."""
+    n = out.numel() if n is None else n
+    rc = lib.zfi_sqrt_probe(out.data_ptr(), int(n), int(first_bits), _stream(stream))
+    if rc != 0:
+        raise RuntimeError(f"zfi_sqrt_probe failed ({rc})")
+
+
+def div_probe(a, b, out, stream=None):
+    """zfi_div_probe: out = a / b, elementwise, binary32."""
+    n = min(a.numel(), b.numel(), out.numel())
+    rc = lib.zfi_div_probe(a.data_ptr(), b.data_ptr(), out.data_ptr(), int(n), _stream(stream))
+    if rc != 0:
+        raise RuntimeError(f"zfi_div_probe failed ({rc})")

@@ -51,6 +51,16 @@ uint64_t zfi_stream_output(uint64_t seed, uint64_t stream, uint64_t j);
 int zfi_stream_probe(const float* const* src, int32_t n_src, float* const* dst, int32_t n_dst,
                      int64_t n, void* stream_handle);
 
+/* Lowering probes for tests (no arithmetic of the step): binary32 sqrt and
+ * division exactly as this compiler emits them under the step library's
+ * flags (-fhip-fp32-correctly-rounded-divide-sqrt, -ffp-contract=off).
+ * zfi_sqrt_probe: out[i] = sqrtf(x) for the binary32 x whose bits are
+ * first_bits + i, i < n, n <= 2^32 - first_bits.  zfi_div_probe: out[i] =
+ * a[i] / b[i], i < n.  Device pointers, 4-byte aligned.  Returns 0, -1
+ * (bad argument) or -5. */
+int zfi_sqrt_probe(float* out, int64_t n, uint32_t first_bits, void* stream_handle);
+int zfi_div_probe(const float* a, const float* b, float* out, int64_t n, void* stream_handle);
+
 #ifdef __cplusplus
 }
 #endif
