@@ -388,3 +388,43 @@ def test_rs_pair_sweep(R, dtype):
         assert np.array_equal(np.isnan(got), nan)
         assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
     assert n == (1 << 16) * 512
+
+
+@pytest.mark.parametrize("dtype", [W.BF16, W.F16])
+def test_rank_order_on_device(R, dtype):
+    """Floating-point addition is not associative ([L13] 3.4, condition 2):
+    three replicas holding a large value, a small one and the large value's
+    negation, in every order, at every element position of several tiles.
+    The device sums in rank order exactly as the oracle does, so the small
+    value survives only when the large ones cancel first."""
+    from fsdp_sharded_mixed_amd import zf
+    if dtype == W.BF16:
+        big, small_v, nbig, small_f = 0x4B80, 0x3F80, 0xCB80, 1.0        # 2^24, 1, -2^24
+    else:
+        big, small_v, nbig, small_f = 0x7BFF, 0x0001, 0xFBFF, 2.0 ** -24  # 65504, 2^-24
+    import itertools
+    orders = list(itertools.permutations([big, small_v, nbig]))
+    n = 6 * 5003  # every order at every residue mod 4 and across tiles, ragged end
+    reps = [np.empty(n, np.uint16) for _ in range(3)]
+    for i in range(n):
+        o = orders[i % 6]
+        for q in range(3):
+            reps[q][i] = o[q]
+    w = small(3, W.GLOBAL_FLAT, [n], gdt=dtype)
+    plan = R.plan_workload(w)
+    tdt = torch.float16 if dtype == W.F16 else torch.bfloat16
+    dev_g = [torch.from_numpy(np.concatenate([x, np.zeros(plan.summary.psi_pad - n, np.uint16)])
+                              .view(np.int16)).cuda().view(tdt) for x in reps]
+    out = torch.empty(plan.summary.psi_pad, dtype=torch.float32, device="cuda")
+    zf.reduce_scatter(plan, dtype, dev_g, out)
+    got = G.f32(out)[:n]
+    # each order's sum by its definition: binary32 additions left to right
+    widen = (lambda h: np.float32(np.array([h], np.uint16).view(np.float16)[0])) \
+        if dtype == W.F16 else (lambda h: np.array([h << 16], np.uint32).view(np.float32)[0])
+    want = np.array([(widen(o[0]) + widen(o[1])) + widen(o[2]) for o in orders], np.float32)
+    assert set(want.tolist()) == {0.0, small_f}  # the order decides
+    assert np.array_equal(got, np.tile(want, n // 6))
+    units, _, psi_pad = OI.plan(w)
+    ref = OI.rank_shards_to_padded(units, O.reduce_scatter(
+        dtype, 3, units, [G.bits16(g) for g in dev_g]))
+    assert np.array_equal(G.f32(out).view(np.uint32), ref.view(np.uint32))
