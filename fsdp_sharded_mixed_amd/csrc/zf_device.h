@@ -31,6 +31,7 @@ struct GradPtrs {
 // non-temporal stores go out as full lines.
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 constexpr int kQuad = 4;
 
 template <bool NT>
@@ -47,6 +48,15 @@ __device__ __forceinline__ f32x4 ldq32(const float* base, int64_t q) {
 }
 __device__ __forceinline__ void stq32_nt(float* base, int64_t q, f32x4 x) {
   __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(base) + q);
+}
+// A plain fp32 quad store, written as two 8-byte halves: a store that does
+// not look like stq32_nt of the same value, so that the compiler never merges
+// the two into one and drops the non-temporal hint (the backend joins the
+// halves into one 16-byte store again).
+__device__ __forceinline__ void stq32_halves(float* base, int64_t q, f32x4 x) {
+  f32x2* p = reinterpret_cast<f32x2*>(base) + 2 * q;
+  p[0] = (f32x2){x.x, x.y};
+  p[1] = (f32x2){x.z, x.w};
 }
 __device__ __forceinline__ void stq16_nt(void* base, int64_t q, u32x2 x) {
   __builtin_nontemporal_store(x, reinterpret_cast<u32x2*>(base) + q);

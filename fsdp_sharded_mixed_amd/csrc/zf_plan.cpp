@@ -153,6 +153,7 @@ extern "C" int zf_plan_flat(const zf_segment* segs, int64_t nseg, int32_t n_rank
   const int64_t nq = s.psi_pad / 4;  // quads; the ragged tail rides on the last tile
   p->unr1 = zf::unr_pass1(n_ranks);
   p->pass1_map = zf::map_pass1(n_ranks);
+  p->cached_sums_quads = zf::cached_sums_quads(s.psi_pad);
   p->unr2 = zf::unr_pass2(n_ranks, s.psi_pad, s.policy != 0);
   const int64_t q1 = (int64_t)zf::kThreads * zf::kQuadsPerUnr * p->unr1;
   const int64_t q2 = (int64_t)zf::kThreads * zf::kQuadsPerUnr * p->unr2;

@@ -48,22 +48,30 @@ using zf::kStateBytes;
 struct Pass1Args {
   GradPtrs g;
   int64_t n;          // Psi'
-  float* rs;          // fp32 sums (OUT == 1) or unused
+  float* rs;          // fp32 sums (OUT == 1, 3) or unused
   uint16_t* rs16;     // 16-bit sums (OUT == 2) or unused
   Partial* partials;  // one per tile (NORM) or unused
   int32_t nr;
   int32_t tile_map;   // see tile_of_block
+  int64_t plain_from; // OUT == 3: full tiles from this quad on store the sums
+                      // cache-allocating (see zf::cached_sums_quads)
 };
 
-// OUT: 0 the sums stay in registers; 1 they are stored in fp32; 2 they are
-// rounded to the gradient dtype and stored in 16 bits, and the overflow flag
-// and the norm are taken on the rounded values (the 16-bit gradients an
-// offloaded optimizer receives).
-//
+// OUT: 0 the sums stay in registers; 1 they are stored in fp32,
+// non-temporal; 3 as 1, but full tiles from quad plain_from on use plain,
+// cache-allocating stores (see zf::cached_sums_quads); 2 they are rounded to
+// the gradient dtype and stored in 16 bits, and the overflow flag and the
+// norm are taken on the rounded values (the 16-bit gradients an offloaded
+// optimizer receives).
+constexpr bool stores_fp32(int out) { return out == 1 || out == 3; }
+
 // The quads of one tile.  FULL: every quad of the tile lies below nq (all
 // tiles but the last), so no load or store carries a range check: the loads
-// issue back to back instead of one predicated branch each.
-template <int NR, int DT, int OUT, bool NORM, int Q, bool FULL>
+// issue back to back instead of one predicated branch each.  PLAIN: the fp32
+// sums go out with plain stores, in another shape than the non-temporal ones
+// (stq32_halves), because the compiler merges two stores of one value to one
+// address into one and drops the non-temporal hint.
+template <int NR, int DT, int OUT, bool NORM, int Q, bool FULL, bool PLAIN>
 __device__ __forceinline__ void pass1_quads(const Pass1Args& a, int nr, int64_t nq, int64_t q0,
                                             double& ss, uint32_t& bad) {
   int64_t qi[Q];
@@ -78,7 +86,8 @@ __device__ __forceinline__ void pass1_quads(const Pass1Args& a, int nr, int64_t 
 #pragma unroll
   for (int h = 0; h < Q; ++h) {
     if (!ok[h]) continue;
-    if constexpr (OUT == 1) stq32_nt(a.rs, qi[h], acc[h]);
+    if constexpr (stores_fp32(OUT) && PLAIN) stq32_halves(a.rs, qi[h], acc[h]);
+    if constexpr (stores_fp32(OUT) && !PLAIN) stq32_nt(a.rs, qi[h], acc[h]);
     if constexpr (OUT == 2) {
       const u32x2 w = (u32x2){pack2<DT>(acc[h].x, acc[h].y), pack2<DT>(acc[h].z, acc[h].w)};
       stq16_nt(a.rs16, qi[h], w);
@@ -94,6 +103,18 @@ __device__ __forceinline__ void pass1_quads(const Pass1Args& a, int nr, int64_t 
   }
 }
 
+// OUT == 3's last tile, which may end inside: one quad at a time, in the
+// same order as pass1_quads.  It runs in one block per launch, and as a loop
+// the compiler cannot fold the full tiles' straight-line code into it.
+template <int NR, int DT, int OUT, bool NORM, int Q>
+__device__ __forceinline__ void pass1_last(const Pass1Args& a, int nr, int64_t nq, int64_t q0,
+                                           double& ss, uint32_t& bad) {
+#pragma unroll 1
+  for (int h = 0; h < Q; ++h)
+    pass1_quads<NR, DT, OUT, NORM, 1, false, false>(a, nr, nq, q0 + (int64_t)h * kThreads, ss,
+                                                     bad);
+}
+
 template <int NR, int DT, int OUT, bool NORM, int Q>
 __global__ __launch_bounds__(kThreads) void zf_pass1(Pass1Args a) {
   // the occupancy cap: dynamic LDS (see occupancy_lds) that no lane touches
@@ -106,15 +127,25 @@ __global__ __launch_bounds__(kThreads) void zf_pass1(Pass1Args a) {
   const int64_t q0 = tile * kThreads * Q + threadIdx.x;
   double ss = 0.0;
   uint32_t bad = 0;
-  if ((tile + 1) * kThreads * Q <= nq)
-    pass1_quads<NR, DT, OUT, NORM, Q, true>(a, nr, nq, q0, ss, bad);
-  else
-    pass1_quads<NR, DT, OUT, NORM, Q, false>(a, nr, nq, q0, ss, bad);
+  const bool full = (tile + 1) * kThreads * Q <= nq;
+  if constexpr (OUT == 3) {
+    if (!full)
+      pass1_last<NR, DT, OUT, NORM, Q>(a, nr, nq, q0, ss, bad);
+    else if (tile * kThreads * Q >= a.plain_from)  // uniform over the block
+      pass1_quads<NR, DT, OUT, NORM, Q, true, true>(a, nr, nq, q0, ss, bad);
+    else
+      pass1_quads<NR, DT, OUT, NORM, Q, true, false>(a, nr, nq, q0, ss, bad);
+  } else {
+    if (full)
+      pass1_quads<NR, DT, OUT, NORM, Q, true, false>(a, nr, nq, q0, ss, bad);
+    else
+      pass1_quads<NR, DT, OUT, NORM, Q, false, false>(a, nr, nq, q0, ss, bad);
+  }
   const int64_t tail0 = nq * kQuad;
   if (tile == gridDim.x - 1 && (int64_t)threadIdx.x < a.n - tail0) {
     const int64_t p = tail0 + threadIdx.x;
     float t = sum1<DT>(a.g, nr, p);
-    if constexpr (OUT == 1) a.rs[p] = t;
+    if constexpr (stores_fp32(OUT)) a.rs[p] = t;
     if constexpr (OUT == 2) {
       const uint16_t q = narrow1<DT>(t);
       a.rs16[p] = q;
@@ -270,6 +301,7 @@ struct Pass2Args {
   int64_t n;
   float dec, b1, c1, b2, c2, lrf, ef;
   int32_t nr;
+  int32_t reverse;  // MAT: 1 if block b takes tile gridDim.x - 1 - b (cached sums first)
 };
 
 struct Coef {
@@ -304,7 +336,8 @@ __global__ __launch_bounds__(kThreads) void zf_pass2(Pass2Args a) {
   c.lrf = a.lrf; c.ef = a.ef;
   const int nr = NR > 0 ? NR : a.nr;
   const int64_t nq = a.n / kQuad;
-  const int64_t tile = blockIdx.x;
+  const int64_t tile =
+      (MAT && a.reverse) ? (int64_t)gridDim.x - 1 - blockIdx.x : (int64_t)blockIdx.x;
   const int64_t q0 = tile * kThreads * Q + threadIdx.x;
   int64_t qi[Q];
   bool ok[Q];
@@ -553,6 +586,10 @@ int zf::step_enqueue(const zf_plan* plan, const zf_hparams* hp, const zf_step_ar
   a1.partials = partials;
   a1.nr = nr;
   a1.tile_map = plan->pass1_map;
+  // sums stored by pass 1 and read back by the update pass: the tail of them
+  // stays in the memory-side cache and the update pass starts there
+  const bool cached = mat && !reduced && !down16 && update && plan->cached_sums_quads > 0;
+  a1.plain_from = cached ? sm.psi_pad / 4 - plan->cached_sums_quads : INT64_MAX;
   if (reduced) {
     const dim3 grid((uint32_t)plan->pass1_tiles);
     if (plan->unr1 == 2)
@@ -562,6 +599,7 @@ int zf::step_enqueue(const zf_plan* plan, const zf_hparams* hp, const zf_step_ar
     rc = hip_ok(hipGetLastError()) ? ZF_OK : ZF_EHIP;
   } else {
     if (down16) rc = launch_pass1<2, true>(plan, args->grad_dtype, s, a1);
+    else if (cached) rc = launch_pass1<3, true>(plan, args->grad_dtype, s, a1);
     else if (mat) rc = launch_pass1<1, true>(plan, args->grad_dtype, s, a1);
     else rc = launch_pass1<0, true>(plan, args->grad_dtype, s, a1);
   }
@@ -608,6 +646,7 @@ int zf::step_enqueue(const zf_plan* plan, const zf_hparams* hp, const zf_step_ar
   a2.lrf = uc.lrf;
   a2.ef = uc.ef;
   a2.nr = nr;
+  a2.reverse = cached ? 1 : 0;
   // with reduced gradients pass 2 reads grad_shards (mat); the gradient
   // dtype then only names an instantiation
   rc = launch_pass2(plan, reduced ? ZF_BF16 : args->grad_dtype, args->param_dtype, mat,
@@ -636,6 +675,7 @@ extern "C" int zf_reduce_scatter(const zf_plan* plan, int32_t grad_dtype,
   a1.n = plan->summary.psi_pad;
   a1.rs = rs_out;
   a1.partials = nullptr;
+  a1.plain_from = INT64_MAX;  // the caller's sums are not read back here
   a1.nr = plan->summary.n_ranks;
   a1.tile_map = plan->pass1_map;
   (void)hipGetLastError();
