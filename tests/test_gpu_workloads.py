@@ -62,7 +62,7 @@ def check_samples(dev, so, pidx, what):
 
 
 def run_workload(R, name, rs_check_step=1):
-    w = W.get(name)
+    w = W.get(name) if isinstance(name, str) else name
     G.say(f"workload {w.name}: Psi={w.psi:,} N={w.n_ranks} stage={w.stage} steps={w.steps}")
     dev = R.DeviceRun(w)
     dev.init_state()
@@ -159,6 +159,26 @@ def test_llama73m_n8(R):
     dev, trace = run_workload(R, "llama-73m-n8")
     assert all(t[1] == 0 for t in trace)
     assert all(abs(t[5] - 3.03) < 0.1 and t[6] < 1.0 for t in trace)
+
+
+def test_materialised_sums_beyond_cache_window(R):
+    """N = 5 over 120M parameters in three ragged FlatParameter units.  The
+    fp32 sums (480 MB) are larger than the size up to which pass 1 keeps a
+    share of them in the Infinity Cache, so every sum goes out non-temporal
+    and the update pass walks its tiles forward: the materialising path that
+    the smaller plans, which all take the cache window, no longer reach.
+    Three steps against the oracle, the reduce-scatter sums checked too."""
+    w = W.Workload(name="flat-120m-n5", description="three ragged units past the cache window",
+                   segments=[W.Segment("a", 50_000_001, 0), W.Segment("b", 40_000_003, 1),
+                             W.Segment("c", 30_000_007, 2)],
+                   n_ranks=5, layout=W.PER_UNIT, stage=2, grad_dtype=W.BF16,
+                   param_dtype=W.BF16, sigma=1e-3, loss_scale=1.0, dynamic=False, lr=1e-4,
+                   steps=3, seed=7)
+    from fsdp_sharded_mixed_amd import zf
+    plan = zf.plan_flat(w.segments, w.n_ranks, w.layout, w.stage)
+    assert plan.summary.psi_pad * 4 > 448 << 20, "the plan must be past the cache window"
+    dev, trace = run_workload(R, w)
+    assert all(t[1] == 0 for t in trace)
 
 
 def test_llama654m_n2(R):
