@@ -652,6 +652,10 @@ def main():
             "traffic": traffic_for(w.name, "zf_pass2"),
             "kernel": "zf_pass2 (fused AdamW" + ("" if w.fp32_params else "+cast+gather") + ")",
             "bytes_per_launch": upd_bytes}
+    if s.cached_sums_bytes and not w.backward_rs:
+        # sums the update pass may read from the Infinity Cache rather than
+        # HBM; `achieved` and the counters count them as HBM bytes
+        roof["cache_window_bytes"] = s.cached_sums_bytes
     kernels = {"pass1_rs_norm": round(p1, 5), "finish": round(fin, 5),
                "pass2_update": round(p2, 5)}
     if w.backward_rs:

@@ -9,6 +9,7 @@
 // DeepSpeed / torchtitan source guide, 五.4) instead shards every parameter
 // along dim 0 like torch.chunk, padding each rank's chunk to ceil(R/N) rows:
 // one shard unit per parameter, padded at row granularity.
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 #include <limits>
@@ -154,6 +155,8 @@ extern "C" int zf_plan_flat(const zf_segment* segs, int64_t nseg, int32_t n_rank
   p->unr1 = zf::unr_pass1(n_ranks);
   p->pass1_map = zf::map_pass1(n_ranks);
   p->cached_sums_quads = zf::cached_sums_quads(s.psi_pad);
+  s.cached_sums_bytes =
+      s.policy != 0 ? std::min(s.psi_pad * 4, p->cached_sums_quads * 16) : 0;
   p->unr2 = zf::unr_pass2(n_ranks, s.psi_pad, s.policy != 0);
   const int64_t q1 = (int64_t)zf::kThreads * zf::kQuadsPerUnr * p->unr1;
   const int64_t q2 = (int64_t)zf::kThreads * zf::kQuadsPerUnr * p->unr2;

@@ -40,7 +40,7 @@ class PlanSummary(C.Structure):
                 ("max_group_numel", C.c_int64), ("n_ranks", C.c_int32), ("layout", C.c_int32),
                 ("stage", C.c_int32), ("policy", C.c_int32), ("workspace_bytes", C.c_int64),
                 ("state_bytes", C.c_int64 * 5), ("stage3_peak_bytes", C.c_int64),
-                ("comm_bytes", C.c_double * 5)]
+                ("comm_bytes", C.c_double * 5), ("cached_sums_bytes", C.c_int64)]
 
 
 class UnitInfo(C.Structure):

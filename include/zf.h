@@ -147,6 +147,13 @@ typedef struct {
    * 4.2): [0] DP all-reduce, [1] stage 1, [2] stage 2, [3] stage 3,
    * [4] the slides' stage 1 (all-reduce of grads + all-gather of params). */
   double comm_bytes[5];
+  /* bytes of the materialised fp32 sums (policy 1 or 2) that pass 1 stores
+   * with cache-allocating stores and the update pass reads first, from the
+   * chip's memory-side cache (Infinity Cache): the last 256 MiB of the sums
+   * when all of them take at most 448 MiB, else 0.  The step on already
+   * reduced gradients (grads_reduced) and the offload step do not use it.
+   * A performance detail only: no result depends on it. */
+  int64_t cached_sums_bytes;
 } zf_plan_summary;
 
 typedef struct {

@@ -141,6 +141,23 @@ def test_policy_and_workspace(zf):
         assert ws % 256 == 0
 
 
+def test_cached_sums_window(zf):
+    """The plan reports how many bytes of materialised sums pass 1 keeps in
+    the memory-side cache: the last 256 MiB of them when all the sums take
+    at most 448 MiB, none when they are recomputed or larger."""
+    MiB = 1 << 20
+    for numel, n, layout, want in (
+            (1000, 8, W.GLOBAL_FLAT, 4000),                       # small: all of them
+            (1000, 4, W.GLOBAL_FLAT, 0),                          # recomputed
+            (1000, 2, W.PER_PARAM_DIM0, 4000),                    # FSDP2's fp32 shard
+            (73_417_728, 8, W.GLOBAL_FLAT, 256 * MiB),            # 280 MiB of sums
+            (448 * MiB // 4, 8, W.GLOBAL_FLAT, 256 * MiB),        # exactly at the limit
+            (448 * MiB // 4 + 8, 8, W.GLOBAL_FLAT, 0),            # just past it
+            (120_000_011, 5, W.GLOBAL_FLAT, 0)):
+        plan = zf.plan_flat([(numel, 0)], n, layout, 2)
+        assert plan.summary.cached_sums_bytes == want, (numel, n, layout)
+
+
 def test_plan_errors(zf):
     Z = zf
     with pytest.raises(Z.ZfError) as e:
