@@ -4,12 +4,15 @@ Each case plants one mistake in a copy of oracle/zf_oracle.c (a dropped
 term, a wrong sign or index, a transposed operand, an off-by-one), builds
 it into a temporary library and runs the pin suite against it
 (tests/test_oracle_pins.py, via ZF_ORACLE_LIB).  The suite must fail.
-CPU only; the shipped oracle is never modified.
+CPU only; the shipped oracle is never modified.  The selected mutants are
+built and checked up front, several at a time (each in its own process),
+and every case then reads its own outcome.
 """
 import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import pytest
 
@@ -122,17 +125,43 @@ MUTANTS = [
 ]
 
 
-@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
-def test_pins_catch_mutant(tmp_path, name, old, new):
+WORKERS = max(1, min(6, os.cpu_count() or 1))
+
+
+def run_mutant(workdir, name, old, new):
+    """Build one mutant and run the pin suite against it: (the suite's exit
+    status, the end of its output), or (None, why) if the site is missing."""
     src = open(SRC).read()
-    assert src.count(old) == 1, f"mutation site not found once: {name}"
-    (tmp_path / "zf_oracle.c").write_text(src.replace(old, new))
-    shutil.copy(HDR, tmp_path / "zf_oracle.h")
-    lib = tmp_path / "libmutant.so"
-    subprocess.run(["gcc", *ob.CFLAGS, "-o", str(lib), str(tmp_path / "zf_oracle.c"), "-lm"],
+    if src.count(old) != 1:
+        return None, f"mutation site not found once: {name}"
+    os.makedirs(workdir, exist_ok=True)
+    with open(os.path.join(workdir, "zf_oracle.c"), "w") as f:
+        f.write(src.replace(old, new))
+    shutil.copy(HDR, os.path.join(workdir, "zf_oracle.h"))
+    lib = os.path.join(workdir, "libmutant.so")
+    subprocess.run(["gcc", *ob.CFLAGS, "-o", lib, os.path.join(workdir, "zf_oracle.c"), "-lm"],
                    check=True)
-    env = dict(os.environ, ZF_ORACLE_LIB=str(lib))
+    env = dict(os.environ, ZF_ORACLE_LIB=lib, OMP_NUM_THREADS="1")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         os.path.join(ROOT, "tests", "test_oracle_pins.py")],
-                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
-    assert r.returncode != 0, f"the pins did not catch: {name}\n{r.stdout[-2000:]}"
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=900)
+    return r.returncode, r.stdout[-2000:]
+
+
+@pytest.fixture(scope="module")
+def outcomes(request, tmp_path_factory):
+    """Outcome of every mutant this session selected, computed together."""
+    picked = {item.callspec.params["name"] for item in request.session.items
+              if getattr(item, "originalname", None) == "test_pins_catch_mutant"}
+    todo = [m for m in MUTANTS if m[0] in picked]
+    base = tmp_path_factory.mktemp("mutants")
+    with ThreadPoolExecutor(WORKERS) as ex:
+        res = ex.map(lambda km: run_mutant(str(base / f"m{km[0]}"), *km[1]), enumerate(todo))
+        return dict(zip((m[0] for m in todo), res))
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(outcomes, name, old, new):
+    rc, out = outcomes[name]
+    assert rc is not None, out
+    assert rc != 0, f"the pins did not catch: {name}\n{out}"
