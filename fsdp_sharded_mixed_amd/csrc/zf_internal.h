@@ -26,17 +26,18 @@ constexpr uint64_t kPlanMagic = 0x7a665f706c616e31ull;  // "zf_plan1"
 //  - the update pass reads master, m and v with the non-temporal hint (under
 //    the occupancy cap: 73M -4%, 654M -7%, 4.06B -2%, FSDP2 2.1B -2%; before
 //    the cap the same hint had cost +15%) and the materialised sums with
-//    plain loads (the hint there: neutral at 73M, +6% for FSDP2); it runs
-//    one 2-quad step per thread (under the occupancy cap two steps cost +5%
-//    at 4.06B, +6% at 73M and +9% for FSDP2 2.1B); its tiles walk in block
-//    order (the XCD-contiguous walk costs +3% there);
-//  - the materialised sums go out with non-temporal stores and the update
-//    pass walks its tiles forward: walking them backward so that the newest
-//    sums might still be in the 256 MB Infinity Cache saved 2% of the update
-//    pass only with temporal stores, which cost pass 1 10% (73M, N = 8).
-//  - occupancy: the update pass runs at most 2 blocks (8 waves) per CU:
-//    73M -8%, 654M -3%, 2.1B FSDP2 -10% against the register-limited 8
-//    blocks; 1 block per CU is slower again (+10% at 73M).  Pass 1 runs at
+//    plain loads (the hint there: neutral at 73M, +6% for FSDP2); its tiles
+//    walk in block order (the XCD-contiguous walk costs +3% there), or
+//    backward behind a cached-sums window (cached_sums_quads);
+//  - the update pass takes one quad per thread per tile and at most 3 blocks
+//    (12 waves) per CU, 4 behind a cached-sums window: the bytes in flight
+//    per CU decide it.  Against two quads at 2 blocks per CU, the step: 4.06B
+//    -3.9%, 2.1B ZeRO-3 -3.3%, FSDP2 2.1B -3.8%, 654M -2.3%, 73M at N = 2
+//    -4.8%, 73M at N = 8 (window) -2.2%.  One quad at 2, 4, 5, 6 blocks or
+//    uncapped gave 4.06B +3.1%, -1.8%, +0.5%, +2.1%, +5.3% and 73M at N = 8
+//    +3.3%, -2.2%, -2.2%, -1.9%, -2.1%; two quads at 3 blocks +1.1% and
+//    -1.0%.  (Two quads at 2 blocks had beaten the register-limited 8 blocks
+//    by 3-10% and 1 block by 10%.)  Pass 1 runs at
 //    most 3 blocks per CU when it streams 6 or more replicas and writes the
 //    sums (73M at N = 6 and N = 8: -2% to -3% against no cap or a cap of
 //    4); with 2 replicas, read-only or writing, it needs every block it can
@@ -54,7 +55,8 @@ constexpr uint64_t kPlanMagic = 0x7a665f706c616e31ull;  // "zf_plan1"
 #endif
 
 constexpr int kThreads = 256;        // 4 wave64 per block
-constexpr int kQuadsPerUnr = 2;      // quads (4 elements) per thread per tile step
+constexpr int kQuadsPerUnr = 2;      // pass 1: quads (4 elements) per thread per tile step
+constexpr int kQuadsPass2 = 1;       // the update pass: quads per thread per tile step
 inline int unr_pass1(int n_ranks) {
 #ifdef ZF_FORCE_UNR1
   (void)n_ranks;
@@ -120,11 +122,12 @@ inline int occ_pass1(int n_ranks, bool writes_sums) {
   return (writes_sums && n_ranks >= 6) ? 3 : 0;
 #endif
 }
-inline int occ_pass2() {
+inline int occ_pass2(bool cached_sums) {
 #ifdef ZF_FORCE_OCC2
+  (void)cached_sums;
   return ZF_FORCE_OCC2;
 #else
-  return 2;
+  return cached_sums ? 4 : 3;
 #endif
 }
 inline uint32_t occupancy_lds(int blocks_per_cu) {
@@ -132,6 +135,7 @@ inline uint32_t occupancy_lds(int blocks_per_cu) {
   return (uint32_t)(kLdsPerCU / (blocks_per_cu + 1) + 1024);
 }
 static_assert(kLdsPerCU / (kLdsPerCU / 3 + 1024) == 2, "two blocks per CU");
+static_assert(kLdsPerCU / (kLdsPerCU / 4 + 1024) == 3, "three blocks per CU");
 static_assert(kLdsPerCU / (kLdsPerCU / 5 + 1024) == 4, "four blocks per CU");
 
 // The device state block (the caller's zf_state_bytes() buffer), also read

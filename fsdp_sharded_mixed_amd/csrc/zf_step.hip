@@ -455,8 +455,8 @@ int launch_pass1(const zf_plan* plan, int32_t dt, hipStream_t s, const Pass1Args
 
 template <int GDT, int PDT, int U, bool OUT16>
 void launch_pass2_nr(int nr, bool mat, dim3 grid, hipStream_t s, const Pass2Args& a) {
-  constexpr int Q = zf::kQuadsPerUnr * U;
-  const uint32_t lds = zf::occupancy_lds(zf::occ_pass2());
+  constexpr int Q = zf::kQuadsPass2 * U;
+  const uint32_t lds = zf::occupancy_lds(zf::occ_pass2(a.reverse != 0));
   if (mat) {
     hipLaunchKernelGGL((zf_pass2<0, GDT, PDT, true, Q, OUT16>), grid, dim3(kThreads), lds, s, a);
     return;
