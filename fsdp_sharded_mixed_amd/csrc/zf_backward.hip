@@ -120,7 +120,12 @@ __global__ __launch_bounds__(kThreads) void zf_bucket_rs_kernel(BucketArgs a) {
 
 // Local accumulation acc[i] (+)= f32(grad[i]), i < n.  vec: acc + head is
 // 16-byte aligned and grad + head 8-byte aligned, so the nq quads after the
-// head are vector accesses; otherwise every element is scalar.
+// head are vector accesses; otherwise every element is scalar.  One quad per
+// thread per block, uncapped: against four quads, the no_sync backward phase
+// -9.9% (654M, four micro-batches); two quads -3.3%; caps of 3-4 blocks per
+// CU lose.  The bucket reduce-scatter keeps two quads uncapped (one quad
+// +5%, caps of 3-4 blocks +18% to +55%).
+constexpr int kAccQuads = 1;
 struct AccArgs {
   const uint16_t* g;
   float* acc;
@@ -130,7 +135,7 @@ struct AccArgs {
 
 template <int DT, bool ACC>
 __global__ __launch_bounds__(kThreads) void zf_accumulate_kernel(AccArgs a) {
-  constexpr int Q = 4;
+  constexpr int Q = kAccQuads;
   if (a.vec) {
     const uint16_t* g = a.g + a.head;
     float* o = a.acc + a.head;
@@ -261,7 +266,7 @@ extern "C" int zf_accumulate(int32_t grad_dtype, const void* grad, float* acc, i
   a.nq = a.vec ? (n - head) / kQuad : 0;
   int64_t bx;
   if (a.vec) {
-    bx = (a.nq + (int64_t)kThreads * 4 - 1) / ((int64_t)kThreads * 4);
+    bx = (a.nq + (int64_t)kThreads * kAccQuads - 1) / ((int64_t)kThreads * kAccQuads);
   } else {
     bx = (n + (int64_t)kThreads * 8 - 1) / ((int64_t)kThreads * 8);
     if (bx > 65536) bx = 65536;

@@ -21,8 +21,10 @@ constexpr uint64_t kPlanMagic = 0x7a665f706c616e31ull;  // "zf_plan1"
 //    +50% at N = 8, where the sums' stores become strided, and +8% at N = 2).  With
 //    N <= 4 it walks the tiles XCD-contiguously (N = 2: -6%, 3: -5%,
 //    4: -5%); at N = 8 that walk costs +4%, so many replicas keep one
-//    shared window.  One 2-quad step per thread for N <= 2 (-6% at 4.06B),
-//    two steps otherwise;
+//    shared window.  One 2-quad step per thread for N <= 2 (-6% at 4.06B)
+//    and for N >= 6 (step time at 73M: N = 6 -1.2%, 8 -1.5%, 12 -2.8%, 16
+//    -1.6%, 32 -1.9%, with the caps below), two steps for N = 3-5 (one step
+//    at N = 5: +0.7%);
 //  - the update pass reads master, m and v with the non-temporal hint (under
 //    the occupancy cap: 73M -4%, 654M -7%, 4.06B -2%, FSDP2 2.1B -2%; before
 //    the cap the same hint had cost +15%) and the materialised sums with
@@ -37,11 +39,12 @@ constexpr uint64_t kPlanMagic = 0x7a665f706c616e31ull;  // "zf_plan1"
 //    uncapped gave 4.06B +3.1%, -1.8%, +0.5%, +2.1%, +5.3% and 73M at N = 8
 //    +3.3%, -2.2%, -2.2%, -1.9%, -2.1%; two quads at 3 blocks +1.1% and
 //    -1.0%.  (Two quads at 2 blocks had beaten the register-limited 8 blocks
-//    by 3-10% and 1 block by 10%.)  Pass 1 runs at
-//    most 3 blocks per CU when it streams 6 or more replicas and writes the
-//    sums (73M at N = 6 and N = 8: -2% to -3% against no cap or a cap of
-//    4); with 2 replicas, read-only or writing, it needs every block it can
-//    get (a cap of 4 costs +13% to +90%).
+//    by 3-10% and 1 block by 10%.)  Pass 1 runs at most 3 blocks per CU
+//    when it streams 6 to 8 replicas and writes the sums, 4 with more (one
+//    step at 73M, N = 8: cap 3 -2.0%, no cap +0.6%, 4 -0.2%, 6 +1.0%; N =
+//    16: cap 4 -2.3%, 3 +0.1%; the earlier two-step tiles had taken cap 3 at
+//    N = 6-8 for -2% to -3%); with 2 replicas, read-only or writing, it needs
+//    every block it can get (a cap of 4 costs +13% to +90%).
 //  - pass 1 splits full tiles from the last one: a full tile's loads carry
 //    no range check and issue back to back (-2% at N = 8; the update pass
 //    measured within 1% either way and keeps one code path).
@@ -62,7 +65,7 @@ inline int unr_pass1(int n_ranks) {
   (void)n_ranks;
   return ZF_FORCE_UNR1;
 #else
-  return n_ranks <= 2 ? 1 : 2;
+  return (n_ranks <= 2 || n_ranks >= 6) ? 1 : 2;
 #endif
 }
 inline int map_pass1(int n_ranks) {
@@ -119,7 +122,8 @@ inline int occ_pass1(int n_ranks, bool writes_sums) {
   (void)writes_sums;
   return ZF_FORCE_OCC1;
 #else
-  return (writes_sums && n_ranks >= 6) ? 3 : 0;
+  if (!writes_sums || n_ranks < 6) return 0;
+  return n_ranks > 8 ? 4 : 3;
 #endif
 }
 inline int occ_pass2(bool cached_sums) {
