@@ -31,12 +31,19 @@ constexpr uint64_t kPlanMagic = 0x7a665f706c616e31ull;  // "zf_plan1"
 //    plain loads (the hint there: neutral at 73M, +6% for FSDP2); its tiles
 //    walk in block order (the XCD-contiguous walk costs +3% there), or
 //    backward behind a cached-sums window (cached_sums_quads);
-//  - the update pass takes one quad per thread per tile and at most 3 blocks
-//    (12 waves) per CU, 4 behind a cached-sums window: the bytes in flight
-//    per CU decide it.  Against two quads at 2 blocks per CU, the step: 4.06B
-//    -3.9%, 2.1B ZeRO-3 -3.3%, FSDP2 2.1B -3.8%, 654M -2.3%, 73M at N = 2
-//    -4.8%, 73M at N = 8 (window) -2.2%.  One quad at 2, 4, 5, 6 blocks or
-//    uncapped gave 4.06B +3.1%, -1.8%, +0.5%, +2.1%, +5.3% and 73M at N = 8
+//  - the update pass takes one quad per thread per tile; recomputing the
+//    sums it runs 128-thread blocks, at most 5 per CU (10 waves), reading
+//    materialised sums 256-thread blocks, at most 3 per CU (12 waves), 4
+//    behind a cached-sums window: the bytes in flight per CU decide it.
+//    128-thread blocks at 4, 5, 6 per CU against 256-thread blocks at 3,
+//    recomputing: 4.06B +5.9%, -2.5%, -1.2%; 2.1B ZeRO-3 +3.4%, -4.7%,
+//    -4.2%; 654M +6.4%, -2.0%, -2.0%; 73M at N = 2-4 +0.7% to +6.4%, -2.0%
+//    to -3.8%, -2.7% to -4.4%; reading FSDP2's fp32 gradient shards they
+//    lose (+2.3% at 5 per CU).  Before that, one quad per thread in
+//    256-thread blocks at 3 per CU (4 behind a window) against the earlier
+//    two quads at 2 per CU, the step: 4.06B -3.9%, 2.1B ZeRO-3 -3.3%, FSDP2
+//    2.1B -3.8%, 654M -2.3%, 73M at N = 2 -4.8%, 73M at N = 8 (window)
+//    -2.2%; one quad at 2, 4, 5, 6 blocks or uncapped gave 4.06B +3.1%, -1.8%, +0.5%, +2.1%, +5.3% and 73M at N = 8
 //    +3.3%, -2.2%, -2.2%, -1.9%, -2.1%; two quads at 3 blocks +1.1% and
 //    -1.0%.  (Two quads at 2 blocks had beaten the register-limited 8 blocks
 //    by 3-10% and 1 block by 10%.)  Pass 1 runs at most 3 blocks per CU
@@ -60,6 +67,11 @@ constexpr uint64_t kPlanMagic = 0x7a665f706c616e31ull;  // "zf_plan1"
 constexpr int kThreads = 256;        // 4 wave64 per block
 constexpr int kQuadsPerUnr = 2;      // pass 1: quads (4 elements) per thread per tile step
 constexpr int kQuadsPass2 = 1;       // the update pass: quads per thread per tile step
+// the update pass's block size: 128 threads when it recomputes the sums from
+// the replicas, 256 when it reads materialised sums
+constexpr int kThreadsPass2Recompute = 128;
+constexpr int kThreadsPass2Mat = 256;
+constexpr int threads_pass2(bool mat) { return mat ? kThreadsPass2Mat : kThreadsPass2Recompute; }
 inline int unr_pass1(int n_ranks) {
 #ifdef ZF_FORCE_UNR1
   (void)n_ranks;
@@ -126,11 +138,13 @@ inline int occ_pass1(int n_ranks, bool writes_sums) {
   return n_ranks > 8 ? 4 : 3;
 #endif
 }
-inline int occ_pass2(bool cached_sums) {
+inline int occ_pass2(bool mat, bool cached_sums) {
 #ifdef ZF_FORCE_OCC2
+  (void)mat;
   (void)cached_sums;
   return ZF_FORCE_OCC2;
 #else
+  if (!mat) return 5;  // 128-thread blocks: 10 waves per CU
   return cached_sums ? 4 : 3;
 #endif
 }
@@ -141,6 +155,7 @@ inline uint32_t occupancy_lds(int blocks_per_cu) {
 static_assert(kLdsPerCU / (kLdsPerCU / 3 + 1024) == 2, "two blocks per CU");
 static_assert(kLdsPerCU / (kLdsPerCU / 4 + 1024) == 3, "three blocks per CU");
 static_assert(kLdsPerCU / (kLdsPerCU / 5 + 1024) == 4, "four blocks per CU");
+static_assert(kLdsPerCU / (kLdsPerCU / 6 + 1024) == 5, "five blocks per CU");
 
 // The device state block (the caller's zf_state_bytes() buffer), also read
 // on the host by the offload step.
@@ -202,13 +217,23 @@ struct zf_plan {
   zf_plan_summary summary;
   std::vector<zf_unit_info> units;
   std::vector<zf_group_info> groups;
-  int32_t unr1, unr2;           // tile depth of pass 1 / pass 2 (x2 quads per thread)
+  int32_t unr1, unr2;           // tile steps of pass 1 / the update pass per thread
   int32_t pass1_map;            // pass-1 tile walk (0 shared window, 1 XCD-contiguous)
   int64_t pass1_tiles;          // pass-1 blocks = squared-norm partials
   int32_t level2_blocks;        // blocks reducing the partials
-  int64_t pass2_tiles;          // update-pass blocks
   int64_t ws_partials_offset;   // bytes
   int64_t ws_partials2_offset;  // bytes
   int64_t ws_rs_offset;         // bytes, -1 if the sums are recomputed
   int64_t cached_sums_quads;    // fp32 sums stored cache-allocating (see cached_sums_quads)
 };
+
+namespace zf {
+// The update pass's blocks for a plan: one tile of threads_pass2(mat) x
+// kQuadsPass2 x unr2 quads each (at least one block; the last one also
+// takes the ragged tail).
+inline int64_t pass2_tiles(const zf_plan* p, bool mat) {
+  const int64_t q = (int64_t)threads_pass2(mat) * kQuadsPass2 * p->unr2;
+  const int64_t t = (p->summary.psi_pad / 4 + q - 1) / q;
+  return t < 1 ? 1 : t;
+}
+}  // namespace zf

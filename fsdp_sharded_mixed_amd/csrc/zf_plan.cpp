@@ -159,11 +159,14 @@ extern "C" int zf_plan_flat(const zf_segment* segs, int64_t nseg, int32_t n_rank
       s.policy != 0 ? std::min(s.psi_pad * 4, p->cached_sums_quads * 16) : 0;
   p->unr2 = zf::unr_pass2(n_ranks, s.psi_pad, s.policy != 0);
   const int64_t q1 = (int64_t)zf::kThreads * zf::kQuadsPerUnr * p->unr1;
-  const int64_t q2 = (int64_t)zf::kThreads * zf::kQuadsPass2 * p->unr2;
   const int64_t t1 = (nq + q1 - 1) / q1;
-  const int64_t t2 = (nq + q2 - 1) / q2;
   p->pass1_tiles = t1 < 1 ? 1 : t1;
-  p->pass2_tiles = t2 < 1 ? 1 : t2;
+  // every launch grid must fit grid.x: pass 1's tiles and the update pass's
+  // smallest tiles (zf::pass2_tiles with 128-thread blocks)
+  if (p->pass1_tiles > 0x7FFFFFFF || zf::pass2_tiles(p, false) > 0x7FFFFFFF) {
+    delete p;
+    return ZF_ESIZE;
+  }
   int64_t l2 = (p->pass1_tiles + zf::kThreads - 1) / zf::kThreads;
   if (l2 > zf::kMaxLevel2Blocks) l2 = zf::kMaxLevel2Blocks;
   p->level2_blocks = (int32_t)l2;

@@ -322,7 +322,8 @@ __device__ __forceinline__ void adamw1(const Coef& c, float acc, float& p, float
 }
 
 template <int NR, int GDT, int PDT, bool MAT, int Q, bool OUT16>
-__global__ __launch_bounds__(kThreads) void zf_pass2(Pass2Args a) {
+__global__ __launch_bounds__(zf::kThreadsPass2Mat) void zf_pass2(Pass2Args a) {
+  constexpr int T = zf::threads_pass2(MAT);  // the block size
   // the occupancy cap: dynamic LDS (see occupancy_lds) that no lane touches
   // (n is never negative)
   extern __shared__ uint32_t zf_occupancy_lds[];
@@ -338,12 +339,12 @@ __global__ __launch_bounds__(kThreads) void zf_pass2(Pass2Args a) {
   const int64_t nq = a.n / kQuad;
   const int64_t tile =
       (MAT && a.reverse) ? (int64_t)gridDim.x - 1 - blockIdx.x : (int64_t)blockIdx.x;
-  const int64_t q0 = tile * kThreads * Q + threadIdx.x;
+  const int64_t q0 = tile * T * Q + threadIdx.x;
   int64_t qi[Q];
   bool ok[Q];
 #pragma unroll
   for (int h = 0; h < Q; ++h) {
-    qi[h] = q0 + (int64_t)h * kThreads;
+    qi[h] = q0 + (int64_t)h * T;
     ok[h] = qi[h] < nq;
   }
   f32x4 acc[Q], p[Q], m[Q], v[Q];
@@ -456,13 +457,14 @@ int launch_pass1(const zf_plan* plan, int32_t dt, hipStream_t s, const Pass1Args
 template <int GDT, int PDT, int U, bool OUT16>
 void launch_pass2_nr(int nr, bool mat, dim3 grid, hipStream_t s, const Pass2Args& a) {
   constexpr int Q = zf::kQuadsPass2 * U;
-  const uint32_t lds = zf::occupancy_lds(zf::occ_pass2(a.reverse != 0));
+  const uint32_t lds = zf::occupancy_lds(zf::occ_pass2(mat, a.reverse != 0));
+  const dim3 block((uint32_t)zf::threads_pass2(mat));
   if (mat) {
-    hipLaunchKernelGGL((zf_pass2<0, GDT, PDT, true, Q, OUT16>), grid, dim3(kThreads), lds, s, a);
+    hipLaunchKernelGGL((zf_pass2<0, GDT, PDT, true, Q, OUT16>), grid, block, lds, s, a);
     return;
   }
 #define ZF_P2(NRV) \
-  hipLaunchKernelGGL((zf_pass2<NRV, GDT, PDT, false, Q, OUT16>), grid, dim3(kThreads), lds, s, a)
+  hipLaunchKernelGGL((zf_pass2<NRV, GDT, PDT, false, Q, OUT16>), grid, block, lds, s, a)
   switch (nr) {
     case 1: ZF_P2(1); break;
     case 2: ZF_P2(2); break;
@@ -496,7 +498,7 @@ void launch_pass2_u(int nr, int32_t gdt, int32_t pdt, bool mat, bool out16, dim3
 
 int launch_pass2(const zf_plan* plan, int32_t gdt, int32_t pdt, bool mat, bool out16,
                  hipStream_t s, const Pass2Args& a) {
-  const dim3 grid((uint32_t)plan->pass2_tiles);
+  const dim3 grid((uint32_t)zf::pass2_tiles(plan, mat));  // fits: checked by the planner
   const int nr = plan->summary.n_ranks;
   if (plan->unr2 == 2) launch_pass2_u<2>(nr, gdt, pdt, mat, out16, grid, s, a);
   else launch_pass2_u<1>(nr, gdt, pdt, mat, out16, grid, s, a);

@@ -174,6 +174,13 @@ def test_plan_errors(zf):
         Z.plan_flat([(10, 0)], 2, 7, 2)
     with pytest.raises(Z.ZfError):
         Z.plan_flat([(10, 0)], 2, W.GLOBAL_FLAT, 4)
+    # launch grids hold at most 2^31 - 1 blocks: the update pass's smallest
+    # tiles are 128 threads x 1 quad = 512 elements
+    edge = (2 ** 31 - 1) * 512
+    Z.plan_flat([(edge, 0)], 2, W.GLOBAL_FLAT, 2)
+    with pytest.raises(Z.ZfError) as e:
+        Z.plan_flat([(edge + 512, 0)], 2, W.GLOBAL_FLAT, 2)
+    assert e.value.status == -4
     assert Z.lib.zf_plan_info(None, C.byref(Z.PlanSummary())) == -1
     assert Z.lib.zf_plan_unit(None, 0, C.byref(Z.UnitInfo())) == -1
     plan = Z.plan_flat([(10, 0)], 2, W.GLOBAL_FLAT, 2)
