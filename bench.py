@@ -288,28 +288,46 @@ def summarize_pmc(fetch_dir, write_dir, workload, out, commands):
 PROBE_FLOATS = 1 << 28  # 1 GiB per array
 
 
+# probe shapes (quads per lane, resident blocks per CU, 0: no limit); the
+# best one per access mix is the box's figure for that mix
+PROBE_SHAPES = ((1, 0), (2, 0), (1, 3), (1, 4), (2, 3), (2, 4))
+
+
 def stream_probes(reps=10):
-    """GB/s of the box for streams in the step kernels' access pattern
-    (zfi_stream_probe): a copy (1 read, 1 write), the update pass's mix of
-    4 reads and 4 writes, and 8 reads + 1 write (pass 1 at N = 8)."""
+    """GB/s of the box for streams in the step kernels' access pattern: a
+    copy (1 read, 1 write), the update pass's mix of 4 reads and 4 writes,
+    and 8 reads + 1 write (pass 1 at N = 8).  Each mix is timed with the
+    fixed-shape zfi_stream_probe and with zfi_stream_probe_shaped in every
+    PROBE_SHAPES shape; the best figure is reported, with its shape in
+    out["shape"] ("fixed" or "q<quads>c<blocks per CU>")."""
     import torch
     from fsdp_sharded_mixed_amd import inputs as I
     bufs = [torch.ones(PROBE_FLOATS, dtype=torch.float32, device="cuda:0") for _ in range(9)]
-    out = {}
-    for name, r, wr in (("1r1w", 1, 1), ("4r4w", 4, 4), ("8r1w", 8, 1)):
-        src, dst = bufs[:r], bufs[r:r + wr]
+    out, shape = {}, {}
+
+    def gbs(run, moved):
         for _ in range(3):
-            I.stream_probe(src, dst)
+            run()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(reps):
-            I.stream_probe(src, dst)
+            run()
         e1.record()
         torch.cuda.synchronize()
-        out[name] = round((r + wr) * 4 * PROBE_FLOATS * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9,
-                          1)
+        return moved * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+    for name, r, wr in (("1r1w", 1, 1), ("4r4w", 4, 4), ("8r1w", 8, 1)):
+        src, dst = bufs[:r], bufs[r:r + wr]
+        moved = (r + wr) * 4 * PROBE_FLOATS
+        best, which = gbs(lambda: I.stream_probe(src, dst), moved), "fixed"
+        for q, c in PROBE_SHAPES:
+            g = gbs(lambda: I.stream_probe_shaped(src, dst, q, c), moved)
+            if g > best:
+                best, which = g, f"q{q}c{c}"
+        out[name], shape[name] = round(best, 1), which
     del bufs
     torch.cuda.empty_cache()
+    out["shape"] = shape
     return out
 
 

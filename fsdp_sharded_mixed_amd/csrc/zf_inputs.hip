@@ -131,6 +131,53 @@ __global__ __launch_bounds__(256) void stream_probe(ProbeArgs a) {
   }
 }
 
+// The same sums in a chosen shape: Q quads per lane per tile, non-temporal
+// loads as well as stores, and at most `cap` resident blocks per CU (dynamic
+// LDS that no lane touches; n is never negative).
+template <int R, int W, int Q>
+__global__ __launch_bounds__(256) void stream_probe_shaped(ProbeArgs a) {
+  extern __shared__ uint32_t probe_cap_lds[];
+  if (a.nq < 0) probe_cap_lds[threadIdx.x] = 0u;
+  const int64_t q0 = (int64_t)blockIdx.x * 256 * Q + threadIdx.x;
+  f32x4p x[Q];
+#pragma unroll
+  for (int h = 0; h < Q; ++h) {
+    const int64_t q = q0 + (int64_t)h * 256;
+    f32x4p t = {0, 0, 0, 0};
+    if (q < a.nq) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        t = t + __builtin_nontemporal_load(reinterpret_cast<const f32x4p*>(a.src[r]) + q);
+    }
+    x[h] = t;
+  }
+#pragma unroll
+  for (int h = 0; h < Q; ++h) {
+    const int64_t q = q0 + (int64_t)h * 256;
+    if (q >= a.nq) continue;
+#pragma unroll
+    for (int k = 0; k < W; ++k)
+      __builtin_nontemporal_store(x[h], reinterpret_cast<f32x4p*>(a.dst[k]) + q);
+  }
+}
+
+template <int R, int W>
+void launch_shaped_q(int q, dim3 g, uint32_t lds, hipStream_t s, const ProbeArgs& a) {
+  if (q == 1) hipLaunchKernelGGL((stream_probe_shaped<R, W, 1>), g, dim3(256), lds, s, a);
+  else if (q == 2) hipLaunchKernelGGL((stream_probe_shaped<R, W, 2>), g, dim3(256), lds, s, a);
+  else hipLaunchKernelGGL((stream_probe_shaped<R, W, 4>), g, dim3(256), lds, s, a);
+}
+
+template <int R>
+void launch_shaped_w(int w, int q, dim3 g, uint32_t lds, hipStream_t s, const ProbeArgs& a) {
+  switch (w) {
+    case 1: launch_shaped_q<R, 1>(q, g, lds, s, a); break;
+    case 2: launch_shaped_q<R, 2>(q, g, lds, s, a); break;
+    case 4: launch_shaped_q<R, 4>(q, g, lds, s, a); break;
+    default: launch_shaped_q<R, 8>(q, g, lds, s, a); break;
+  }
+}
+
 template <int R>
 void launch_probe_w(int w, dim3 g, hipStream_t s, const ProbeArgs& a) {
   switch (w) {
@@ -142,6 +189,46 @@ void launch_probe_w(int w, dim3 g, hipStream_t s, const ProbeArgs& a) {
 }
 
 }  // namespace
+
+extern "C" int zfi_stream_probe_shaped(const float* const* src, int32_t n_src,
+                                       float* const* dst, int32_t n_dst, int64_t n,
+                                       int32_t quads, int32_t blocks_per_cu,
+                                       void* stream_handle) {
+  if (!src || !dst || n <= 0 || n % 4 != 0) return -1;
+  if (!(n_src == 1 || n_src == 2 || n_src == 4 || n_src == 8)) return -1;
+  if (!(n_dst == 1 || n_dst == 2 || n_dst == 4 || n_dst == 8)) return -1;
+  if (!(quads == 1 || quads == 2 || quads == 4)) return -1;
+  if (blocks_per_cu < 0 || blocks_per_cu > 8) return -1;
+  ProbeArgs a;
+  for (int k = 0; k < 8; ++k) {
+    a.src[k] = nullptr;
+    a.dst[k] = nullptr;
+  }
+  for (int k = 0; k < n_src; ++k) {
+    if (!src[k] || (reinterpret_cast<uintptr_t>(src[k]) & 15u)) return -1;
+    a.src[k] = src[k];
+  }
+  for (int k = 0; k < n_dst; ++k) {
+    if (!dst[k] || (reinterpret_cast<uintptr_t>(dst[k]) & 15u)) return -1;
+    a.dst[k] = dst[k];
+  }
+  a.nq = n / 4;
+  const int64_t per = 256 * (int64_t)quads;
+  const int64_t blocks = (a.nq + per - 1) / per;
+  if (blocks > 0x7FFFFFFF) return -1;
+  const dim3 g((uint32_t)blocks);
+  // a CU holds 160 KiB of LDS: k blocks fit, k + 1 do not
+  const uint32_t lds = blocks_per_cu ? (uint32_t)(160 * 1024 / (blocks_per_cu + 1) + 1024) : 0u;
+  hipStream_t s = static_cast<hipStream_t>(stream_handle);
+  (void)hipGetLastError();
+  switch (n_src) {
+    case 1: launch_shaped_w<1>(n_dst, quads, g, lds, s, a); break;
+    case 2: launch_shaped_w<2>(n_dst, quads, g, lds, s, a); break;
+    case 4: launch_shaped_w<4>(n_dst, quads, g, lds, s, a); break;
+    default: launch_shaped_w<8>(n_dst, quads, g, lds, s, a); break;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
 
 extern "C" int zfi_stream_probe(const float* const* src, int32_t n_src, float* const* dst,
                                 int32_t n_dst, int64_t n, void* stream_handle) {

@@ -26,6 +26,10 @@ def _load():
     lib.zfi_stream_probe.restype = C.c_int
     lib.zfi_stream_probe.argtypes = [C.POINTER(C.c_void_p), C.c_int32, C.POINTER(C.c_void_p),
                                      C.c_int32, C.c_int64, C.c_void_p]
+    lib.zfi_stream_probe_shaped.restype = C.c_int
+    lib.zfi_stream_probe_shaped.argtypes = [C.POINTER(C.c_void_p), C.c_int32,
+                                            C.POINTER(C.c_void_p), C.c_int32, C.c_int64,
+                                            C.c_int32, C.c_int32, C.c_void_p]
     lib.zfi_stream_output.restype = C.c_uint64
     lib.zfi_stream_output.argtypes = [C.c_uint64, C.c_uint64, C.c_uint64]
     lib.zfi_sqrt_probe.restype = C.c_int
@@ -81,6 +85,18 @@ def stream_probe(srcs, dsts, n=None, stream=None):
     rc = lib.zfi_stream_probe(sp, len(srcs), dp, len(dsts), int(n), _stream(stream))
     if rc != 0:
         raise RuntimeError(f"zfi_stream_probe failed ({rc})")
+
+
+def stream_probe_shaped(srcs, dsts, quads, blocks_per_cu, n=None, stream=None):
+    """zfi_stream_probe_shaped: the same sums with `quads` quads per lane and
+    at most `blocks_per_cu` resident blocks per CU (0: no limit)."""
+    n = min(t.numel() for t in list(srcs) + list(dsts)) if n is None else n
+    sp = (C.c_void_p * len(srcs))(*[t.data_ptr() for t in srcs])
+    dp = (C.c_void_p * len(dsts))(*[t.data_ptr() for t in dsts])
+    rc = lib.zfi_stream_probe_shaped(sp, len(srcs), dp, len(dsts), int(n), int(quads),
+                                     int(blocks_per_cu), _stream(stream))
+    if rc != 0:
+        raise RuntimeError(f"zfi_stream_probe_shaped failed ({rc})")
 
 
 def sqrt_probe(out, first_bits, n=None, stream=None):

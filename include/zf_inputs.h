@@ -51,6 +51,15 @@ uint64_t zfi_stream_output(uint64_t seed, uint64_t stream, uint64_t j);
 int zfi_stream_probe(const float* const* src, int32_t n_src, float* const* dst, int32_t n_dst,
                      int64_t n, void* stream_handle);
 
+/* The same probe in a chosen shape, to find the box's best figure for an
+ * access mix: `quads` (1, 2 or 4) quads per lane per 256-thread block,
+ * non-temporal loads as well as stores, and at most `blocks_per_cu` (1..8;
+ * 0: no limit) resident blocks per compute unit.  Arguments otherwise as
+ * zfi_stream_probe.  Returns 0, -1 (bad argument) or -5. */
+int zfi_stream_probe_shaped(const float* const* src, int32_t n_src, float* const* dst,
+                            int32_t n_dst, int64_t n, int32_t quads, int32_t blocks_per_cu,
+                            void* stream_handle);
+
 /* Lowering probes for tests (no arithmetic of the step): binary32 sqrt and
  * division exactly as this compiler emits them under the step library's
  * flags (-fhip-fp32-correctly-rounded-divide-sqrt, -ffp-contract=off).

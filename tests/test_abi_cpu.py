@@ -37,7 +37,8 @@ def test_headers_declare_the_calls():
         assert required in names
     assert _declared("zf_inputs.h") == sorted(["zfi_fill_normal16", "zfi_fill_normal32",
                                                "zfi_stream_output", "zfi_stream_probe",
-                                               "zfi_sqrt_probe", "zfi_div_probe"])
+                                               "zfi_stream_probe_shaped", "zfi_sqrt_probe",
+                                               "zfi_div_probe"])
 
 
 @pytest.mark.parametrize("header,lib", [("zf.h", "libzf.so"), ("zf_inputs.h", "libzf_inputs.so")])

@@ -350,6 +350,12 @@ def test_stream_probe_sums(R):
             want = want + t
         for d in dst:
             assert torch.equal(d, want)
+        for quads, cap in ((1, 0), (2, 4), (4, 3)):
+            for d in dst:
+                d.zero_()
+            I.stream_probe_shaped(src, dst, quads, cap)
+            for d in dst:
+                assert torch.equal(d, want), (r, wr, quads, cap)
 
 
 @pytest.mark.parametrize("dtype", [W.F16, W.BF16])
