@@ -171,7 +171,8 @@ typedef struct {
  * zf_shard_step (0-2: full buffer; 3: resident shards) and the ledger row.
  * Host only; *out receives a plan to release with zf_plan_free.
  * Errors: ZF_EINVAL (NULL, nseg < 1, numel < 1, unit ids not 0,0,..,1,..),
- * ZF_ESIZE (n_ranks out of range, Psi' >= 2^62), ZF_ENOMEM. */
+ * ZF_ESIZE (n_ranks out of range, Psi' >= 2^62, or a step kernel's grid
+ * above 2^31 - 1 blocks: Psi' above about 2^40), ZF_ENOMEM. */
 int zf_plan_flat(const zf_segment* segs, int64_t nseg, int32_t n_ranks, int32_t layout,
                  int32_t stage, zf_plan** out);
 
