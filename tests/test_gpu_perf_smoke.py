@@ -1,10 +1,13 @@
 """Performance smoke: the kernels keep their measured bandwidth, relative to
 the same box's own stream ceiling (so box-to-box variance does not matter).
 
-The update pass of the 73M workload (4 fp32 reads + 4 writes per element)
-must reach 85% of zfi_stream_probe's 4-read/4-write figure measured in the
-same process, and pass 1 (8 replicas in, the fp32 sums out) 85% of the
-8-read/1-write figure.  Both run at or above 100% today.
+The ceiling of an access mix is the best of the fixed-shape zfi_stream_probe
+and zfi_stream_probe_shaped in six shapes, measured in the same process.
+The update pass (4 reads + 4 writes per element, fp32 or a mix of 16-bit
+replicas and fp32 state) must reach 85% of the best 4-read/4-write figure,
+on the 73M workload (materialised sums) and the 654M one (recomputed sums);
+73M's pass 1 (8 replicas in, the fp32 sums out) 85% of the best
+8-read/1-write figure.  They run at 97% or more today.
 """
 import pytest
 import torch
@@ -14,22 +17,36 @@ from fsdp_sharded_mixed_amd import workloads as W
 pytestmark = pytest.mark.gpu
 
 
-def _probe(I, r, w, n=1 << 26, reps=10):
+SHAPES = ((1, 0), (2, 0), (1, 3), (1, 4), (2, 3), (2, 4))
+
+
+def _probe(I, r, w, n=1 << 28, reps=10):
+    """Best GB/s of the fixed probe and the shaped probe in SHAPES, on 1 GiB
+    arrays allocated one by one (smaller arrays carved from one allocation
+    can share DRAM address bits and read lower)."""
     bufs = [torch.ones(n, device="cuda") for _ in range(r + w)]
-    for _ in range(3):
-        I.stream_probe(bufs[:r], bufs[r:])
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        I.stream_probe(bufs[:r], bufs[r:])
-    e1.record()
-    torch.cuda.synchronize()
-    return (r + w) * 4 * n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    runs = [lambda: I.stream_probe(bufs[:r], bufs[r:])]
+    runs += [lambda q=q, c=c: I.stream_probe_shaped(bufs[:r], bufs[r:], q, c) for q, c in SHAPES]
+    best = 0.0
+    for run in runs:
+        for _ in range(3):
+            run()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, (r + w) * 4 * n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del bufs
+    torch.cuda.empty_cache()
+    return best
 
 
-def test_update_pass_near_box_ceiling():
+@pytest.mark.parametrize("name", ["llama-73m-n8", "llama-654m-n2"])
+def test_update_pass_near_box_ceiling(name):
     from fsdp_sharded_mixed_amd import inputs as I, runner
-    w = W.get("llama-73m-n8")
+    w = W.get(name)
     dev = runner.DeviceRun(w)
     dev.init_state()
     dev.fill_grads(1, w.loss_scale)
@@ -52,7 +69,8 @@ def test_update_pass_near_box_ceiling():
     del dev
     torch.cuda.empty_cache()
     c44, c81 = _probe(I, 4, 4), _probe(I, 8, 1)
-    print(f"pass1 {pass1_gbs:.0f} GB/s, pass2 {pass2_gbs:.0f} GB/s, probes 4+4 {c44:.0f}, "
-          f"8+1 {c81:.0f}", flush=True)
+    print(f"{name}: pass1 {pass1_gbs:.0f} GB/s, pass2 {pass2_gbs:.0f} GB/s, best probes 4+4 "
+          f"{c44:.0f}, 8+1 {c81:.0f}", flush=True)
     assert pass2_gbs >= 0.85 * c44, (pass2_gbs, c44)
-    assert pass1_gbs >= 0.85 * c81, (pass1_gbs, c81)
+    if w.n_ranks == 8:
+        assert pass1_gbs >= 0.85 * c81, (pass1_gbs, c81)
