@@ -254,6 +254,7 @@ extern "C" const char* zf_strerror(int status) {
     case ZF_ESIZE: return "size out of range";
     case ZF_EHIP: return "HIP runtime error";
     case ZF_ENOMEM: return "host allocation failed";
+    case ZF_EUNSUP: return "the host CPU lacks AVX2 or F16C (CPU-Adam)";
     default: return "unknown status";
   }
 }

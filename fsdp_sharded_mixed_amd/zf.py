@@ -161,7 +161,9 @@ def _ptr(x):
         return None
     if isinstance(x, int):
         return x
-    return x.data_ptr()
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    return x.ctypes.data  # a numpy host array
 
 
 def _stream(stream):
@@ -171,6 +173,15 @@ def _stream(stream):
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream
+
+
+def _host_elems(x, elem_bytes):
+    """Elements of elem_bytes bytes that a tensor or numpy array holds, or
+    None for a raw address (its size is the caller's to pass as numel)."""
+    if x is None or isinstance(x, int):
+        return None
+    nbytes = x.numel() * x.element_size() if hasattr(x, "element_size") else x.nbytes
+    return nbytes // elem_bytes
 
 
 def _ptr_array(items):
@@ -376,8 +387,15 @@ def offload_step(plan, hp, grad_dtype, param_dtype, grads, grad_shards, params, 
     raw hipEvent_t handles.  Returns the StepResult."""
     ev = (C.c_void_p * 4)(*phase_events) if phase_events is not None else None
     if numel is None:
-        arrays = list(grads or []) + [grad_shards, params]
-        numel = min(t.numel() for t in arrays if t is not None)
+        # every per-element array counts, host ones included: h_grad holds
+        # the sums that come down (4 bytes each, 2 with down16), h_params the
+        # 16-bit parameters going up, the h_ state arrays fp32
+        sized = [(t, t.element_size()) for t in list(grads or []) + [grad_shards, params]
+                 if t is not None and not isinstance(t, int)]
+        sized += [(h_grad, 2 if down16 else 4), (h_master, 4), (h_exp_avg, 4),
+                  (h_exp_avg_sq, 4), (h_params, 2)]
+        counts = [_host_elems(t, eb) for t, eb in sized]
+        numel = min(c for c in counts if c is not None)
     gp = _ptr_array(grads) if grads is not None else None
     a = OffloadArgs(int(grad_dtype), int(param_dtype), gp, _ptr(grad_shards), _ptr(params),
                     int(numel), _ptr(workspace), _nbytes(workspace, None), _ptr(state),

@@ -190,6 +190,22 @@ def test_plan_errors(zf):
     assert Z.strerror(-2) and Z.strerror(12345) == "unknown status"
 
 
+def test_every_status_has_its_own_text(zf):
+    """Every value of enum zf_status in include/zf.h maps to a text of its
+    own (never the fallback for an unknown code), and the binding names
+    every one of them."""
+    text = open(os.path.join(INCLUDE, "zf.h")).read()
+    body = re.search(r"enum zf_status\s*\{(.*?)\};", text, flags=re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    codes = {name: int(val) for name, val in re.findall(r"(ZF_[A-Z]+)\s*=\s*(-?\d+)", body)}
+    assert len(codes) >= 8 and codes["ZF_OK"] == 0 and codes["ZF_EUNSUP"] == -7
+    texts = {c: zf.strerror(c) for c in codes.values()}
+    assert all(t and t != "unknown status" for t in texts.values()), texts
+    assert len(set(texts.values())) == len(texts), "two codes share one text"
+    assert {zf.STATUS[c] for c in codes.values()} == set(codes)
+    assert "AVX2" in zf.strerror(codes["ZF_EUNSUP"])
+
+
 def test_step_argument_errors_enqueue_nothing(zf):
     """Invalid arguments are rejected before any HIP call (so this runs on a
     machine without a GPU): NULLs, bad dtypes, misaligned pointers."""
@@ -362,3 +378,41 @@ def test_bucket_plan_matches_oracle(zf):
     assert p.summary.n_groups == p.summary.n_units == 12
     for g, u in zip(p.groups, p.units):
         assert g.padded == u.P and u.P % 2 == 0 and u.P - u.L < 2
+
+
+def test_offload_default_size_counts_host_arrays(zf):
+    """offload_step's default element count is the smallest over every
+    per-element array, the host ones included (h_grad counted in the bytes
+    of what comes down: 4 per element, 2 with down16), so a short host array
+    is refused with ZF_ESIZE before anything is enqueued instead of being
+    overrun by the copies or by CPU-Adam.  Device pointers here are
+    addresses the library never dereferences: every call fails validation."""
+    Z = zf
+    import torch
+    plan = Z.plan_flat([(100, 0)], 2, W.GLOBAL_FLAT, 2)
+    hp = Z.hparams(1e-3)
+    ok = 0x10000
+    ws = torch.zeros(Z.workspace_bytes(plan), dtype=torch.uint8)
+
+    def call(down16=False, h_grad=100, h_master=100, h_avg=100, h_avg_sq=100, h_params=100):
+        h = dict(h_state=np.zeros(256, np.uint8), h_grad=np.zeros(h_grad, np.float32),
+                 h_master=np.zeros(h_master, np.float32), h_exp_avg=np.zeros(h_avg, np.float32),
+                 h_exp_avg_sq=np.zeros(h_avg_sq, np.float32),
+                 h_params=np.zeros(h_params, np.uint16))
+        with pytest.raises(Z.ZfError) as e:
+            Z.offload_step(plan, hp, W.BF16, W.BF16, [ok, ok], ok, ok, ws, ok, stream=0,
+                           down16=down16, **h)
+        return e.value.status
+
+    assert call(h_master=99) == -4
+    assert call(h_avg=99) == -4
+    assert call(h_avg_sq=1) == -4
+    assert call(h_params=99) == -4
+    assert call(h_grad=99) == -4
+    # 16-bit sums come down into h_grad's first 2 bytes per element
+    assert call(down16=True, h_grad=49) == -4
+    # an explicit numel is the caller's statement of every array's size
+    with pytest.raises(Z.ZfError) as e:
+        Z.offload_step(plan, hp, W.BF16, W.BF16, [ok, ok], ok, ok, ws, ok, ok, ok, ok, ok, ok,
+                       ok, stream=0, numel=99)
+    assert e.value.status == -4
