@@ -179,8 +179,11 @@ constexpr int64_t kStateBytes = 256;
 // touched and grad_shards must be given (pass 1 leaves the sums there, in
 // fp32, or with down16 rounded to the gradient dtype in its first Psi'*2
 // bytes, the norm and overflow then taken on the rounded values).
+// noalloc: the workspace is the library's static device scratch array
+// (zf_shard_step_noalloc) instead of args->workspace, which must then be
+// NULL with workspace_size 0.
 int step_enqueue(const zf_plan* plan, const zf_hparams* hp, const zf_step_args* args,
-                 void* stream, bool update, bool down16);
+                 void* stream, bool update, bool down16, bool noalloc = false);
 
 // Binary32 hyperparameters of the update, each rounded once from its double.
 struct UpdateConsts {
@@ -224,6 +227,8 @@ struct zf_plan {
   int64_t ws_partials_offset;   // bytes
   int64_t ws_partials2_offset;  // bytes
   int64_t ws_rs_offset;         // bytes, -1 if the sums are recomputed
+  int64_t ws_partials_bytes;    // bytes of the two partials regions (the
+                                // workspace without the fp32 sums)
   int64_t cached_sums_quads;    // fp32 sums stored cache-allocating (see cached_sums_quads)
 };
 

@@ -174,6 +174,7 @@ extern "C" int zf_plan_flat(const zf_segment* segs, int64_t nseg, int32_t n_rank
   int64_t ws = round_up(p->pass1_tiles * 16, 256);
   p->ws_partials2_offset = ws;
   ws += round_up(l2 * 16, 256);
+  p->ws_partials_bytes = ws;
   p->ws_rs_offset = -1;
   if (s.policy == 1) {
     p->ws_rs_offset = ws;

@@ -29,10 +29,18 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 
 #include "zf_device.h"
 #include "zf_hip_status.h"
 #include "zf_internal.h"
+
+// The workspace of zf_shard_step_noalloc: a static device array that every
+// GPU the library runs on holds from the code object's load until the
+// process ends, each GPU its own copy at its own address.  In host code the
+// name `scratch` only stands for the symbol: its device address comes from
+// hipGetSymbolAddress (noalloc_scratch below), never from the name itself.
+static __device__ __align__(256) unsigned char scratch[ZF_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -505,6 +513,39 @@ int launch_pass2(const zf_plan* plan, int32_t gdt, int32_t pdt, bool mat, bool o
   return hip_ok(hipGetLastError()) ? ZF_OK : ZF_EHIP;
 }
 
+// The device address of `scratch` on the device that runs `s` (the
+// current device for the NULL stream), looked up once per device with that
+// device current and kept until the process ends.  No allocation: a fixed
+// table, one entry per device ordinal.
+constexpr int kMaxDevices = 64;
+
+int noalloc_scratch(hipStream_t s, char** out) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  if (s) {
+    hipDevice_t d = 0;
+    if (!hip_ok(hipStreamGetDevice(s, &d))) return ZF_EHIP;
+    dev = static_cast<int>(d);
+  } else if (!hip_ok(hipGetDevice(&dev))) {
+    return ZF_EHIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return ZF_EINVAL;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    int cur = 0;
+    if (!hip_ok(hipGetDevice(&cur))) return ZF_EHIP;
+    if (cur != dev && !hip_ok(hipSetDevice(dev))) return ZF_EHIP;
+    void* p = nullptr;
+    const bool found = hip_ok(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (!found || !p) return ZF_EHIP;
+    addr[dev] = p;
+  }
+  *out = static_cast<char*>(addr[dev]);
+  return ZF_OK;
+}
+
 int record(void* const* ev, int i, hipStream_t s) {
   if (!ev || !ev[i]) return ZF_OK;
   return hip_ok(hipEventRecord(static_cast<hipEvent_t>(ev[i]), s)) ? ZF_OK : ZF_EHIP;
@@ -533,7 +574,7 @@ extern "C" int zf_state_init(void* d_state, double loss_scale, int32_t dynamic,
 }
 
 int zf::step_enqueue(const zf_plan* plan, const zf_hparams* hp, const zf_step_args* args,
-                     void* stream, bool update, bool down16) {
+                     void* stream, bool update, bool down16, bool noalloc) {
   if (!valid_plan(plan) || !hp || !args) return ZF_EINVAL;
   const zf_plan_summary& sm = plan->summary;
   if (args->grads_reduced != 0 && args->grads_reduced != 1) return ZF_EINVAL;
@@ -562,13 +603,23 @@ int zf::step_enqueue(const zf_plan* plan, const zf_hparams* hp, const zf_step_ar
   if (args->grad_shards && !aligned16(args->grad_shards)) return ZF_EALIGN;
   if (sm.policy == 2 && !args->grad_shards) return ZF_EINVAL;
   if (args->numel < sm.psi_pad) return ZF_ESIZE;
-  if (sm.workspace_bytes > 0) {
+  if (noalloc) {
+    // the static scratch holds the partials, and the fp32 sums only when
+    // the plan materialises them and the caller gives no grad_shards
+    if (args->workspace || args->workspace_size != 0) return ZF_EINVAL;
+    const int64_t need = (plan->ws_rs_offset >= 0 && !args->grad_shards)
+                             ? sm.workspace_bytes
+                             : plan->ws_partials_bytes;
+    if (need > ZF_NOALLOC_SCRATCH_BYTES) return ZF_ESIZE;
+  } else if (sm.workspace_bytes > 0) {
     if (!args->workspace) return ZF_EINVAL;
     if (!aligned16(args->workspace)) return ZF_EALIGN;
     if (args->workspace_size < sm.workspace_bytes) return ZF_ESIZE;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(args->workspace);
+  // every argument is valid: only now touch the runtime for the scratch
+  if (noalloc && (rc = noalloc_scratch(s, &ws)) != ZF_OK) return rc;
   Partial* partials = reinterpret_cast<Partial*>(ws + plan->ws_partials_offset);
   // the sums go to the caller's fp32 gradient shard if given, else to the
   // workspace copy if the plan materialises them, else nowhere (recomputed)
@@ -660,6 +711,11 @@ int zf::step_enqueue(const zf_plan* plan, const zf_hparams* hp, const zf_step_ar
 extern "C" int zf_shard_step(const zf_plan* plan, const zf_hparams* hp,
                              const zf_step_args* args, void* stream) {
   return zf::step_enqueue(plan, hp, args, stream, true, false);
+}
+
+extern "C" int zf_shard_step_noalloc(const zf_plan* plan, const zf_hparams* hp,
+                                     const zf_step_args* args, void* stream) {
+  return zf::step_enqueue(plan, hp, args, stream, true, false, true);
 }
 
 extern "C" int zf_reduce_scatter(const zf_plan* plan, int32_t grad_dtype,

@@ -109,6 +109,8 @@ _SIGNATURES = {
     "zf_state_init": (C.c_int, [C.c_void_p, C.c_double, C.c_int32, C.c_int32, C.c_void_p]),
     "zf_shard_step": (C.c_int, [C.c_void_p, C.POINTER(Hparams), C.POINTER(StepArgs),
                                 C.c_void_p]),
+    "zf_shard_step_noalloc": (C.c_int, [C.c_void_p, C.POINTER(Hparams), C.POINTER(StepArgs),
+                                        C.c_void_p]),
     "zf_reduce_scatter": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(C.c_void_p), C.c_void_p,
                                     C.c_int64, C.c_void_p]),
     "zf_gather": (C.c_int, [C.c_void_p, C.c_int64, C.c_int32, C.POINTER(C.c_void_p),
@@ -298,6 +300,26 @@ def shard_step(plan, hp, grad_dtype, param_dtype, grads, master, exp_avg, exp_av
                     _ptr(state), ev)
     _check(lib.zf_shard_step(_handle(plan), C.byref(hp), C.byref(args), _stream(stream)),
            "zf_shard_step")
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def shard_step_noalloc(plan, hp, grad_dtype, param_dtype, grads, master, exp_avg, exp_avg_sq,
+                       params, state, stream=None, phase_events=None, numel=None,
+                       grad_shards=None, grads_reduced=False):
+    """zf_shard_step_noalloc: shard_step with the library's static scratch
+    as the workspace (no workspace argument; nothing is allocated)."""
+    gp = _ptr_array(grads) if grads is not None else None
+    ev = (C.c_void_p * 4)(*phase_events) if phase_events is not None else None
+    if numel is None:
+        arrays = list(grads or []) + [master, exp_avg, exp_avg_sq, params, grad_shards]
+        numel = min(t.numel() for t in arrays if t is not None and not isinstance(t, int))
+    args = StepArgs(int(grad_dtype), int(param_dtype), gp, _ptr(master), _ptr(exp_avg),
+                    _ptr(exp_avg_sq), _ptr(params), _ptr(grad_shards), int(bool(grads_reduced)),
+                    0, int(numel), None, 0, _ptr(state), ev)
+    _check(lib.zf_shard_step_noalloc(_handle(plan), C.byref(hp), C.byref(args),
+                                     _stream(stream)), "zf_shard_step_noalloc")
 
 
 def reduce_scatter(plan, grad_dtype, grads, rs_out, stream=None, numel=None):

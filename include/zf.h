@@ -277,6 +277,37 @@ typedef struct {
 int zf_shard_step(const zf_plan* plan, const zf_hparams* hp, const zf_step_args* args,
                   void* stream);
 
+/* Bytes of the library's static device scratch array (64 MiB), the
+ * workspace of zf_shard_step_noalloc. */
+#define ZF_NOALLOC_SCRATCH_BYTES (64ll << 20)
+
+/* zf_shard_step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same kernels on the same grids, so the same results bit
+ * for bit, but the workspace is the library's static device array of
+ * ZF_NOALLOC_SCRATCH_BYTES instead of a caller buffer.  The caller still
+ * passes every input and output; args->workspace must be NULL and
+ * args->workspace_size 0.  The call allocates nothing (no hipMalloc, no
+ * host allocation): the array is part of the library's code object, held
+ * on every GPU that runs the library from its load until the process ends,
+ * each GPU its own copy.  The first call on a device looks up the array's
+ * address there (a query, not an allocation); a caller that captures the
+ * call in a graph makes one call on that device before capturing.
+ * Scratch needed: zf_workspace_bytes(plan), less the fp32 sums' share
+ * (Psi' * 4 bytes rounded up to 256) when the plan materialises the sums
+ * (zf_plan_summary.policy 1) and args->grad_shards is given, since pass 1
+ * then writes the sums there; a plan that needs more than
+ * ZF_NOALLOC_SCRATCH_BYTES (policy 1 without grad_shards above about 16.7M
+ * elements, or any plan above about 8.5e9 elements) gets ZF_ESIZE before
+ * anything is enqueued.  Every scratch byte a call reads it first writes
+ * in the same call, so nothing needs clearing, but every call on one GPU
+ * shares that GPU's one array: calls that overlap on a GPU (two streams,
+ * two threads) race and must be serialised by the caller.  Errors: as
+ * zf_shard_step, plus ZF_EINVAL (workspace given; a device ordinal >= 64)
+ * and ZF_ESIZE (scratch too small). */
+int zf_shard_step_noalloc(const zf_plan* plan, const zf_hparams* hp, const zf_step_args* args,
+                          void* stream);
+
 /* The reduce-scatter alone ([L13] 3.2; [F7] gradient hook): rs_out[p] is
  * the fixed-order binary32 sum of the N replicas at p, for every p < Psi'
  * (each rank's shard in its padded-flat place).  numel: elements of every

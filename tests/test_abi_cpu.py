@@ -416,3 +416,42 @@ def test_offload_default_size_counts_host_arrays(zf):
         Z.offload_step(plan, hp, W.BF16, W.BF16, [ok, ok], ok, ok, ws, ok, ok, ok, ok, ok, ok,
                        ok, stream=0, numel=99)
     assert e.value.status == -4
+
+
+def test_noalloc_step_refuses_before_enqueueing(zf):
+    """zf_shard_step_noalloc checks its arguments and the scratch it needs
+    before it touches the HIP runtime (so this runs without a GPU): a
+    caller workspace is refused, and a plan whose workspace does not fit the
+    static scratch gets ZF_ESIZE, unless the sums go to the caller's fp32
+    gradient shards.  Only failing calls are made here."""
+    Z = zf
+    hp = Z.hparams(1e-3)
+    ok = 0x10000
+    cap = Z.NOALLOC_SCRATCH_BYTES
+    text = open(os.path.join(INCLUDE, "zf.h")).read()
+    assert re.search(r"#define ZF_NOALLOC_SCRATCH_BYTES \(64ll << 20\)", text)
+
+    def call(plan, n, **kw):
+        grads = (C.c_void_p * plan.n_ranks)(*([ok] * plan.n_ranks))
+        d = dict(grad_dtype=2, param_dtype=2, grads=grads, master=ok, exp_avg=ok,
+                 exp_avg_sq=ok, params=ok, grad_shards=None, grads_reduced=0, reserved=0,
+                 numel=n, workspace=None, workspace_size=0, state=ok, phase_events=None)
+        d.update(kw)
+        a = Z.StepArgs(*[d[f] for f, _ in Z.StepArgs._fields_])
+        return Z.lib.zf_shard_step_noalloc(plan.handle, C.byref(hp), C.byref(a), None)
+
+    # N = 8 materialises the sums: 20M elements need 80 MB of them
+    n = 20_000_000
+    big = Z.plan_flat([(n, 0)], 8, W.GLOBAL_FLAT, 2)
+    assert big.summary.policy == 1 and big.summary.workspace_bytes > cap
+    assert call(big, n) == -4
+    assert call(big, n, workspace=ok, workspace_size=big.summary.workspace_bytes) == -1
+    assert call(big, n, workspace_size=16) == -1
+    assert call(big, n - 1, grad_shards=ok) == -4   # the usual checks still come first
+    assert call(big, n, master=ok + 4, grad_shards=ok) == -2
+    # the partials alone: past about 8.5e9 elements they do not fit either
+    huge_n = 9_000_000_000
+    huge = Z.plan_flat([(huge_n, 0)], 2, W.GLOBAL_FLAT, 2)
+    assert huge.summary.policy == 0 and huge.summary.workspace_bytes > cap
+    assert call(huge, huge_n) == -4
+    assert Z.lib.zf_shard_step_noalloc(None, C.byref(hp), None, None) == -1
