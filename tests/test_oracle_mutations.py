@@ -65,6 +65,15 @@ MUTANTS = [
     ("unit gather transposes rank and offset",
      "unit_buf[(int64_t)r * units[u].S + j] = param_shards[r][units[u].M + j];",
      "unit_buf[j * n_ranks + r] = param_shards[r][units[u].M + j];"),
+    ("fp32 draws scaled by sigma twice",
+     "for (i = 0; i < n; ++i) dst[i] = or_normal_z(st, logical_base + i) * sf;",
+     "for (i = 0; i < n; ++i) dst[i] = or_normal_z(st, logical_base + i) * sf * sf;"),
+    ("fp32 draws multiplied by sigma in double",
+     "for (i = 0; i < n; ++i) dst[i] = or_normal_z(st, logical_base + i) * sf;",
+     "for (i = 0; i < n; ++i) dst[i] = (float)((double)or_normal_z(st, logical_base + i) * sigma);"),
+    ("fp32 draws ignore sigma",
+     "for (i = 0; i < n; ++i) dst[i] = or_normal_z(st, logical_base + i) * sf;",
+     "for (i = 0; i < n; ++i) dst[i] = or_normal_z(st, logical_base + i) * (sf / sf);"),
     ("Irwin-Hall centred on the wrong mean",
      "return (float)(sum - 393210) / 65536.0f;", "return (float)(sum - 393216) / 65536.0f;"),
     ("FSDP2 chunk rows rounded the wrong way",

@@ -212,6 +212,29 @@ def test_gen16_is_rne_of_scaled_normal(orc):
     assert np.array_equal(hb, xb.view(np.uint16))
 
 
+def test_gen32_is_binary32_product_of_z_and_sigma(orc):
+    """An fp32 draw is one binary32 product f32(z) * f32(sigma), with z the
+    Irwin-Hall value pinned above: checked against numpy's float32
+    multiplication for the sigmas the workloads use (master init 0.02, the
+    654M gradient sigma) and others, at several logical offsets.  A sigma
+    applied twice, dropped, or multiplied in double and rounded afterwards
+    disagrees with numpy on many of these draws."""
+    n = 60_000
+    for seed, stream, base in ((5, W.STREAM_MASTER, 0), (2, W.STREAM_MASTER, 73_000_000),
+                               (11, 12345, 2**33 + 7)):
+        z = O.normal_z(seed, stream, range(base, base + n))
+        for sigma in (0.02, 0.5, 1e-3, 1.6586e-4, 3.0, 1.0):
+            want = z * _f32(sigma)
+            got = O.gen32(n, seed, stream, base, sigma)
+            assert want.dtype == np.float32
+            assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), (seed, sigma)
+    # the product really is rounded in binary32: for sigma = 0.02 a product
+    # in binary64 rounded once to binary32 differs from it on some draws,
+    # so the pin above tells the two apart
+    z = O.normal_z(5, W.STREAM_MASTER, range(n)).astype(np.float64)
+    assert np.any((z * 0.02).astype(np.float32) != (z.astype(np.float32) * _f32(0.02)))
+
+
 # ----------------------------------------------------------------- casts ----
 def _f32_patterns():
     """All 2^16 upper halves crossed with 64 lower halves (zero, round-bit and
