@@ -3,6 +3,12 @@
 libzf.so         the step (planner + kernels + C ABI, include/zf.h) and the
                  host side of ZeRO-Offload (CPU-Adam, the offload step)
 libzf_inputs.so  the seeded input generator (include/zf_inputs.h)
+libzf_window_test.so
+                 a test build of the step (planner + step kernels, the same
+                 C ABI) whose memory-side cache window is 1 MiB for every
+                 plan, so that the tests can run the split of pass 1's sum
+                 stores (non-temporal below the window, cache-allocating in
+                 it) and the update pass's backward walk on small plans
 
 Flags that matter for the arithmetic contract:
   -ffp-contract=off                        no a*b+c -> fma fusion
@@ -20,6 +26,7 @@ INCLUDE = os.path.join(ROOT, "include")
 
 LIB_ZF = os.path.join(PKG, "libzf.so")
 LIB_INPUTS = os.path.join(PKG, "libzf_inputs.so")
+LIB_WINDOW_TEST = os.path.join(PKG, "libzf_window_test.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -31,10 +38,10 @@ FLAGS = [
 ]
 
 
-def _hipcc(out, sources, host_sources=()):
+def _hipcc(out, sources, host_sources=(), defines=()):
     """Link `sources` (HIP) and `host_sources` (plain host C++) into `out`."""
     tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-o", tmp]
+    cmd = [HIPCC, *FLAGS, *defines, "-o", tmp]
     if host_sources:
         cmd += ["-x", "c++", *host_sources]
     cmd += ["-x", "hip", *sources]
@@ -44,12 +51,14 @@ def _hipcc(out, sources, host_sources=()):
 
 
 def build():
-    """Build both libraries; returns their paths."""
+    """Build the libraries; returns their paths."""
     zf = _hipcc(LIB_ZF, [os.path.join(CSRC, f) for f in
                          ("zf_step.hip", "zf_backward.hip", "zf_gather.hip", "zf_offload.hip")],
                 [os.path.join(CSRC, f) for f in ("zf_plan.cpp", "zf_cpu_adam.cpp")])
     inputs = _hipcc(LIB_INPUTS, [os.path.join(CSRC, "zf_inputs.hip")])
-    return zf, inputs
+    window = _hipcc(LIB_WINDOW_TEST, [os.path.join(CSRC, "zf_step.hip")],
+                    [os.path.join(CSRC, "zf_plan.cpp")], defines=["-DZF_TEST_CACHED_SUMS_MB=1"])
+    return zf, inputs, window
 
 
 if __name__ == "__main__":

@@ -57,12 +57,6 @@ constexpr uint64_t kPlanMagic = 0x7a665f706c616e31ull;  // "zf_plan1"
 //    measured within 1% either way and keeps one code path).
 //    The cap is dynamic LDS that the kernel never touches, sized so that no
 //    more blocks fit in a CU's 160 KiB.
-// Builds may pin a choice for measurement: ZF_FORCE_UNR1, ZF_FORCE_UNR2 (1|2),
-// ZF_FORCE_MAP1 (0|1), ZF_PASS1_NT_LOADS (0|1), ZF_FORCE_OCC1, ZF_FORCE_OCC2
-// (blocks per CU, 0: no cap).
-#ifndef ZF_PASS1_NT_LOADS
-#define ZF_PASS1_NT_LOADS 1
-#endif
 
 constexpr int kThreads = 256;        // 4 wave64 per block
 constexpr int kQuadsPerUnr = 2;      // pass 1: quads (4 elements) per thread per tile step
@@ -72,32 +66,9 @@ constexpr int kQuadsPass2 = 1;       // the update pass: quads per thread per ti
 constexpr int kThreadsPass2Recompute = 128;
 constexpr int kThreadsPass2Mat = 256;
 constexpr int threads_pass2(bool mat) { return mat ? kThreadsPass2Mat : kThreadsPass2Recompute; }
-inline int unr_pass1(int n_ranks) {
-#ifdef ZF_FORCE_UNR1
-  (void)n_ranks;
-  return ZF_FORCE_UNR1;
-#else
-  return (n_ranks <= 2 || n_ranks >= 6) ? 1 : 2;
-#endif
-}
-inline int map_pass1(int n_ranks) {
-#ifdef ZF_FORCE_MAP1
-  (void)n_ranks;
-  return ZF_FORCE_MAP1;
-#else
-  return n_ranks <= 4 ? 1 : 0;
-#endif
-}
-inline int unr_pass2(int n_ranks, int64_t psi_pad, bool materialize) {
-  (void)n_ranks;
-  (void)psi_pad;
-  (void)materialize;
-#ifdef ZF_FORCE_UNR2
-  return ZF_FORCE_UNR2;
-#else
-  return 1;
-#endif
-}
+inline int unr_pass1(int n_ranks) { return (n_ranks <= 2 || n_ranks >= 6) ? 1 : 2; }
+inline int map_pass1(int n_ranks) { return n_ranks <= 4 ? 1 : 0; }
+inline int unr_pass2() { return 1; }
 constexpr int kMaxLevel2Blocks = 1024;
 
 // Materialised sums and the memory-side cache.  Pass 1 stores the fp32 sums
@@ -113,11 +84,14 @@ constexpr int kMaxLevel2Blocks = 1024;
 // MiB and of the whole sums did worse at most sizes.
 constexpr int64_t kCachedSumsBytes = 256ll << 20;
 constexpr int64_t kCachedSumsLimit = 448ll << 20;
-// quads of the window for a plan of psi_pad elements (0: no window)
+// quads of the window for a plan of psi_pad elements (0: no window).  A
+// test build (ZF_TEST_CACHED_SUMS_MB) gives every plan a window of that many
+// MiB, so that small plans split their sums between non-temporal and
+// cache-allocating stores the way the 73M-parameter plan at N = 8 does.
 inline int64_t cached_sums_quads(int64_t psi_pad) {
-#ifdef ZF_FORCE_CACHED_SUMS_MB
+#ifdef ZF_TEST_CACHED_SUMS_MB
   (void)psi_pad;
-  return (int64_t)ZF_FORCE_CACHED_SUMS_MB * (1 << 16);
+  return (int64_t)ZF_TEST_CACHED_SUMS_MB * (1 << 16);
 #else
   if (psi_pad * 4 > kCachedSumsLimit) return 0;
   return kCachedSumsBytes / 16;
@@ -129,24 +103,12 @@ inline int64_t cached_sums_quads(int64_t psi_pad) {
 // covers the kernels' own few hundred bytes of static LDS).
 constexpr int64_t kLdsPerCU = 160 * 1024;
 inline int occ_pass1(int n_ranks, bool writes_sums) {
-#ifdef ZF_FORCE_OCC1
-  (void)n_ranks;
-  (void)writes_sums;
-  return ZF_FORCE_OCC1;
-#else
   if (!writes_sums || n_ranks < 6) return 0;
   return n_ranks > 8 ? 4 : 3;
-#endif
 }
 inline int occ_pass2(bool mat, bool cached_sums) {
-#ifdef ZF_FORCE_OCC2
-  (void)mat;
-  (void)cached_sums;
-  return ZF_FORCE_OCC2;
-#else
   if (!mat) return 5;  // 128-thread blocks: 10 waves per CU
   return cached_sums ? 4 : 3;
-#endif
 }
 inline uint32_t occupancy_lds(int blocks_per_cu) {
   if (blocks_per_cu <= 0) return 0;

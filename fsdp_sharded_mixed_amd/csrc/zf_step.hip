@@ -90,7 +90,7 @@ __device__ __forceinline__ void pass1_quads(const Pass1Args& a, int nr, int64_t 
     ok[h] = FULL || qi[h] < nq;
   }
   f32x4 acc[Q];
-  sum_quads<NR, DT, ZF_PASS1_NT_LOADS != 0, Q>(a.g, nr, qi, ok, acc);
+  sum_quads<NR, DT, true, Q>(a.g, nr, qi, ok, acc);
 #pragma unroll
   for (int h = 0; h < Q; ++h) {
     if (!ok[h]) continue;

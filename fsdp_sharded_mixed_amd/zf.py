@@ -133,12 +133,14 @@ _SIGNATURES = {
 }
 
 
-def _load():
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run fsdp_sharded_mixed_amd/build.py "
+def _load(path=LIB_PATH, names=None):
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run fsdp_sharded_mixed_amd/build.py "
                           "(or __graft_entry__.build())")
-    lib = C.CDLL(LIB_PATH)
+    lib = C.CDLL(path)
     for name, (res, args) in _SIGNATURES.items():
+        if names is not None and name not in names:
+            continue
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
@@ -146,6 +148,12 @@ def _load():
 
 
 lib = _load()
+
+
+def load_library(path, names):
+    """Another build of the library (a test build), with the signatures of
+    the named calls set; its plans and state blocks are its own."""
+    return _load(path, names)
 
 
 def strerror(status):

@@ -31,6 +31,12 @@ def bits32(t):
     return t.detach().view(torch.int32).cpu().numpy().view(np.uint32)
 
 
+def bits_view(t):
+    """A device tensor's bits as integers of its element size (bitwise
+    comparison with torch.equal: NaN payloads and signed zeros count)."""
+    return t.view(torch.int32 if t.element_size() == 4 else torch.int16)
+
+
 def f32(t):
     return t.detach().cpu().numpy()
 

@@ -1,0 +1,337 @@
+"""Element-by-element GPU parity at the workloads' full sizes: every
+element of the 73M decoder at N = 8 (ten steps), the 654M decoder at N = 2
+(five steps), the 4.06B decoder at N = 2 (four steps, the second skipped
+by an injected +inf), and the 2.1B decoder under ZeRO-3 and under FSDP2
+(three steps each, every unit gather), compared with the CPU oracle after
+every step, in the launch configuration the bench times.
+
+The oracle side holds the full state on the host.  FullOracle carries
+every element through the oracle's own functions, split into index ranges
+over a thread pool (each range is independent: the generator is keyed by
+logical index and the update is per element): the master from the
+oracle's generator, the exact global squared norm and overflow flag by
+regeneration (range partials added in order), the fixed-order
+reduce-scatter sums by regeneration, the binary32 AdamW update and the
+nearest-even cast.  These workloads have no padding (every FlatParameter
+length is a multiple of N), so the padded flat index of the device arrays
+is the logical index.  test_full_oracle_matches_single_threaded pins this
+harness to the plain single-threaded oracle step on the CPU.
+
+Bars: the reduce-scatter sums bit for bit; master, exp_avg, exp_avg_sq
+within 4 ulp (relative 1e-6); the 16-bit parameters and every gathered
+unit within 1 ulp; the step result (overflow, skip, t, loss scale) exactly
+and the norm within 1e-5.  Each step reports the share of elements that
+match bit for bit.
+"""
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from fsdp_sharded_mixed_amd import workloads as W
+from tests import gpu_common as G
+from tests import oracle_inputs as OI
+
+CHUNK = 1 << 21        # elements per host task
+CMP_CHUNK = 1 << 25    # elements per device-to-host comparison slice
+
+
+class FullOracle:
+    """The full state of a workload without padding (the padded index
+    equals the logical index), stepped element by element by the oracle
+    over a thread pool."""
+
+    def __init__(self, w, threads=None):
+        _, psi, psi_pad = OI.plan(w)
+        assert psi == psi_pad == w.psi and not w.backward_rs and not w.offload
+        self.w, self.psi = w, w.psi
+        self.edges = list(range(0, w.psi, CHUNK)) + [w.psi]
+        self.pool = ThreadPoolExecutor(threads or G.POOL_THREADS)
+        self.p = np.empty(w.psi, np.float32)
+
+        def init(c):
+            a, b = self.edges[c], self.edges[c + 1]
+            self.p[a:b] = O.gen32(b - a, w.seed, W.STREAM_MASTER, a, w.master_sigma)
+
+        list(self.pool.map(init, range(len(self.edges) - 1)))
+        if w.norm_weights_one:
+            for a, b in w.norm_ranges():
+                self.p[a:b] = 1.0
+        self.m = np.zeros(w.psi, np.float32)
+        self.v = np.zeros(w.psi, np.float32)
+        self.hp = OI.hparams(w)
+        self.st = OI.scale_state(w)
+        self.step_no = 0
+
+    def close(self):
+        self.pool.shutdown()
+
+    def step(self, inject_index=None, keep_sums=False):
+        """One step: returns (result, sums or None).  keep_sums keeps every
+        reduce-scatter sum of the step (also of a skipped one)."""
+        w = self.w
+        self.step_no += 1
+        scale = self.st.loss_scale
+        inj = None
+        if inject_index is not None:
+            inj = O.Inject(step=self.step_no, replica=w.inject_replica, index=int(inject_index),
+                           bits=OI.inf_bits(w.grad_dtype))
+        ss, bad = G.regen_sumsq_threaded(w, self.step_no, scale, self.psi, inj)
+        sc, res = O.finish(ss, bad, w.n_ranks, self.hp, self.st)
+        sums = np.empty(self.psi, np.float32) if keep_sums else None
+        if res.skipped and not keep_sums:
+            return res, None
+
+        def part(c):
+            a, b = self.edges[c], self.edges[c + 1]
+            acc = O.regen_accum_acc(w.grad_dtype, w.n_ranks, 1, W.ACCUM_REDUCE_EACH, w.seed,
+                                    self.step_no, w.sigma, scale, np.arange(a, b, dtype=np.int64),
+                                    inj)
+            if sums is not None:
+                sums[a:b] = acc
+            if not res.skipped:
+                O.adamw_array(acc, sc, self.p[a:b], self.m[a:b], self.v[a:b])
+
+        list(self.pool.map(part, range(len(self.edges) - 1)))
+        return res, sums
+
+
+def _chunks(pool, n, fn):
+    """fn(a, b) over [0, n) in slices of CMP_CHUNK elements, on the pool."""
+    return list(pool.map(lambda a: fn(a, min(n, a + CMP_CHUNK)), range(0, n, CMP_CHUNK)))
+
+
+def compare_f32(pool, t, ref, what, max_ulp=4):
+    """Every element of device fp32 array t against ref: within max_ulp
+    ulp.  Returns (share bit-identical, worst ulp)."""
+    def one(a, b):
+        got = t[a:b].cpu().numpy()
+        want = ref[a:b]
+        diff = got.view(np.uint32) != want.view(np.uint32)
+        nd = int(diff.sum())
+        worst = 0
+        if nd:
+            d = G.ulp_distance(got[diff], want[diff])
+            k = int(d.argmax())
+            worst = int(d[k])
+            assert worst <= max_ulp, \
+                f"{what}: {worst} ulp at {a + int(np.flatnonzero(diff)[k])}"
+        return (b - a) - nd, worst
+
+    parts = _chunks(pool, ref.size, one)
+    return sum(x[0] for x in parts) / ref.size, max(x[1] for x in parts)
+
+
+def compare_bits32(pool, t, ref, what):
+    """Every element bit for bit (NaN payloads included)."""
+    def one(a, b):
+        bad = np.flatnonzero(t[a:b].cpu().numpy().view(np.uint32) != ref[a:b].view(np.uint32))
+        assert bad.size == 0, f"{what}: {bad.size} elements differ, first at {a + int(bad[0])}"
+
+    _chunks(pool, ref.size, one)
+
+
+def compare_16(pool, t, p_ref, dtype, what):
+    """Every 16-bit element of device array t within 1 ulp of RNE16 of the
+    oracle's fp32 values p_ref; returns the share that is bit-identical."""
+    def one(a, b):
+        got = t[a:b].view(torch.int16).cpu().numpy().view(np.uint16)
+        diff = got != O.narrow(dtype, p_ref[a:b])
+        nd = int(diff.sum())
+        if nd:
+            want = O.narrow(dtype, p_ref[a:b])
+            assert G.ulp16_distance(got[diff], want[diff]).max() <= 1, what
+        return (b - a) - nd
+
+    return sum(_chunks(pool, p_ref.size, one)) / p_ref.size
+
+
+def check_state(dev, orc, what):
+    em, wm = compare_f32(orc.pool, dev.master, orc.p, f"{what} master")
+    ea, wa = compare_f32(orc.pool, dev.exp_avg, orc.m, f"{what} exp_avg")
+    ev, wv = compare_f32(orc.pool, dev.exp_avg_sq, orc.v, f"{what} exp_avg_sq")
+    out = {"master": round(em, 6), "exp_avg": round(ea, 6), "exp_avg_sq": round(ev, 6),
+           "worst_ulp": max(wm, wa, wv)}
+    if dev.params is not None:
+        out["params"] = round(compare_16(orc.pool, dev.params, orc.p, dev.w.param_dtype,
+                                         f"{what} params"), 6)
+    return out
+
+
+def check_gathers(dev, orc, what):
+    """ZeRO-3: every unit gathered into the reused unit buffer; FSDP2: every
+    FSDP unit cast-gathered into the reused group buffer.  Each against
+    RNE16 of the oracle's master over the unit's logical range (no padding,
+    so a unit's padded and logical lengths agree)."""
+    w, shares = dev.w, []
+    if w.fp32_params:
+        for g, info in enumerate(dev.plan.groups):
+            buf = dev.gather_cast(g)
+            lam0 = dev.plan.units[info.first_unit].lam
+            shares.append(compare_16(orc.pool, buf, orc.p[lam0:lam0 + info.numel],
+                                     w.param_dtype, f"{what} group {g}"))
+    elif w.stage == 3:
+        for u, info in enumerate(dev.plan.units):
+            assert info.P == info.L
+            buf = dev.gather(u)
+            shares.append(compare_16(orc.pool, buf, orc.p[info.lam:info.lam + info.L],
+                                     w.param_dtype, f"{what} unit {u}"))
+    return min(shares) if shares else None
+
+
+def test_full_oracle_matches_single_threaded(orc):
+    """CPU pin of the harness: FullOracle (range-parallel regeneration and
+    update) tracks the oracle's own single-threaded step on a whole padded
+    flat (O.zero_step via OracleRun) for three steps at N = 4 on 5,000,004
+    elements with a norm weight range and clipping active: the same
+    results, the norm to within rounding, the state and the sums within
+    4 ulp and almost all bit for bit."""
+    segs = [W.Segment("w", 4_000_000, 0), W.Segment("n", 4, 0, W.KIND_NORM),
+            W.Segment("b", 1_000_000, 0)]
+    w = W.Workload(name="flat-5m-n4", description="", segments=segs, n_ranks=4,
+                   layout=W.GLOBAL_FLAT, stage=2, grad_dtype=W.BF16, param_dtype=W.BF16,
+                   sigma=2e-3, loss_scale=1.0, dynamic=False, lr=1e-3, steps=3, seed=13,
+                   norm_weights_one=True, max_norm=1.0)
+    full = FullOracle(w, threads=4)
+    ref = OI.OracleRun(w)
+    try:
+        for k in range(1, 4):
+            grads = OI.replicas(w, ref.units, ref.psi_pad, k, ref.st.loss_scale)
+            acc_ref = np.concatenate(O.reduce_scatter(w.grad_dtype, w.n_ranks, ref.units, grads))
+            r_ref = ref.step(grads)
+            r_full, sums = full.step(keep_sums=True)
+            assert (r_full.skipped, r_full.t, r_full.scale_next) == \
+                (r_ref.skipped, r_ref.t, r_ref.scale_next)
+            assert abs(r_full.norm - r_ref.norm) <= 1e-12 * r_ref.norm and r_ref.coef < 1.0
+            # the global flat has no padding: rank r's shard is [r*S, (r+1)*S)
+            assert np.array_equal(sums.view(np.uint32), acc_ref.view(np.uint32))
+            for mine, theirs in ((full.p, ref.master), (full.m, ref.m), (full.v, ref.v)):
+                share = G.assert_state_close("full oracle", mine, np.concatenate(theirs))
+                assert share > 0.999
+    finally:
+        full.close()
+
+
+@pytest.fixture(scope="module")
+def R():
+    from fsdp_sharded_mixed_amd import runner
+    assert torch.cuda.is_available()
+    return runner
+
+
+def run_full(R, name, twin_sums=False, rs_first_step=True):
+    """Every step of workload `name` on the device against FullOracle, every
+    element of the state, the 16-bit parameters and every gathered unit.
+
+    twin_sums: a second device run steps in lockstep on the same replicas
+    with fp32 gradient shards given, where the same kernels write the sums
+    that the first run keeps in its workspace; its sums are compared with
+    the oracle's every step and its state with the first run's.
+    rs_first_step: at step 1 the reduce-scatter alone (zf_reduce_scatter)
+    into a full fp32 buffer, compared with the oracle's sums.  FSDP2 keeps
+    the sums in its resident fp32 gradient shards: compared every step."""
+    from fsdp_sharded_mixed_amd import inputs as I
+    from fsdp_sharded_mixed_amd import zf
+    torch.cuda.empty_cache()
+    w = W.get(name)
+    G.say(f"full parity {w.name}: Psi={w.psi:,} N={w.n_ranks} stage={w.stage}, {w.steps} steps")
+    dev = R.DeviceRun(w)
+    twin = None
+    if twin_sums:
+        twin = R.DeviceRun(w, grads=False)
+        twin.grads = dev.grads
+        twin.grad_shards = torch.zeros(dev.psi_pad, dtype=torch.float32, device=dev.device)
+        twin.init_state()
+    dev.init_state()
+    inj = I.inject_index(w, w.psi) if w.inject_step else None
+    orc = FullOracle(w)
+    trace = []
+    try:
+        compare_bits32(orc.pool, dev.master, orc.p, "initial master")
+        for k in range(1, w.steps + 1):
+            dev.fill_grads(k, dev.loss_scale)
+            if w.inject_step == k:
+                dev.inject_inf()
+            rs = None
+            if rs_first_step and k == 1 and not w.fp32_params:
+                rs = torch.empty(dev.psi_pad, dtype=torch.float32, device=dev.device)
+                zf.reduce_scatter(dev.plan, w.grad_dtype, dev.grads, rs)
+            dev.step()
+            if twin is not None:
+                twin.step()
+            res_d = dev.result()
+            dev.loss_scale = res_d.scale_next
+            keep = twin is not None or w.fp32_params or rs is not None
+            res_o, sums = orc.step(inject_index=inj if w.inject_step == k else None,
+                                   keep_sums=keep)
+            G.assert_result_matches(res_d, res_o, f"{w.name} step {k}")
+            src = twin.grad_shards if twin is not None else \
+                (dev.grad_shards if w.fp32_params else rs)
+            if sums is not None:
+                compare_bits32(orc.pool, src, sums, f"{w.name} step {k} reduce-scatter sums")
+            del rs, sums
+            if twin is not None:
+                for nm in ("master", "exp_avg", "exp_avg_sq", "params"):
+                    assert torch.equal(G.bits_view(getattr(dev, nm)),
+                                       G.bits_view(getattr(twin, nm))), f"step {k} {nm}"
+            shares = check_state(dev, orc, f"{w.name} step {k}")
+            g = check_gathers(dev, orc, f"{w.name} step {k}")
+            if g is not None:
+                shares["gathers"] = round(g, 6)
+            trace.append((k, res_d.skipped, res_d.t, res_d.scale_used, res_d.scale_next,
+                          res_d.norm, res_d.coef))
+            G.say(f"  step {k}: skipped={res_d.skipped} t={res_d.t} S={res_d.scale_used}->"
+                  f"{res_d.scale_next} norm={res_d.norm:.6f} (oracle {res_o.norm:.6f}) "
+                  f"coef={res_d.coef:.6f} sums {'bit-exact' if keep else '-'}; "
+                  f"bit-identical shares {shares}")
+    finally:
+        orc.close()
+    return trace
+
+
+@pytest.mark.gpu
+def test_llama73m_n8_every_element(R):
+    """73M decoder, N = 8 (the sums materialised, the last 256 MiB of them
+    in the memory-side cache window: pass 1's tiles split between
+    non-temporal and cache-allocating stores, the update pass walking
+    backward), ten steps, clipped each step; a twin run with fp32 gradient
+    shards exposes the sums of every step."""
+    trace = run_full(R, "llama-73m-n8", twin_sums=True)
+    assert all(t[1] == 0 and abs(t[5] - 3.03) < 0.1 and t[6] < 1.0 for t in trace)
+
+
+@pytest.mark.gpu
+def test_llama654m_n2_every_element(R):
+    """654M decoder, N = 2 (the update pass recomputes the sums from the
+    replicas), five steps with clipping active."""
+    trace = run_full(R, "llama-654m-n2")
+    assert all(t[1] == 0 and abs(t[5] - 3.0) < 0.1 and t[6] < 1.0 for t in trace)
+
+
+@pytest.mark.gpu
+def test_llama2b_zero3_every_element(R):
+    """2.1B decoder as 34 FSDP units, N = 2, stage 3: resident 16-bit shards
+    and every unit gathered into one reused buffer every step."""
+    trace = run_full(R, "llama-2.1b-n2-zero3")
+    assert all(t[1] == 0 and t[6] < 1.0 for t in trace)
+
+
+@pytest.mark.gpu
+def test_llama2b_fsdp2_every_element(R):
+    """2.1B decoder under FSDP2: per-parameter dim-0 shards over N = 2, fp32
+    parameters, the sums in resident fp32 gradient shards (every step, bit
+    for bit), all 34 FSDP units cast-gathered every step."""
+    trace = run_full(R, "llama-2.1b-n2-fsdp2")
+    assert all(t[1] == 0 for t in trace)
+
+
+@pytest.mark.gpu
+def test_llama4b_n2_every_element(R):
+    """4.06B decoder, N = 2, fp16 under dynamic loss scaling with +inf in
+    replica 1 at step 2: step 2 is skipped (state untouched, every element)
+    and S halves 32768 -> 16384; steps 1, 3, 4 applied."""
+    trace = run_full(R, "llama-4.06b-n2")
+    assert [(t[1], t[2]) for t in trace] == [(0, 1), (1, 1), (0, 2), (0, 3)]
+    assert trace[1][3] == 32768.0 and trace[1][4] == 16384.0 and trace[2][3] == 16384.0
