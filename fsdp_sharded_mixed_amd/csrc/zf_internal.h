@@ -68,7 +68,6 @@ constexpr int kThreadsPass2Mat = 256;
 constexpr int threads_pass2(bool mat) { return mat ? kThreadsPass2Mat : kThreadsPass2Recompute; }
 inline int unr_pass1(int n_ranks) { return (n_ranks <= 2 || n_ranks >= 6) ? 1 : 2; }
 inline int map_pass1(int n_ranks) { return n_ranks <= 4 ? 1 : 0; }
-inline int unr_pass2() { return 1; }
 constexpr int kMaxLevel2Blocks = 1024;
 
 // Materialised sums and the memory-side cache.  Pass 1 stores the fp32 sums
@@ -182,7 +181,7 @@ struct zf_plan {
   zf_plan_summary summary;
   std::vector<zf_unit_info> units;
   std::vector<zf_group_info> groups;
-  int32_t unr1, unr2;           // tile steps of pass 1 / the update pass per thread
+  int32_t unr1;                 // tile steps of pass 1 per thread
   int32_t pass1_map;            // pass-1 tile walk (0 shared window, 1 XCD-contiguous)
   int64_t pass1_tiles;          // pass-1 blocks = squared-norm partials
   int32_t level2_blocks;        // blocks reducing the partials
@@ -196,10 +195,10 @@ struct zf_plan {
 
 namespace zf {
 // The update pass's blocks for a plan: one tile of threads_pass2(mat) x
-// kQuadsPass2 x unr2 quads each (at least one block; the last one also
+// kQuadsPass2 quads each (at least one block; the last one also
 // takes the ragged tail).
 inline int64_t pass2_tiles(const zf_plan* p, bool mat) {
-  const int64_t q = (int64_t)threads_pass2(mat) * kQuadsPass2 * p->unr2;
+  const int64_t q = (int64_t)threads_pass2(mat) * kQuadsPass2;
   const int64_t t = (p->summary.psi_pad / 4 + q - 1) / q;
   return t < 1 ? 1 : t;
 }

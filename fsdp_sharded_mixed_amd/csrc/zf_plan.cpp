@@ -157,7 +157,6 @@ extern "C" int zf_plan_flat(const zf_segment* segs, int64_t nseg, int32_t n_rank
   p->cached_sums_quads = zf::cached_sums_quads(s.psi_pad);
   s.cached_sums_bytes =
       s.policy != 0 ? std::min(s.psi_pad * 4, p->cached_sums_quads * 16) : 0;
-  p->unr2 = zf::unr_pass2();
   const int64_t q1 = (int64_t)zf::kThreads * zf::kQuadsPerUnr * p->unr1;
   const int64_t t1 = (nq + q1 - 1) / q1;
   p->pass1_tiles = t1 < 1 ? 1 : t1;

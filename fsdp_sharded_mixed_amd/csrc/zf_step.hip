@@ -462,9 +462,9 @@ int launch_pass1(const zf_plan* plan, int32_t dt, hipStream_t s, const Pass1Args
   return hip_ok(hipGetLastError()) ? ZF_OK : ZF_EHIP;
 }
 
-template <int GDT, int PDT, int U, bool OUT16>
+template <int GDT, int PDT, bool OUT16>
 void launch_pass2_nr(int nr, bool mat, dim3 grid, hipStream_t s, const Pass2Args& a) {
-  constexpr int Q = zf::kQuadsPass2 * U;
+  constexpr int Q = zf::kQuadsPass2;
   const uint32_t lds = zf::occupancy_lds(zf::occ_pass2(mat, a.reverse != 0));
   const dim3 block((uint32_t)zf::threads_pass2(mat));
   if (mat) {
@@ -487,20 +487,19 @@ void launch_pass2_nr(int nr, bool mat, dim3 grid, hipStream_t s, const Pass2Args
 #undef ZF_P2
 }
 
-template <int U>
-void launch_pass2_u(int nr, int32_t gdt, int32_t pdt, bool mat, bool out16, dim3 grid,
-                    hipStream_t s, const Pass2Args& a) {
+void launch_pass2_dt(int nr, int32_t gdt, int32_t pdt, bool mat, bool out16, dim3 grid,
+                     hipStream_t s, const Pass2Args& a) {
   if (!out16) {  // fp32 parameters: no 16-bit copy, the param dtype is unused
-    if (gdt == ZF_BF16) launch_pass2_nr<ZF_BF16, ZF_BF16, U, false>(nr, mat, grid, s, a);
-    else launch_pass2_nr<ZF_F16, ZF_BF16, U, false>(nr, mat, grid, s, a);
+    if (gdt == ZF_BF16) launch_pass2_nr<ZF_BF16, ZF_BF16, false>(nr, mat, grid, s, a);
+    else launch_pass2_nr<ZF_F16, ZF_BF16, false>(nr, mat, grid, s, a);
     return;
   }
   if (gdt == ZF_BF16) {
-    if (pdt == ZF_BF16) launch_pass2_nr<ZF_BF16, ZF_BF16, U, true>(nr, mat, grid, s, a);
-    else launch_pass2_nr<ZF_BF16, ZF_F16, U, true>(nr, mat, grid, s, a);
+    if (pdt == ZF_BF16) launch_pass2_nr<ZF_BF16, ZF_BF16, true>(nr, mat, grid, s, a);
+    else launch_pass2_nr<ZF_BF16, ZF_F16, true>(nr, mat, grid, s, a);
   } else {
-    if (pdt == ZF_BF16) launch_pass2_nr<ZF_F16, ZF_BF16, U, true>(nr, mat, grid, s, a);
-    else launch_pass2_nr<ZF_F16, ZF_F16, U, true>(nr, mat, grid, s, a);
+    if (pdt == ZF_BF16) launch_pass2_nr<ZF_F16, ZF_BF16, true>(nr, mat, grid, s, a);
+    else launch_pass2_nr<ZF_F16, ZF_F16, true>(nr, mat, grid, s, a);
   }
 }
 
@@ -508,8 +507,7 @@ int launch_pass2(const zf_plan* plan, int32_t gdt, int32_t pdt, bool mat, bool o
                  hipStream_t s, const Pass2Args& a) {
   const dim3 grid((uint32_t)zf::pass2_tiles(plan, mat));  // fits: checked by the planner
   const int nr = plan->summary.n_ranks;
-  if (plan->unr2 == 2) launch_pass2_u<2>(nr, gdt, pdt, mat, out16, grid, s, a);
-  else launch_pass2_u<1>(nr, gdt, pdt, mat, out16, grid, s, a);
+  launch_pass2_dt(nr, gdt, pdt, mat, out16, grid, s, a);
   return hip_ok(hipGetLastError()) ? ZF_OK : ZF_EHIP;
 }
 

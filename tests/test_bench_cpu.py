@@ -115,3 +115,22 @@ def test_roctx_spans():
         assert trace.enabled()
     finally:
         trace._lib = None
+
+
+@pytest.mark.parametrize("name,expected", [
+    ("llama-73m-n8", 24 + 2),               # master, m, v in and out; 16-bit param out
+    ("llama-4.06b-n2", 24 + 2),
+    ("llama-2.1b-n2-zero3", 24 + 2),
+    ("llama-2.1b-n2-fsdp2", 4 + 24),        # the fp32 gradient shard is the method's; no 16-bit
+    ("llama-654m-n2-buckets-a4", 4 + 24 + 2),
+])
+def test_update_pass_algorithmic_bytes(name, expected):
+    """The roofline's bytes for the update pass are the method's: the
+    replicas' re-read (or the fp32 sums pass 1 wrote) that the global-norm
+    barrier costs is counted only in the design bytes beside them."""
+    w = W.get(name)
+    assert bench.update_alg_bytes_per_param(w) == expected
+    design = bench.update_kernel_bytes_per_elem(w, w.n_ranks > 4 or w.fp32_params
+                                                or w.backward_rs)
+    assert design - expected == {"llama-73m-n8": 4, "llama-4.06b-n2": 4,
+                                 "llama-2.1b-n2-zero3": 4}.get(name, 0)

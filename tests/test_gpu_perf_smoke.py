@@ -7,7 +7,10 @@ The update pass (4 reads + 4 writes per element, fp32 or a mix of 16-bit
 replicas and fp32 state) must reach 85% of the best 4-read/4-write figure,
 on the 73M workload (materialised sums) and the 654M one (recomputed sums);
 73M's pass 1 (8 replicas in, the fp32 sums out) 85% of the best
-8-read/1-write figure.  They run at 97% or more today.
+8-read/1-write figure.  They run at 97% or more today.  The update pass
+must also reach an absolute 70% of the MI355X's 8 TB/s on the bytes it
+moves, so that a box-wide slowdown that lowers the probes too (placement,
+clocks) still fails; it runs at 78-86% today.
 """
 import pytest
 import torch
@@ -18,6 +21,7 @@ pytestmark = pytest.mark.gpu
 
 
 SHAPES = ((1, 0), (2, 0), (1, 3), (1, 4), (2, 3), (2, 4))
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, vendor figure
 
 
 def _probe(I, r, w, n=1 << 28, reps=10):
@@ -72,5 +76,6 @@ def test_update_pass_near_box_ceiling(name):
     print(f"{name}: pass1 {pass1_gbs:.0f} GB/s, pass2 {pass2_gbs:.0f} GB/s, best probes 4+4 "
           f"{c44:.0f}, 8+1 {c81:.0f}", flush=True)
     assert pass2_gbs >= 0.85 * c44, (pass2_gbs, c44)
+    assert pass2_gbs >= 0.70 * PEAK_HBM_GBS, (pass2_gbs, PEAK_HBM_GBS)
     if w.n_ranks == 8:
         assert pass1_gbs >= 0.85 * c81, (pass1_gbs, c81)
