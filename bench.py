@@ -29,7 +29,9 @@ Prints one JSON line:
                sums that the global-norm barrier costs), the same less the
                sums the memory-side cache window serves, and traffic =
                counted bytes per launch from the committed counter summaries
-               of the same kernel code (null otherwise)
+               of the same kernel code (null otherwise), and traffic_dram32 =
+               the bytes of L2's 32-byte-unit requests to memory per launch
+               (no calibration)
   hbm_gbs_counted
                counter bytes of every kernel of a step (bytes leaving L2)
                less the cache window's reads, over the step time; the raw
@@ -333,6 +335,66 @@ def summarize_pmc(fetch_dir, write_dir, workload, out, commands):
 
 
 PROBE_FLOATS = 1 << 28  # 1 GiB per array
+
+DRAM32_COUNTERS = ("TCC_EA0_RDREQ_DRAM_32B_sum", "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum")
+
+
+def summarize_dram32(directory, workload, out, command):
+    """Per-launch bytes of the step's kernels from one counter run of L2's
+    read and write requests to memory, counted in 32-byte units
+    (DRAM32_COUNTERS: a 64-byte request counts 2, a 128-byte one 4), so
+    bytes = 32 x count with no calibration; the run's 1 GiB probe copy is
+    reported beside them as the check.  These requests are what leaves L2
+    for memory: the memory-side cache may still serve some of them."""
+    from fsdp_sharded_mixed_amd import workloads as W
+    rows = _csv_rows(directory, "counter_collection.csv")
+    vals = {}
+    for r in rows:
+        vals.setdefault((r["Kernel_Name"], r["Counter_Name"]), []).append(
+            32.0 * float(r["Counter_Value"]))
+
+    def med(key, counter):
+        xs = sorted(x for (k, c), v in vals.items() if key in k and c == counter for x in v)
+        return xs[len(xs) // 2] if xs else None
+
+    def tot(key, counter):
+        return sum(x for (k, c), v in vals.items() if key in k and c == counter for x in v)
+
+    rd, wr = DRAM32_COUNTERS
+    w = W.get(workload)
+    steps = len([x for (k, c), v in vals.items() if "zf_finish" in k and c == rd for x in v])
+    res = {"workload": workload, "kernel_source_sha256_16": kernel_source_hash(),
+           "counters": list(DRAM32_COUNTERS), "bytes_per_count": 32, "commands": command,
+           "steps": steps,
+           "copy_check": {"kernel": "stream_probe<1, 1> (1 GiB read, 1 GiB written)",
+                          "expected_bytes_each_way": 4 * PROBE_FLOATS,
+                          "read_bytes": med("stream_probe<1, 1>", rd),
+                          "write_bytes": med("stream_probe<1, 1>", wr)}}
+    for key in ("zf_pass1_reduced", "zf_pass1<", "zf_pass2", "zf_gather_kernel",
+                "zf_gather_cast_kernel", "zf_bucket_rs_kernel", "zf_accumulate_kernel"):
+        r1, w1 = med(key, rd), med(key, wr)
+        if r1 is None:
+            continue
+        step_bytes = (tot(key, rd) + tot(key, wr)) / max(steps, 1)
+        res[key.rstrip("<")] = {"read_bytes": r1, "write_bytes": w1,
+                                "bytes_per_launch": r1 + w1, "bytes_per_step": step_bytes,
+                                "per_param_per_step": step_bytes / w.psi}
+    with open(out, "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps(res, indent=1))
+
+
+def dram32_for(workload, kernel="zf_pass2", per="launch"):
+    """Bytes per launch (or per step) of a step kernel from the committed
+    32-byte request counter summary of these kernel sources, or None."""
+    path = os.path.join(PROFILES, f"zf_step_{workload}_dram32.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_sha256_16") != kernel_source_hash() or kernel not in d:
+        return None
+    return d[kernel]["bytes_per_" + per]
 
 
 # probe shapes (quads per lane, resident blocks per CU, 0: no limit); the
@@ -689,6 +751,7 @@ def bench_workload(w, args, probe, copy_gbs, graph=True, skip_probe=True):
     roof = {"bound": "hbm", "achieved": round(upd_gbs, 2), "peak": PEAK_HBM_GBS,
             "unit": "GB/s", "frac": round(upd_gbs / PEAK_HBM_GBS, 4),
             "traffic": traffic_for(w.name, "zf_pass2"),
+            "traffic_dram32": dram32_for(w.name, "zf_pass2"),
             "kernel": "zf_pass2 (fused AdamW" + ("" if w.fp32_params else "+cast+gather") + ")",
             "bytes_per_launch": upd_alg,
             "bytes_basis": f"algorithmic: {update_alg_bytes_per_param(w)} B per parameter",
@@ -833,6 +896,8 @@ def main():
                     help="with --summarize-trace: the profiled run's stdout, whose bench "
                          "line's figures are added to the summary")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"))
+    ap.add_argument("--summarize-dram32", nargs=2, metavar=("DIR", "OUT"),
+                    help="summary of a run with --pmc " + " ".join(DRAM32_COUNTERS))
     ap.add_argument("--command", default="", help="command text recorded in a summary")
     args = ap.parse_args()
     default_run = args.workload is None and not args.set and not args.no_headline_2
@@ -841,6 +906,10 @@ def main():
     args.workload = args.workload or DEFAULT_WORKLOAD
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace, args.command, args.bench_json)
+        return
+    if args.summarize_dram32:
+        summarize_dram32(args.summarize_dram32[0], args.workload, args.summarize_dram32[1],
+                         args.command)
         return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload,
