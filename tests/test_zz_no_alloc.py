@@ -132,3 +132,52 @@ def test_noalloc_fsdp2_and_skip_on_a_side_stream(R):
     w.inject_step, w.inject_replica = 2, 1
     a, b = run_twins(R, w, side_stream=True)
     assert b.result().t == 2 and b.loss_scale == 2048.0
+
+
+def test_noalloc_in_a_captured_graph(R):
+    """Code under HIP graph capture is one of the callers the entry point is
+    for.  Step 1 runs eagerly (the first call on the device looks up the
+    scratch's address); steps 2.. replay one captured call.  An eager twin
+    steps with zf_shard_step on the same replicas; after every replay the
+    two agree bit for bit.  N = 8 with the sums in the scratch, then N = 3
+    in fp16 with +inf at step 3, skipped inside a replay."""
+    for w, inject in ((flat_workload(8, 1_000_003, steps=4), None),
+                      (flat_workload(3, 300_007, gdt=W.F16, steps=5), 3)):
+        G.say(f"noalloc graph case {w.name}")
+        a, b = R.DeviceRun(w), R.DeviceRun(w)
+        a.init_state()
+        b.init_state()
+
+        def noalloc_step():
+            zf.shard_step_noalloc(b.plan, b.hp, w.grad_dtype, w.param_dtype, b.grads, b.master,
+                                  b.exp_avg, b.exp_avg_sq, b.params, b.state)
+
+        graph = None
+        for k in range(1, w.steps + 1):
+            a.fill_grads(k, a.loss_scale)
+            if inject == k:
+                a.grads[w.inject_replica][17] = float("inf")
+            for ga, gb in zip(a.grads, b.grads):
+                gb.copy_(ga)
+            a.step()
+            if k == 1:
+                noalloc_step()
+            else:
+                if graph is None:
+                    torch.cuda.synchronize()
+                    graph = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(graph):
+                        noalloc_step()
+                graph.replay()
+            torch.cuda.synchronize()
+            ra, rb = a.result(), b.result()
+            for f in RESULT_FIELDS:
+                assert getattr(ra, f) == getattr(rb, f), f"{w.name} step {k}: {f}"
+            a.loss_scale = ra.scale_next
+            for name in ("master", "exp_avg", "exp_avg_sq", "params"):
+                assert torch.equal(bits(getattr(a, name)), bits(getattr(b, name))), \
+                    f"{w.name} step {k}: {name}"
+            G.say(f"  step {k}: skipped={rb.skipped} t={rb.t} equal "
+                  f"({'eager' if k == 1 else 'replay'})")
+        assert b.result().t == w.steps - (1 if inject else 0)
+        del graph
