@@ -12,7 +12,6 @@ import numpy as np
 import torch
 
 import oracle as O
-from fsdp_sharded_mixed_amd import workloads as W
 from tests import oracle_inputs as OI
 
 POOL_THREADS = min(16, os.cpu_count() or 1)
@@ -111,41 +110,3 @@ def regen_sumsq_threaded(w, step, scale, psi, inject=None, chunks=None):
         ss += s
         bad |= b
     return ss, bad
-
-
-class SampledOracle:
-    """Trajectories of a sample of logical indices through the oracle's
-    element update, with the exact global norm from regeneration."""
-
-    def __init__(self, w, psi, idx):
-        self.w = w
-        self.psi = psi
-        self.idx = np.asarray(sorted(set(int(i) for i in idx)), np.int64)
-        p = O.gen32(1, w.seed, W.STREAM_MASTER, 0, w.master_sigma)  # warm the library
-        del p
-        self.p = np.array([O.gen32(1, w.seed, W.STREAM_MASTER, int(i), w.master_sigma)[0]
-                           for i in self.idx], np.float32)
-        if w.norm_weights_one:
-            for a, b in w.norm_ranges():
-                self.p[(self.idx >= a) & (self.idx < b)] = 1.0
-        self.m = np.zeros_like(self.p)
-        self.v = np.zeros_like(self.p)
-        self.hp = OI.hparams(w)
-        self.st = OI.scale_state(w)
-        self.step_no = 0
-
-    def step(self, inject_index=None):
-        w = self.w
-        self.step_no += 1
-        scale = self.st.loss_scale
-        inj = None
-        if inject_index is not None:
-            inj = O.Inject(step=self.step_no, replica=w.inject_replica, index=int(inject_index),
-                           bits=OI.inf_bits(w.grad_dtype))
-        ss, bad = regen_sumsq_threaded(w, self.step_no, scale, self.psi, inj)
-        sc, res = O.finish(ss, bad, w.n_ranks, self.hp, self.st)
-        if not res.skipped:
-            acc = O.regen_accum_acc(w.grad_dtype, w.n_ranks, w.n_micro, w.accum_mode, w.seed,
-                                    self.step_no, w.sigma, scale, self.idx, inj)
-            O.adamw_array(acc, sc, self.p, self.m, self.v)
-        return res

@@ -1,27 +1,39 @@
-"""Element-by-element GPU parity at the workloads' full sizes: every
-element of the 73M decoder at N = 8 (ten steps), the 654M decoder at N = 2
-(five steps), the 4.06B decoder at N = 2 (four steps, the second skipped
-by an injected +inf), and the 2.1B decoder under ZeRO-3 and under FSDP2
-(three steps each, every unit gather), compared with the CPU oracle after
-every step, in the launch configuration the bench times.
+"""Element-by-element GPU parity at the workloads' full sizes, in the launch
+configuration the bench times: every element compared with the CPU oracle
+after every step of
+  - the 73M decoder at N = 8 (ten steps; its sums split around the
+    memory-side cache window),
+  - the 654M decoder at N = 2 (five steps),
+  - the 4.06B decoder at N = 2 (four steps, the second skipped by an
+    injected +inf),
+  - the 2.1B decoder under ZeRO-3 and under FSDP2 (three steps each, every
+    unit gather),
+  - a 120M plan of three ragged FlatParameter units at N = 5 whose
+    materialised sums lie past the cache window (three steps),
+  - the 654M decoder in Megatron's gradient buckets over four micro-batches,
+    reduced every micro-batch or (no_sync) accumulated locally and reduced
+    once (three steps each),
+  - the 654M decoder under ZeRO-Offload (fp32 state and CPU-Adam on the
+    host; three steps).
 
-The oracle side holds the full state on the host.  FullOracle carries
-every element through the oracle's own functions, split into index ranges
-over a thread pool (each range is independent: the generator is keyed by
-logical index and the update is per element): the master from the
-oracle's generator, the exact global squared norm and overflow flag by
-regeneration (range partials added in order), the fixed-order
-reduce-scatter sums by regeneration, the binary32 AdamW update and the
-nearest-even cast.  These workloads have no padding (every FlatParameter
-length is a multiple of N), so the padded flat index of the device arrays
-is the logical index.  test_full_oracle_matches_single_threaded pins this
+The oracle side holds the full state on the host, in logical order.
+FullOracle carries every element through the oracle's own functions, split
+into index ranges over a thread pool (each range is independent: the
+generator is keyed by logical index and the update is per element): the
+master from the oracle's generator, the exact global squared norm and
+overflow flag by regeneration (range partials added in order), the
+fixed-order reduce-scatter sums -- accumulated over the micro-batches in the
+workload's scheme -- by regeneration, the binary32 AdamW update and the
+nearest-even cast.  The device arrays are in the padded flat layout: each
+unit's real elements are compared with the oracle's logical range and its
+padding must be bit-zero.  test_full_oracle_matches_single_threaded pins the
 harness to the plain single-threaded oracle step on the CPU.
 
 Bars: the reduce-scatter sums bit for bit; master, exp_avg, exp_avg_sq
-within 4 ulp (relative 1e-6); the 16-bit parameters and every gathered
-unit within 1 ulp; the step result (overflow, skip, t, loss scale) exactly
-and the norm within 1e-5.  Each step reports the share of elements that
-match bit for bit.
+within 4 ulp (relative 1e-6); the 16-bit parameters and every gathered unit
+within 1 ulp; padding bit-zero everywhere; the step result (overflow, skip,
+t, loss scale) exactly and the norm within 1e-5.  Each step reports the
+share of elements that match bit for bit.
 """
 from concurrent.futures import ThreadPoolExecutor
 
@@ -39,14 +51,14 @@ CMP_CHUNK = 1 << 25    # elements per device-to-host comparison slice
 
 
 class FullOracle:
-    """The full state of a workload without padding (the padded index
-    equals the logical index), stepped element by element by the oracle
-    over a thread pool."""
+    """The full state of a workload in logical order, stepped element by
+    element by the oracle over a thread pool."""
 
     def __init__(self, w, threads=None):
-        _, psi, psi_pad = OI.plan(w)
-        assert psi == psi_pad == w.psi and not w.backward_rs and not w.offload
-        self.w, self.psi = w, w.psi
+        assert not w.offload_down16
+        self.w = w
+        self.units, self.psi, self.psi_pad = OI.plan(w)
+        assert self.psi == w.psi
         self.edges = list(range(0, w.psi, CHUNK)) + [w.psi]
         self.pool = ThreadPoolExecutor(threads or G.POOL_THREADS)
         self.p = np.empty(w.psi, np.float32)
@@ -70,7 +82,8 @@ class FullOracle:
 
     def step(self, inject_index=None, keep_sums=False):
         """One step: returns (result, sums or None).  keep_sums keeps every
-        reduce-scatter sum of the step (also of a skipped one)."""
+        reduce-scatter sum of the step (accumulated over the micro-batches),
+        in logical order, also of a skipped step."""
         w = self.w
         self.step_no += 1
         scale = self.st.loss_scale
@@ -86,7 +99,7 @@ class FullOracle:
 
         def part(c):
             a, b = self.edges[c], self.edges[c + 1]
-            acc = O.regen_accum_acc(w.grad_dtype, w.n_ranks, 1, W.ACCUM_REDUCE_EACH, w.seed,
+            acc = O.regen_accum_acc(w.grad_dtype, w.n_ranks, w.n_micro, w.accum_mode, w.seed,
                                     self.step_no, w.sigma, scale, np.arange(a, b, dtype=np.int64),
                                     inj)
             if sums is not None:
@@ -103,9 +116,26 @@ def _chunks(pool, n, fn):
     return list(pool.map(lambda a: fn(a, min(n, a + CMP_CHUNK)), range(0, n, CMP_CHUNK)))
 
 
+class Tally:
+    """Bit-identical element counts per array over the units of a step."""
+
+    def __init__(self):
+        self.exact, self.total, self.worst = {}, {}, 0
+
+    def add(self, name, exact, total, worst=0):
+        self.exact[name] = self.exact.get(name, 0) + exact
+        self.total[name] = self.total.get(name, 0) + total
+        self.worst = max(self.worst, worst)
+
+    def shares(self):
+        out = {k: round(self.exact[k] / self.total[k], 6) for k in self.exact}
+        out["worst_ulp"] = self.worst
+        return out
+
+
 def compare_f32(pool, t, ref, what, max_ulp=4):
-    """Every element of device fp32 array t against ref: within max_ulp
-    ulp.  Returns (share bit-identical, worst ulp)."""
+    """Every element of fp32 array t (device or host) against ref: within
+    max_ulp ulp.  Returns (bit-identical count, worst ulp)."""
     def one(a, b):
         got = t[a:b].cpu().numpy()
         want = ref[a:b]
@@ -121,7 +151,7 @@ def compare_f32(pool, t, ref, what, max_ulp=4):
         return (b - a) - nd, worst
 
     parts = _chunks(pool, ref.size, one)
-    return sum(x[0] for x in parts) / ref.size, max(x[1] for x in parts)
+    return sum(x[0] for x in parts), max([0] + [x[1] for x in parts])
 
 
 def compare_bits32(pool, t, ref, what):
@@ -134,84 +164,124 @@ def compare_bits32(pool, t, ref, what):
 
 
 def compare_16(pool, t, p_ref, dtype, what):
-    """Every 16-bit element of device array t within 1 ulp of RNE16 of the
-    oracle's fp32 values p_ref; returns the share that is bit-identical."""
+    """Every 16-bit element of t within 1 ulp of RNE16 of the oracle's fp32
+    values p_ref; returns the bit-identical count."""
     def one(a, b):
         got = t[a:b].view(torch.int16).cpu().numpy().view(np.uint16)
-        diff = got != O.narrow(dtype, p_ref[a:b])
+        want = O.narrow(dtype, p_ref[a:b])
+        diff = got != want
         nd = int(diff.sum())
         if nd:
-            want = O.narrow(dtype, p_ref[a:b])
             assert G.ulp16_distance(got[diff], want[diff]).max() <= 1, what
         return (b - a) - nd
 
-    return sum(_chunks(pool, p_ref.size, one)) / p_ref.size
+    return sum(_chunks(pool, p_ref.size, one))
 
 
-def check_state(dev, orc, what):
-    em, wm = compare_f32(orc.pool, dev.master, orc.p, f"{what} master")
-    ea, wa = compare_f32(orc.pool, dev.exp_avg, orc.m, f"{what} exp_avg")
-    ev, wv = compare_f32(orc.pool, dev.exp_avg_sq, orc.v, f"{what} exp_avg_sq")
-    out = {"master": round(em, 6), "exp_avg": round(ea, 6), "exp_avg_sq": round(ev, 6),
-           "worst_ulp": max(wm, wa, wv)}
-    if dev.params is not None:
-        out["params"] = round(compare_16(orc.pool, dev.params, orc.p, dev.w.param_dtype,
-                                         f"{what} params"), 6)
-    return out
+def assert_zero(t, what):
+    if t.numel():
+        assert int(torch.count_nonzero(G.bits_view(t))) == 0, f"{what}: padding is not zero"
 
 
-def check_gathers(dev, orc, what):
+def check_state(dev, orc, units, what):
+    """Master, exp_avg, exp_avg_sq and the 16-bit parameters: each unit's
+    real range against the oracle's logical range, its padding zero."""
+    tally = Tally()
+    arrays = [("master", dev.master, orc.p), ("exp_avg", dev.exp_avg, orc.m),
+              ("exp_avg_sq", dev.exp_avg_sq, orc.v)]
+    for u in units:
+        o, L, P, lam = int(u["O"]), int(u["L"]), int(u["P"]), int(u["lam"])
+        for name, t, ref in arrays:
+            ex, worst = compare_f32(orc.pool, t[o:o + L], ref[lam:lam + L], f"{what} {name}")
+            tally.add(name, ex, L, worst)
+            assert_zero(t[o + L:o + P], f"{what} {name}")
+        if dev.params is not None:
+            ex = compare_16(orc.pool, dev.params[o:o + L], orc.p[lam:lam + L],
+                            dev.w.param_dtype, f"{what} params")
+            tally.add("params", ex, L)
+            assert_zero(dev.params[o + L:o + P], f"{what} params")
+    return tally
+
+
+def check_sums(orc, t, units, sums, what):
+    """Reduce-scatter sums (padded flat t) against the oracle's logical
+    sums, bit for bit; padding zero."""
+    for u in units:
+        o, L, P, lam = int(u["O"]), int(u["L"]), int(u["P"]), int(u["lam"])
+        compare_bits32(orc.pool, t[o:o + L], sums[lam:lam + L], what)
+        assert_zero(t[o + L:o + P], what)
+
+
+def check_gathers(dev, orc, tally, what):
     """ZeRO-3: every unit gathered into the reused unit buffer; FSDP2: every
     FSDP unit cast-gathered into the reused group buffer.  Each against
-    RNE16 of the oracle's master over the unit's logical range (no padding,
-    so a unit's padded and logical lengths agree)."""
-    w, shares = dev.w, []
+    RNE16 of the oracle's master over the unit's logical range; a ZeRO-3
+    unit's padding zero."""
+    w = dev.w
     if w.fp32_params:
         for g, info in enumerate(dev.plan.groups):
             buf = dev.gather_cast(g)
             lam0 = dev.plan.units[info.first_unit].lam
-            shares.append(compare_16(orc.pool, buf, orc.p[lam0:lam0 + info.numel],
-                                     w.param_dtype, f"{what} group {g}"))
+            tally.add("gathers", compare_16(orc.pool, buf, orc.p[lam0:lam0 + info.numel],
+                                            w.param_dtype, f"{what} group {g}"), info.numel)
     elif w.stage == 3:
         for u, info in enumerate(dev.plan.units):
-            assert info.P == info.L
             buf = dev.gather(u)
-            shares.append(compare_16(orc.pool, buf, orc.p[info.lam:info.lam + info.L],
-                                     w.param_dtype, f"{what} unit {u}"))
-    return min(shares) if shares else None
+            tally.add("gathers", compare_16(orc.pool, buf[:info.L],
+                                            orc.p[info.lam:info.lam + info.L], w.param_dtype,
+                                            f"{what} unit {u}"), info.L)
+            assert_zero(buf[info.L:info.P], f"{what} unit {u}")
 
 
 def test_full_oracle_matches_single_threaded(orc):
     """CPU pin of the harness: FullOracle (range-parallel regeneration and
-    update) tracks the oracle's own single-threaded step on a whole padded
-    flat (O.zero_step via OracleRun) for three steps at N = 4 on 5,000,004
-    elements with a norm weight range and clipping active: the same
-    results, the norm to within rounding, the state and the sums within
-    4 ulp and almost all bit for bit."""
+    update) tracks the oracle's own single-threaded step (O.zero_step, and
+    O.step_reduced after the backward-side reduction, via OracleRun) for
+    three steps: at N = 4 on a 5,000,004-element flat with a norm weight
+    range and clipping active, and at N = 3 on three ragged units (padding)
+    whose gradients are reduce-scattered in buckets over three
+    micro-batches, in both accumulation schemes.  The same results, the
+    norm to within rounding, the sums bit for bit, the state within 4 ulp
+    and almost all bit for bit."""
     segs = [W.Segment("w", 4_000_000, 0), W.Segment("n", 4, 0, W.KIND_NORM),
             W.Segment("b", 1_000_000, 0)]
-    w = W.Workload(name="flat-5m-n4", description="", segments=segs, n_ranks=4,
-                   layout=W.GLOBAL_FLAT, stage=2, grad_dtype=W.BF16, param_dtype=W.BF16,
-                   sigma=2e-3, loss_scale=1.0, dynamic=False, lr=1e-3, steps=3, seed=13,
-                   norm_weights_one=True, max_norm=1.0)
-    full = FullOracle(w, threads=4)
-    ref = OI.OracleRun(w)
-    try:
-        for k in range(1, 4):
-            grads = OI.replicas(w, ref.units, ref.psi_pad, k, ref.st.loss_scale)
-            acc_ref = np.concatenate(O.reduce_scatter(w.grad_dtype, w.n_ranks, ref.units, grads))
-            r_ref = ref.step(grads)
-            r_full, sums = full.step(keep_sums=True)
-            assert (r_full.skipped, r_full.t, r_full.scale_next) == \
-                (r_ref.skipped, r_ref.t, r_ref.scale_next)
-            assert abs(r_full.norm - r_ref.norm) <= 1e-12 * r_ref.norm and r_ref.coef < 1.0
-            # the global flat has no padding: rank r's shard is [r*S, (r+1)*S)
-            assert np.array_equal(sums.view(np.uint32), acc_ref.view(np.uint32))
-            for mine, theirs in ((full.p, ref.master), (full.m, ref.m), (full.v, ref.v)):
-                share = G.assert_state_close("full oracle", mine, np.concatenate(theirs))
-                assert share > 0.999
-    finally:
-        full.close()
+    flat = W.Workload(name="flat-5m-n4", description="", segments=segs, n_ranks=4,
+                      layout=W.GLOBAL_FLAT, stage=2, grad_dtype=W.BF16, param_dtype=W.BF16,
+                      sigma=2e-3, loss_scale=1.0, dynamic=False, lr=1e-3, steps=3, seed=13,
+                      norm_weights_one=True, max_norm=1.0)
+    cases = [flat]
+    for mode in (W.ACCUM_REDUCE_EACH, W.ACCUM_NO_SYNC):
+        cases.append(W.Workload(
+            name=f"units-acc-m{mode}", description="",
+            segments=[W.Segment("a", 700_001, 0), W.Segment("b", 300_002, 1),
+                      W.Segment("c", 99_998, 2)],
+            n_ranks=3, layout=W.PER_UNIT, stage=2, grad_dtype=W.F16, param_dtype=W.F16,
+            sigma=1e-3, loss_scale=1024.0, dynamic=True, lr=1e-3, steps=3, seed=17,
+            max_norm=0.5, n_micro=3, accum_mode=mode, bucket_numel=400_000))
+    for w in cases:
+        full = FullOracle(w, threads=4)
+        ref = OI.OracleRun(w)
+        try:
+            for k in range(1, 4):
+                if w.backward_rs:
+                    r_ref = ref.step()
+                    sums_ref = OI.rank_shards_to_logical(ref.units, ref.grad_shards)
+                else:
+                    grads = OI.replicas(w, ref.units, ref.psi_pad, k, ref.st.loss_scale)
+                    sums_ref = OI.rank_shards_to_logical(
+                        ref.units, O.reduce_scatter(w.grad_dtype, w.n_ranks, ref.units, grads))
+                    r_ref = ref.step(grads)
+                r_full, sums = full.step(keep_sums=True)
+                assert (r_full.skipped, r_full.t, r_full.scale_next) == \
+                    (r_ref.skipped, r_ref.t, r_ref.scale_next), w.name
+                assert abs(r_full.norm - r_ref.norm) <= 1e-12 * r_ref.norm and r_ref.coef < 1.0
+                assert np.array_equal(sums.view(np.uint32), sums_ref.view(np.uint32)), w.name
+                for mine, theirs in ((full.p, ref.master), (full.m, ref.m), (full.v, ref.v)):
+                    logical = OI.rank_shards_to_logical(ref.units, theirs)
+                    share = G.assert_state_close(f"full oracle {w.name}", mine, logical)
+                    assert share > 0.999
+        finally:
+            full.close()
 
 
 def host_available_bytes():
@@ -233,21 +303,35 @@ def R():
     return runner
 
 
-def run_full(R, name, twin_sums=False, rs_first_step=True):
-    """Every step of workload `name` on the device against FullOracle, every
-    element of the state, the 16-bit parameters and every gathered unit.
+def flat120m_n5():
+    """Three ragged FlatParameter units at N = 5: 480 MB of materialised
+    sums, past the size up to which pass 1 keeps a share of them in the
+    memory-side cache, so every sum goes out non-temporal and the update
+    pass walks its tiles forward."""
+    return W.Workload(name="flat-120m-n5", description="three ragged units past the cache window",
+                      segments=[W.Segment("a", 50_000_001, 0), W.Segment("b", 40_000_003, 1),
+                                W.Segment("c", 30_000_007, 2)],
+                      n_ranks=5, layout=W.PER_UNIT, stage=2, grad_dtype=W.BF16,
+                      param_dtype=W.BF16, sigma=1e-3, loss_scale=1.0, dynamic=False, lr=1e-4,
+                      steps=3, seed=7)
 
-    twin_sums: a second device run steps in lockstep on the same replicas
-    with fp32 gradient shards given, where the same kernels write the sums
-    that the first run keeps in its workspace; its sums are compared with
-    the oracle's every step and its state with the first run's.
-    rs_first_step: at step 1 the reduce-scatter alone (zf_reduce_scatter)
-    into a full fp32 buffer, compared with the oracle's sums.  FSDP2 keeps
-    the sums in its resident fp32 gradient shards: compared every step."""
+
+def run_full(R, w, twin_sums=False, rs_first_step=True):
+    """Every step of workload w on the device against FullOracle: every
+    element of the state, the 16-bit parameters (padding zero) and every
+    gathered unit.
+
+    Sums: with twin_sums a second device run steps in lockstep on the same
+    replicas with fp32 gradient shards given, where the same kernels write
+    the sums that the first run keeps in its workspace; its sums are
+    compared every step and its state with the first run's.  Workloads
+    that keep fp32 gradient shards (FSDP2, the backward-side reduction,
+    ZeRO-Offload) are compared there every step.  Otherwise, with
+    rs_first_step, the reduce-scatter alone (zf_reduce_scatter) at step 1."""
     from fsdp_sharded_mixed_amd import inputs as I
     from fsdp_sharded_mixed_amd import zf
     torch.cuda.empty_cache()
-    w = W.get(name)
+    w = W.get(w) if isinstance(w, str) else w
     # the host holds master, m and v (12 B per parameter) and one step's sums
     # (4 B), plus the comparison slices in flight
     need = 16 * w.psi + 2 * G.POOL_THREADS * CMP_CHUNK * 4
@@ -255,7 +339,8 @@ def run_full(R, name, twin_sums=False, rs_first_step=True):
     if avail is not None and avail < need:
         pytest.skip(f"{w.name} needs about {need / 2**30:.0f} GiB of host memory for the "
                     f"full oracle state; {avail / 2**30:.0f} GiB available")
-    G.say(f"full parity {w.name}: Psi={w.psi:,} N={w.n_ranks} stage={w.stage}, {w.steps} steps")
+    G.say(f"full parity {w.name}: Psi={w.psi:,} N={w.n_ranks} stage={w.stage} "
+          f"micro={w.n_micro} offload={w.offload}, {w.steps} steps")
     dev = R.DeviceRun(w)
     twin = None
     if twin_sums:
@@ -266,15 +351,30 @@ def run_full(R, name, twin_sums=False, rs_first_step=True):
     dev.init_state()
     inj = I.inject_index(w, w.psi) if w.inject_step else None
     orc = FullOracle(w)
+    units = orc.units
+    assert [(u.O, u.L, u.P, u.lam) for u in dev.plan.units] == \
+        [(int(u["O"]), int(u["L"]), int(u["P"]), int(u["lam"])) for u in units]
+    resident_sums = dev.grad_shards is not None
     trace = []
     try:
-        compare_bits32(orc.pool, dev.master, orc.p, "initial master")
+        for u in units:  # the initial master, bit for bit
+            o, L, lam = int(u["O"]), int(u["L"]), int(u["lam"])
+            compare_bits32(orc.pool, dev.master[o:o + L], orc.p[lam:lam + L], "initial master")
         for k in range(1, w.steps + 1):
-            dev.fill_grads(k, dev.loss_scale)
-            if w.inject_step == k:
-                dev.inject_inf()
+            scale = dev.loss_scale
+            if w.backward_rs:
+                # every micro-batch filled and reduced bucket by bucket, then the step
+                for a in range(w.n_micro):
+                    dev.fill_grads(k, scale, micro=a)
+                    if w.inject_step == k and a == 0:
+                        dev.inject_inf()
+                    dev.backward(a)
+            else:
+                dev.fill_grads(k, scale)
+                if w.inject_step == k:
+                    dev.inject_inf()
             rs = None
-            if rs_first_step and k == 1 and not w.fp32_params:
+            if rs_first_step and k == 1 and not (resident_sums or twin is not None):
                 rs = torch.empty(dev.psi_pad, dtype=torch.float32, device=dev.device)
                 zf.reduce_scatter(dev.plan, w.grad_dtype, dev.grads, rs)
             dev.step()
@@ -282,32 +382,30 @@ def run_full(R, name, twin_sums=False, rs_first_step=True):
                 twin.step()
             res_d = dev.result()
             dev.loss_scale = res_d.scale_next
-            keep = twin is not None or w.fp32_params or rs is not None
+            keep = twin is not None or resident_sums or rs is not None
             res_o, sums = orc.step(inject_index=inj if w.inject_step == k else None,
                                    keep_sums=keep)
             G.assert_result_matches(res_d, res_o, f"{w.name} step {k}")
-            src = twin.grad_shards if twin is not None else \
-                (dev.grad_shards if w.fp32_params else rs)
             if sums is not None:
-                compare_bits32(orc.pool, src, sums, f"{w.name} step {k} reduce-scatter sums")
+                src = twin.grad_shards if twin is not None else \
+                    (dev.grad_shards if resident_sums else rs)
+                check_sums(orc, src, units, sums, f"{w.name} step {k} reduce-scatter sums")
             del rs, sums
             if twin is not None:
                 for nm in ("master", "exp_avg", "exp_avg_sq", "params"):
                     assert torch.equal(G.bits_view(getattr(dev, nm)),
                                        G.bits_view(getattr(twin, nm))), f"step {k} {nm}"
-            shares = check_state(dev, orc, f"{w.name} step {k}")
-            g = check_gathers(dev, orc, f"{w.name} step {k}")
-            if g is not None:
-                shares["gathers"] = round(g, 6)
+            tally = check_state(dev, orc, units, f"{w.name} step {k}")
+            check_gathers(dev, orc, tally, f"{w.name} step {k}")
             trace.append((k, res_d.skipped, res_d.t, res_d.scale_used, res_d.scale_next,
                           res_d.norm, res_d.coef))
             G.say(f"  step {k}: skipped={res_d.skipped} t={res_d.t} S={res_d.scale_used}->"
                   f"{res_d.scale_next} norm={res_d.norm:.6f} (oracle {res_o.norm:.6f}) "
                   f"coef={res_d.coef:.6f} sums {'bit-exact' if keep else '-'}; "
-                  f"bit-identical shares {shares}")
+                  f"bit-identical shares {tally.shares()}")
     finally:
         orc.close()
-    return trace
+    return dev, trace
 
 
 @pytest.mark.gpu
@@ -317,7 +415,7 @@ def test_llama73m_n8_every_element(R):
     non-temporal and cache-allocating stores, the update pass walking
     backward), ten steps, clipped each step; a twin run with fp32 gradient
     shards exposes the sums of every step."""
-    trace = run_full(R, "llama-73m-n8", twin_sums=True)
+    _, trace = run_full(R, "llama-73m-n8", twin_sums=True)
     assert all(t[1] == 0 and abs(t[5] - 3.03) < 0.1 and t[6] < 1.0 for t in trace)
 
 
@@ -325,15 +423,28 @@ def test_llama73m_n8_every_element(R):
 def test_llama654m_n2_every_element(R):
     """654M decoder, N = 2 (the update pass recomputes the sums from the
     replicas), five steps with clipping active."""
-    trace = run_full(R, "llama-654m-n2")
+    _, trace = run_full(R, "llama-654m-n2")
     assert all(t[1] == 0 and abs(t[5] - 3.0) < 0.1 and t[6] < 1.0 for t in trace)
+
+
+@pytest.mark.gpu
+def test_flat120m_n5_past_cache_window_every_element(R):
+    """120M parameters in three ragged units at N = 5 (padding in every
+    unit), the materialised sums past the cache window; a twin run exposes
+    the sums of every step."""
+    from fsdp_sharded_mixed_amd import zf
+    w = flat120m_n5()
+    s = zf.plan_flat(w.segments, w.n_ranks, w.layout, w.stage).summary
+    assert s.policy == 1 and s.cached_sums_bytes == 0 and s.psi_pad > s.psi
+    _, trace = run_full(R, w, twin_sums=True)
+    assert all(t[1] == 0 for t in trace)
 
 
 @pytest.mark.gpu
 def test_llama2b_zero3_every_element(R):
     """2.1B decoder as 34 FSDP units, N = 2, stage 3: resident 16-bit shards
     and every unit gathered into one reused buffer every step."""
-    trace = run_full(R, "llama-2.1b-n2-zero3")
+    _, trace = run_full(R, "llama-2.1b-n2-zero3")
     assert all(t[1] == 0 and t[6] < 1.0 for t in trace)
 
 
@@ -342,8 +453,33 @@ def test_llama2b_fsdp2_every_element(R):
     """2.1B decoder under FSDP2: per-parameter dim-0 shards over N = 2, fp32
     parameters, the sums in resident fp32 gradient shards (every step, bit
     for bit), all 34 FSDP units cast-gathered every step."""
-    trace = run_full(R, "llama-2.1b-n2-fsdp2")
+    dev, trace = run_full(R, "llama-2.1b-n2-fsdp2")
+    assert len(dev.plan.groups) == 34 and len(dev.plan.units) == 291
     assert all(t[1] == 0 for t in trace)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name", ["llama-654m-n2-buckets-a4", "llama-654m-n2-nosync-a4"])
+def test_llama654m_bucketed_accumulation_every_element(R, name):
+    """654M decoder in Megatron's gradient buffer (12 buckets of >= 40M
+    elements, last layer first, each padded to a multiple of N), N = 2,
+    four micro-batches per step: every bucket reduce-scattered into the fp32
+    gradient shards each micro-batch, or (no_sync) fp32 local accumulation
+    and one reduction; the accumulated shards bit for bit every step; global
+    norm about 3, so clipping is active."""
+    dev, trace = run_full(R, name)
+    assert len(dev.plan.groups) == 12
+    assert all(t[1] == 0 and abs(t[5] - 3.0) < 0.1 and t[6] < 1.0 for t in trace)
+
+
+@pytest.mark.gpu
+def test_llama654m_offload_every_element(R):
+    """654M decoder under ZeRO-Offload: the GPU reduces into fp32 gradient
+    shards (bit for bit every step), the fp32 state and CPU-Adam live on
+    the host (every element), bf16 parameters come back in chunks."""
+    dev, trace = run_full(R, "llama-654m-n2-offload")
+    assert dev.master.device.type == "cpu"
+    assert all(t[1] == 0 and abs(t[5] - 3.0) < 0.1 and t[6] < 1.0 for t in trace)
 
 
 @pytest.mark.gpu
@@ -351,6 +487,6 @@ def test_llama4b_n2_every_element(R):
     """4.06B decoder, N = 2, fp16 under dynamic loss scaling with +inf in
     replica 1 at step 2: step 2 is skipped (state untouched, every element)
     and S halves 32768 -> 16384; steps 1, 3, 4 applied."""
-    trace = run_full(R, "llama-4.06b-n2")
+    _, trace = run_full(R, "llama-4.06b-n2")
     assert [(t[1], t[2]) for t in trace] == [(0, 1), (1, 1), (0, 2), (0, 3)]
     assert trace[1][3] == 32768.0 and trace[1][4] == 16384.0 and trace[2][3] == 16384.0
