@@ -118,6 +118,7 @@ def lib():
                                          C.POINTER(Inject), C.POINTER(dbl), C.POINTER(i32)]),
             "or_regen_acc": (C.c_int, [i32, i32, u64, i64, dbl, dbl, i64, vp,
                                        C.POINTER(Inject), vp]),
+            "or_sumsq_array": (C.c_int, [i64, vp, C.POINTER(dbl), C.POINTER(i32)]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -393,3 +394,11 @@ def regen_accum_acc(dtype, n_ranks, n_micro, mode, seed, step, sigma, scale, idx
     _check(lib().or_regen_accum_acc(dtype, n_ranks, n_micro, mode, seed, step, sigma, scale,
                                     idx.size, _p(idx), inj, _p(out)), "regen_accum_acc")
     return out
+
+
+def sumsq_array(x):
+    """Squared norm (double, in order) and overflow flag of given values."""
+    x = np.ascontiguousarray(x, np.float32)
+    ss, nf = C.c_double(), C.c_int32()
+    _check(lib().or_sumsq_array(x.size, _p(x), C.byref(ss), C.byref(nf)), "sumsq_array")
+    return ss.value, nf.value

@@ -859,6 +859,25 @@ int or_regen_accum_acc(int32_t grad_dtype, int32_t n_ranks, int32_t n_micro, int
   return 0;
 }
 
+/* The squared norm and overflow flag of given reduced values (steps 2-3 of
+ * the step, [MDT] 四.3 check overflow then clip by the global norm): used
+ * where the values are not the plain sums, e.g. sums rounded to the
+ * gradient dtype before an offloaded update ([L13] 7.1's 16-bit gradient
+ * edge). */
+int or_sumsq_array(int64_t n, const float* x, double* sumsq, int32_t* nonfinite) {
+  int64_t i;
+  double ss = 0.0;
+  int32_t nf = 0;
+  if (!sumsq || !nonfinite || n < 0 || (n > 0 && !x)) return -1;
+  for (i = 0; i < n; ++i) {
+    if (!isfinite(x[i])) nf = 1;
+    ss += (double)x[i] * (double)x[i];
+  }
+  *sumsq = ss;
+  *nonfinite = nf;
+  return 0;
+}
+
 int or_regen_sumsq(int32_t grad_dtype, int32_t n_ranks, uint64_t seed, int64_t step, double sigma,
                    double scale, int64_t i0, int64_t i1, const or_inject* inj, double* sumsq,
                    int32_t* nonfinite) {

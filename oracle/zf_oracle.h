@@ -166,6 +166,9 @@ int or_regen_accum_sumsq(int32_t grad_dtype, int32_t n_ranks, int32_t n_micro, i
 int or_regen_accum_acc(int32_t grad_dtype, int32_t n_ranks, int32_t n_micro, int32_t mode,
                        uint64_t seed, int64_t step, double sigma, double scale, int64_t n,
                        const int64_t* logical_idx, const or_inject* inj, float* acc_out);
+/* Steps 2-3 of the step on n given reduced values in their order: the
+ * squared norm sum of (double)x^2 and the overflow flag (any non-finite). */
+int or_sumsq_array(int64_t n, const float* x, double* sumsq, int32_t* nonfinite);
 
 #ifdef __cplusplus
 }

@@ -14,7 +14,7 @@ after every step of
     reduced every micro-batch or (no_sync) accumulated locally and reduced
     once (three steps each),
   - the 654M decoder under ZeRO-Offload (fp32 state and CPU-Adam on the
-    host; three steps).
+    host), with fp32 or 16-bit sums going down (three steps each).
 
 The oracle side holds the full state on the host, in logical order.
 FullOracle carries every element through the oracle's own functions, split
@@ -55,7 +55,6 @@ class FullOracle:
     element by the oracle over a thread pool."""
 
     def __init__(self, w, threads=None):
-        assert not w.offload_down16
         self.w = w
         self.units, self.psi, self.psi_pad = OI.plan(w)
         assert self.psi == w.psi
@@ -91,6 +90,8 @@ class FullOracle:
         if inject_index is not None:
             inj = O.Inject(step=self.step_no, replica=w.inject_replica, index=int(inject_index),
                            bits=OI.inf_bits(w.grad_dtype))
+        if w.offload_down16:
+            return self._step_rounded(scale, inj, keep_sums)
         ss, bad = G.regen_sumsq_threaded(w, self.step_no, scale, self.psi, inj)
         sc, res = O.finish(ss, bad, w.n_ranks, self.hp, self.st)
         sums = np.empty(self.psi, np.float32) if keep_sums else None
@@ -109,6 +110,35 @@ class FullOracle:
 
         list(self.pool.map(part, range(len(self.edges) - 1)))
         return res, sums
+
+    def _step_rounded(self, scale, inj, keep_sums):
+        """The offload step with 16-bit sums down: the sums rounded to the
+        gradient dtype and widened back, the squared norm and the overflow
+        flag taken on those values (range partials added in order), then
+        the update from them.  The returned sums are the rounded values."""
+        w = self.w
+        rounded = np.empty(self.psi, np.float32)
+
+        def part(c):
+            a, b = self.edges[c], self.edges[c + 1]
+            acc = O.regen_accum_acc(w.grad_dtype, w.n_ranks, w.n_micro, w.accum_mode, w.seed,
+                                    self.step_no, w.sigma, scale, np.arange(a, b, dtype=np.int64),
+                                    inj)
+            rounded[a:b] = O.widen(w.grad_dtype, O.narrow(w.grad_dtype, acc))
+            return O.sumsq_array(rounded[a:b])
+
+        ss, bad = 0.0, 0
+        for s_c, b_c in self.pool.map(part, range(len(self.edges) - 1)):
+            ss += s_c
+            bad |= b_c
+        sc, res = O.finish(ss, bad, w.n_ranks, self.hp, self.st)
+        if not res.skipped:
+            def upd(c):
+                a, b = self.edges[c], self.edges[c + 1]
+                O.adamw_array(rounded[a:b], sc, self.p[a:b], self.m[a:b], self.v[a:b])
+
+            list(self.pool.map(upd, range(len(self.edges) - 1)))
+        return res, (rounded if keep_sums else None)
 
 
 def _chunks(pool, n, fn):
@@ -212,6 +242,22 @@ def check_sums(orc, t, units, sums, what):
         assert_zero(t[o + L:o + P], what)
 
 
+def check_sums16(orc, t16, units, rounded, dtype, what):
+    """16-bit sums (the first Psi' 16-bit words of the device's fp32
+    gradient-shard buffer) against the oracle's rounded sums, bit for bit;
+    padding zero."""
+    for u in units:
+        o, L, P, lam = int(u["O"]), int(u["L"]), int(u["P"]), int(u["lam"])
+
+        def one(a, b, o=o, lam=lam):
+            got = t16[o + a:o + b].cpu().numpy().view(np.uint16)
+            bad = np.flatnonzero(got != O.narrow(dtype, rounded[lam + a:lam + b]))
+            assert bad.size == 0, f"{what}: {bad.size} differ, first at {o + a + int(bad[0])}"
+
+        _chunks(orc.pool, L, one)
+        assert_zero(t16[o + L:o + P], what)
+
+
 def check_gathers(dev, orc, tally, what):
     """ZeRO-3: every unit gathered into the reused unit buffer; FSDP2: every
     FSDP unit cast-gathered into the reused group buffer.  Each against
@@ -238,9 +284,10 @@ def test_full_oracle_matches_single_threaded(orc):
     update) tracks the oracle's own single-threaded step (O.zero_step, and
     O.step_reduced after the backward-side reduction, via OracleRun) for
     three steps: at N = 4 on a 5,000,004-element flat with a norm weight
-    range and clipping active, and at N = 3 on three ragged units (padding)
+    range and clipping active, at N = 3 on three ragged units (padding)
     whose gradients are reduce-scattered in buckets over three
-    micro-batches, in both accumulation schemes.  The same results, the
+    micro-batches, in both accumulation schemes, and at N = 2 with the sums
+    rounded to bf16 on their way to an offloaded update.  The same results, the
     norm to within rounding, the sums bit for bit, the state within 4 ulp
     and almost all bit for bit."""
     segs = [W.Segment("w", 4_000_000, 0), W.Segment("n", 4, 0, W.KIND_NORM),
@@ -258,6 +305,11 @@ def test_full_oracle_matches_single_threaded(orc):
             n_ranks=3, layout=W.PER_UNIT, stage=2, grad_dtype=W.F16, param_dtype=W.F16,
             sigma=1e-3, loss_scale=1024.0, dynamic=True, lr=1e-3, steps=3, seed=17,
             max_norm=0.5, n_micro=3, accum_mode=mode, bucket_numel=400_000))
+    cases.append(W.Workload(
+        name="flat-offload16", description="", segments=[W.Segment("f", 2_000_002, 0)],
+        n_ranks=2, layout=W.GLOBAL_FLAT, stage=2, grad_dtype=W.BF16, param_dtype=W.BF16,
+        sigma=1e-3, loss_scale=1.0, dynamic=False, lr=1e-3, steps=3, seed=19, max_norm=0.5,
+        offload=True, offload_down16=True))
     for w in cases:
         full = FullOracle(w, threads=4)
         ref = OI.OracleRun(w)
@@ -270,6 +322,8 @@ def test_full_oracle_matches_single_threaded(orc):
                     grads = OI.replicas(w, ref.units, ref.psi_pad, k, ref.st.loss_scale)
                     sums_ref = OI.rank_shards_to_logical(
                         ref.units, O.reduce_scatter(w.grad_dtype, w.n_ranks, ref.units, grads))
+                    if w.offload_down16:  # the sums as they go down: rounded to bf16
+                        sums_ref = O.widen(w.grad_dtype, O.narrow(w.grad_dtype, sums_ref))
                     r_ref = ref.step(grads)
                 r_full, sums = full.step(keep_sums=True)
                 assert (r_full.skipped, r_full.t, r_full.scale_next) == \
@@ -386,7 +440,10 @@ def run_full(R, w, twin_sums=False, rs_first_step=True):
             res_o, sums = orc.step(inject_index=inj if w.inject_step == k else None,
                                    keep_sums=keep)
             G.assert_result_matches(res_d, res_o, f"{w.name} step {k}")
-            if sums is not None:
+            if sums is not None and w.offload_down16:
+                check_sums16(orc, dev.grad_shards.view(torch.int16)[:dev.psi_pad], units, sums,
+                             w.grad_dtype, f"{w.name} step {k} 16-bit reduce-scatter sums")
+            elif sums is not None:
                 src = twin.grad_shards if twin is not None else \
                     (dev.grad_shards if resident_sums else rs)
                 check_sums(orc, src, units, sums, f"{w.name} step {k} reduce-scatter sums")
@@ -479,6 +536,17 @@ def test_llama654m_offload_every_element(R):
     the host (every element), bf16 parameters come back in chunks."""
     dev, trace = run_full(R, "llama-654m-n2-offload")
     assert dev.master.device.type == "cpu"
+    assert all(t[1] == 0 and abs(t[5] - 3.0) < 0.1 and t[6] < 1.0 for t in trace)
+
+
+@pytest.mark.gpu
+def test_llama654m_offload16_every_element(R):
+    """The same with 16-bit sums down: the GPU rounds the sums to bf16
+    (bit for bit every step), the norm and overflow are taken on the rounded
+    values and CPU-Adam updates from them (every element of the host
+    state)."""
+    dev, trace = run_full(R, "llama-654m-n2-offload16")
+    assert dev.w.offload_down16 and dev.master.device.type == "cpu"
     assert all(t[1] == 0 and abs(t[5] - 3.0) < 0.1 and t[6] < 1.0 for t in trace)
 
 

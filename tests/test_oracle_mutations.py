@@ -74,6 +74,15 @@ MUTANTS = [
     ("fp32 draws ignore sigma",
      "for (i = 0; i < n; ++i) dst[i] = or_normal_z(st, logical_base + i) * sf;",
      "for (i = 0; i < n; ++i) dst[i] = or_normal_z(st, logical_base + i) * (sf / sf);"),
+    ("squared norm of an array skips its last value",
+     "  for (i = 0; i < n; ++i) {\n    if (!isfinite(x[i])) nf = 1;\n    ss += (double)x[i] * (double)x[i];",
+     "  for (i = 0; i < n; ++i) {\n    if (!isfinite(x[i])) nf = 1;\n    if (i + 1 < n) ss += (double)x[i] * (double)x[i];"),
+    ("squared norm of an array squares in binary32",
+     "    ss += (double)x[i] * (double)x[i];\n  }\n  *sumsq = ss;",
+     "    ss += (double)(x[i] * x[i]);\n  }\n  *sumsq = ss;"),
+    ("overflow flag of an array misses NaN",
+     "    if (!isfinite(x[i])) nf = 1;\n    ss += (double)x[i] * (double)x[i];\n  }\n  *sumsq = ss;",
+     "    if (isinf(x[i])) nf = 1;\n    ss += (double)x[i] * (double)x[i];\n  }\n  *sumsq = ss;"),
     ("Irwin-Hall centred on the wrong mean",
      "return (float)(sum - 393210) / 65536.0f;", "return (float)(sum - 393216) / 65536.0f;"),
     ("FSDP2 chunk rows rounded the wrong way",

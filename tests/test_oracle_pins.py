@@ -587,6 +587,34 @@ def test_norm_exact_on_dyadic_inputs(orc):
         assert res.norm == 64 * 2.0 ** -10 and res.coef == 1.0
 
 
+def test_sumsq_array(orc):
+    """The squared norm of given values: exact on dyadic values with known
+    counts; bit-identical to the regeneration's own sum over the same range
+    (same values, same order); within the recursive-summation bound of
+    math.fsum on random values; the flag set by +inf, -inf or NaN anywhere
+    and by nothing finite; empty input gives 0."""
+    rng = np.random.default_rng(23)
+    k = rng.integers(-30, 10, 5000)
+    sign = rng.choice([-1.0, 1.0], 5000)
+    x = (sign * np.ldexp(1.0, k)).astype(np.float32)
+    exact = sum(math.ldexp(1.0, 2 * int(e)) for e in k)  # every square is a power of two
+    ss, nf = O.sumsq_array(x)
+    assert nf == 0 and ss == exact
+    acc = O.regen_acc(O.BF16, 3, 5, 2, 1e-3, 1.0, np.arange(1000, 41000, dtype=np.int64))
+    ref_ss, ref_nf = O.regen_sumsq(O.BF16, 3, 5, 2, 1e-3, 1.0, 1000, 41000)
+    assert O.sumsq_array(acc) == (ref_ss, ref_nf)
+    y = rng.standard_normal(100_000).astype(np.float32)
+    ss, _ = O.sumsq_array(y)
+    want = math.fsum(float(v) * float(v) for v in y)
+    assert abs(ss - want) <= y.size * 2.0 ** -53 * want
+    for bad in (np.inf, -np.inf, np.nan):
+        z = y.copy()
+        z[77] = bad
+        assert O.sumsq_array(z)[1] == 1
+    assert O.sumsq_array(np.array([3.0e38, -3.0e38], np.float32))[1] == 0
+    assert O.sumsq_array(np.zeros(0, np.float32)) == (0.0, 0)
+
+
 def test_tiny_workload_trajectory(orc):
     """The tiny workload: norm close to sigma*sqrt(Psi/N) = 0.090, never
     clipped (coefficient exactly 1), never skipped, over ten steps."""
