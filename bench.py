@@ -242,6 +242,32 @@ def summarize_trace(directory, out, command, bench_json=None):
                      f"{float(r['MinNs']) / 1e3:>10.2f} {float(r['MaxNs']) / 1e3:>10.2f} "
                      f"{float(r['Percentage']):>6.2f}")
     import glob
+    # the update pass of a skipped step exits at once: its launches are
+    # listed apart from the applied ones (a run with the skipped-step probe
+    # has both under one kernel name)
+    traces = glob.glob(os.path.join(directory, "**", "*kernel_trace.csv"), recursive=True)
+    if traces:
+        durs = {}
+        with open(traces[0]) as f:
+            import csv
+            for r in csv.DictReader(f):
+                if "zf_pass2" in r["Kernel_Name"]:
+                    name = r["Kernel_Name"].replace("(anonymous namespace)::", "")
+                    durs.setdefault(name, []).append(
+                        (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        split = []
+        for name, xs in sorted(durs.items()):
+            med = sorted(xs)[len(xs) // 2]
+            # an empty launch costs only the dispatch of its blocks: well
+            # under half an applied one at every size
+            full = [x for x in xs if x >= 0.5 * med]
+            short = [x for x in xs if x < 0.5 * med]
+            if short:
+                split.append(f"{name[:70]:<70} applied {len(full):>4} x {sum(full) / len(full):>10.2f}"
+                             f" us; exited at once (skipped steps) {len(short):>3} x "
+                             f"{sum(short) / len(short):.2f} us")
+        if split:
+            lines += ["", "update-pass launches (kernel trace), applied and skipped:"] + split
     if glob.glob(os.path.join(directory, "**", "*marker_api_stats.csv"), recursive=True):
         lines += ["", "roctx ranges (host time from push to pop; the enqueue waits once the "
                       "launch queue is full, so it follows the device's pace):",
@@ -254,18 +280,23 @@ def summarize_trace(directory, out, command, bench_json=None):
         with open(bench_json) as f:
             rows = [ln for ln in f if ln.startswith("{")]
         d = json.loads(rows[-1])
-        roof = {k: d["roofline"].get(k) for k in
-                ("kernel", "achieved", "frac", "design_gbs", "frac_design_bytes",
-                 "hbm_gbs_design_less_window", "hbm_frac_of_4r4w_probe", "traffic")
-                if k in d["roofline"]}
-        lines += ["", "bench line of the same profiled run (HIP events on the step's stream, "
-                      "ms):",
-                  f"  kernels_ms: {json.dumps(d.get('kernels_ms', d.get('phases_ms')))}",
-                  f"  stream_probe_gbs: {json.dumps(d.get('stream_probe_gbs'))}",
-                  f"  roofline: {json.dumps(roof)}",
-                  f"  ms_per_step: {d['ms_per_step']}  value (GB/s): {d['value']}  "
-                  f"pct_hbm_peak: {d['pct_hbm_peak']}  device_copy_gbs: "
-                  f"{d.get('device_copy_gbs')}"]
+
+        def excerpt(d, label):
+            roof = {k: d["roofline"].get(k) for k in
+                    ("kernel", "achieved", "frac", "design_gbs", "frac_design_bytes",
+                     "hbm_gbs_design_less_window", "hbm_frac_of_4r4w_probe", "traffic",
+                     "traffic_dram32") if k in d["roofline"]}
+            return [f"{label} (HIP events on the step's stream, ms):",
+                    f"  kernels_ms: {json.dumps(d.get('kernels_ms', d.get('phases_ms')))}",
+                    f"  roofline: {json.dumps(roof)}",
+                    f"  ms_per_step: {d['ms_per_step']}  value (GB/s): {d['value']}  "
+                    f"pct_hbm_peak: {d['pct_hbm_peak']}"]
+
+        lines += [""] + excerpt(d, "bench line of the same profiled run")
+        lines += [f"  stream_probe_gbs: {json.dumps(d.get('stream_probe_gbs'))}  "
+                  f"device_copy_gbs: {d.get('device_copy_gbs')}"]
+        if "headline_2" in d:
+            lines += excerpt(d["headline_2"], f"its headline_2 ({d['headline_2']['workload']})")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
