@@ -247,15 +247,9 @@ struct FinishArgs {
   int32_t np, n_ranks;
 };
 
-__global__ __launch_bounds__(kThreads) void zf_finish(FinishArgs a) {
-  double ss = 0.0;
-  uint32_t bad = 0;
-  for (int i = threadIdx.x; i < a.np; i += kThreads) {
-    ss = ss + a.partials[i].ss;
-    bad = bad | a.partials[i].bad;
-  }
-  block_reduce(ss, bad);
-  if (threadIdx.x != 0) return;
+// The step's scalars from the total squared norm and the overflow bits
+// (one thread).
+__device__ __forceinline__ void finish_state(const FinishArgs& a, double ss, uint32_t bad) {
   DevState* s = a.st;
   s->overflow = bad ? 1 : 0;
   s->sumsq = ss;
@@ -294,6 +288,32 @@ __global__ __launch_bounds__(kThreads) void zf_finish(FinishArgs a) {
   s->gs = (float)(coef / sn);
   s->bc1 = (float)(1.0 - s->beta1_pow);
   s->bc2 = (float)(1.0 - s->beta2_pow);
+}
+
+__global__ __launch_bounds__(kThreads) void zf_finish(FinishArgs a) {
+  double ss = 0.0;
+  uint32_t bad = 0;
+  for (int i = threadIdx.x; i < a.np; i += kThreads) {
+    ss = ss + a.partials[i].ss;
+    bad = bad | a.partials[i].bad;
+  }
+  block_reduce(ss, bad);
+  if (threadIdx.x == 0) finish_state(a, ss, bad);
+}
+
+// Level 2 and the finish in one launch, for plans whose norm reduction has
+// a single level-2 block: that block reduces every tile partial in the
+// order zf_level2 does and finishes.  The result is the same bits as the
+// two launches, whose finish would add zeros to the one level-2 partial.
+__global__ __launch_bounds__(kThreads) void zf_level2_finish(Level2Args l, FinishArgs a) {
+  double ss = 0.0;
+  uint32_t bad = 0;
+  for (int64_t i = threadIdx.x; i < l.n_in; i += kThreads) {
+    ss = ss + l.in[i].ss;
+    bad = bad | l.in[i].bad;
+  }
+  block_reduce(ss, bad);
+  if (threadIdx.x == 0) finish_state(a, ss, bad);
 }
 
 // ---------------------------------------------------------------------------
@@ -662,9 +682,6 @@ int zf::step_enqueue(const zf_plan* plan, const zf_hparams* hp, const zf_step_ar
   a2l.in = partials;
   a2l.out = partials2;
   a2l.n_in = plan->pass1_tiles;
-  hipLaunchKernelGGL(zf_level2, dim3((uint32_t)plan->level2_blocks), dim3(kThreads), 0, s, a2l);
-  if (!hip_ok(hipGetLastError())) return ZF_EHIP;
-
   FinishArgs af;
   af.partials = partials2;
   af.st = static_cast<DevState*>(args->state);
@@ -673,8 +690,16 @@ int zf::step_enqueue(const zf_plan* plan, const zf_hparams* hp, const zf_step_ar
   af.max_norm = hp->max_norm;
   af.np = plan->level2_blocks;
   af.n_ranks = nr;
-  hipLaunchKernelGGL(zf_finish, dim3(1), dim3(kThreads), 0, s, af);
-  if (!hip_ok(hipGetLastError())) return ZF_EHIP;
+  if (plan->level2_blocks == 1) {
+    hipLaunchKernelGGL(zf_level2_finish, dim3(1), dim3(kThreads), 0, s, a2l, af);
+    if (!hip_ok(hipGetLastError())) return ZF_EHIP;
+  } else {
+    hipLaunchKernelGGL(zf_level2, dim3((uint32_t)plan->level2_blocks), dim3(kThreads), 0, s,
+                       a2l);
+    if (!hip_ok(hipGetLastError())) return ZF_EHIP;
+    hipLaunchKernelGGL(zf_finish, dim3(1), dim3(kThreads), 0, s, af);
+    if (!hip_ok(hipGetLastError())) return ZF_EHIP;
+  }
   if ((rc = record(args->phase_events, 2, s)) != ZF_OK) return rc;
   if (!update) return ZF_OK;
 
