@@ -51,8 +51,9 @@
  *     reported as ZF_EHIP (the stream may then hold part of the step).
  *   - An overflow (skipped step) is a result, not an error.
  *   - No call aborts or throws.
- *   - HIP graphs: zf_shard_step, zf_reduce_scatter, zf_gather,
- *     zf_gather_cast, zf_bucket_reduce_scatter, zf_accumulate and
+ *   - HIP graphs: zf_shard_step, zf_shard_step_noalloc (after its first
+ *     call on the device), zf_reduce_scatter, zf_gather, zf_gather_cast,
+ *     zf_bucket_reduce_scatter, zf_accumulate and
  *     zf_state_init enqueue kernels only (no memset, copy, allocation or
  *     synchronisation; every pointer travels by value in the kernel
  *     arguments), so a caller may capture them on a stream and replay the
