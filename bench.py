@@ -284,7 +284,8 @@ def summarize_trace(directory, out, command, bench_json=None):
         def excerpt(d, label):
             roof = {k: d["roofline"].get(k) for k in
                     ("kernel", "achieved", "frac", "design_gbs", "frac_design_bytes",
-                     "hbm_gbs_design_less_window", "hbm_frac_of_4r4w_probe", "traffic",
+                     "hbm_gbs_design_less_window", "hbm_frac_of_4r4w_probe",
+                     "own_mix_probe", "frac_of_own_mix_probe", "traffic",
                      "traffic_dram32") if k in d["roofline"]}
             return [f"{label} (HIP events on the step's stream, ms):",
                     f"  kernels_ms: {json.dumps(d.get('kernels_ms', d.get('phases_ms')))}",
@@ -300,6 +301,58 @@ def summarize_trace(directory, out, command, bench_json=None):
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+def summarize_table(jsonl, out, command):
+    """Markdown table of bench lines (one JSON line per workload, as the
+    bench prints them) written to `out`."""
+    with open(jsonl) as f:
+        rows = [json.loads(ln) for ln in f if ln.startswith("{")]
+    L = ["# bench.py on one MI355X: every workload (same box, one run)", "",
+         f"command: `{command}`", "",
+         "Columns: ms/step = K timed steps over K; algorithmic = the method's bytes per step "
+         "(`algorithmic_bytes_per_param` x Psi) over the step time, and its share of 8 TB/s "
+         "(`pct_hbm_peak`, the bench's headline figure); roofline frac = the dominant "
+         "kernel's algorithmic bytes per launch over its mean duration (HIP events in the "
+         "same run), over 8 TB/s; design frac = the same kernel's actual bytes (with the "
+         "global-norm barrier's re-read) over 8 TB/s; HBM/probe = the update pass's actual "
+         "bytes less the cache window's reads, per second, over the box's best "
+         "4-read/4-write probe; own-mix probe = the time of a kernel that moves the update "
+         "pass's 30 bytes per element with no arithmetic (its sums read from HBM) over the "
+         "update pass's time, on equal element counts; counted HBM = FETCH_SIZE + "
+         "WRITE_SIZE of every step kernel (committed summaries of the same code, each "
+         "counter scaled by its reading for a 1 GiB copy) less the cache window's reads, per "
+         "step time; L2 egress = the same without that subtraction; graph = the same K "
+         "steps replayed from a HIP graph of 10 steps.", "",
+         "| workload | ms/step | algorithmic GB/s (% of 8 TB/s) | params/s | roofline kernel | "
+         "roofline frac (algorithmic) | design frac | HBM / 4+4 probe | own-mix probe | "
+         "counted HBM GB/s (% of 8 TB/s) | L2 egress GB/s | skipped step ms | graph ms/step "
+         "| probes 1+1 / 4+4 / 8+1 / update mix (replicas, sums) GB/s | phases (ms) |",
+         "|" + "---|" * 15]
+    for d in rows:
+        r, p = d["roofline"], d.get("stream_probe_gbs", {})
+        ph = d.get("kernels_ms") or d.get("phases_ms") or {}
+        g = d.get("graph_replay", {}).get("ms_per_step", "—")
+        counted = (f"{d['hbm_gbs_counted']:.0f} ({d['pct_hbm_peak_counted']:.1f}%)"
+                   if "hbm_gbs_counted" in d else "—")
+        probes = " / ".join(str(p.get(k, "—")) for k in
+                            ("1r1w", "4r4w", "8r1w", "update_mix_replicas", "update_mix_sums"))
+        L.append(f"| {d['config']['workload']} | {d['ms_per_step']:.4f} | {d['value']:.0f} "
+                 f"({d['pct_hbm_peak']:.1f}%) | {d['params_updated_per_s']:.3g} | "
+                 f"{r['kernel'].split(' (')[0]} | {r['frac']:.3f} | "
+                 f"{r.get('frac_design_bytes', '—')} | {r.get('hbm_frac_of_4r4w_probe', '—')} | "
+                 f"{r.get('frac_of_own_mix_probe', '—')} | {counted} | "
+                 f"{d.get('l2_egress_gbs_counted', '—')} | {d.get('skipped_step_ms', '—')} | "
+                 f"{g} | {probes} | " + ", ".join(f"{k} {v}" for k, v in ph.items()) + " |")
+    for d in rows:
+        if "cpu_baseline" in d:
+            cb = d["cpu_baseline"]
+            L += ["", f"CPU baseline ({d['config']['workload']}): {cb['value']} GB/s "
+                      f"algorithmic, {cb['params_per_s']:.3g} params/s, {cb['s_per_step']} "
+                      f"s/step, {cb['cores']} core(s): {cb['sample']}"]
+    with open(out, "w") as f:
+        f.write("\n".join(L) + "\n")
+    print("\n".join(L))
 
 
 def summarize_pmc(fetch_dir, write_dir, workload, out, commands):
@@ -465,10 +518,36 @@ def stream_probes(reps=10):
             if g > best:
                 best, which = g, f"q{q}c{c}"
         out[name], shape[name] = round(best, 1), which
+    # the update pass's own bytes (30 per element: two 16-bit replicas or
+    # fp32 sums in, fp32 master/m/v in and out, the 16-bit parameter out)
+    p, m, v, o = bufs[2], bufs[3], bufs[4], bufs[5]
+    for name, g in (("update_mix_replicas", (bufs[0], bufs[1])), ("update_mix_sums", bufs[0])):
+        best, which = 0.0, None
+        for t, c in MIX_SHAPES:
+            gb = gbs(lambda: I.update_mix_probe(g, p, m, v, o, PROBE_FLOATS, t, c),
+                     UPDATE_MIX_BYTES * PROBE_FLOATS)
+            if gb > best:
+                best, which = gb, f"t{t}c{c}"
+        out[name], shape[name] = round(best, 1), which
     del bufs
     torch.cuda.empty_cache()
     out["shape"] = shape
     return out
+
+
+# the update-mix probe's shapes (threads per block, resident blocks per CU)
+MIX_SHAPES = tuple((t, c) for t in (128, 256) for c in (0, 2, 3, 4, 6))
+UPDATE_MIX_BYTES = 30
+
+
+def own_mix_probe(w, materialized):
+    """The stream_probes key whose bytes per element equal the update pass's
+    (None where no probe has its mix: N = 3 or 4 recomputing, fp32 params)."""
+    if w.fp32_params:
+        return None
+    if materialized or w.backward_rs:
+        return "update_mix_sums"
+    return "update_mix_replicas" if w.n_ranks == 2 else None
 
 
 def apply_overrides(w, items):
@@ -857,6 +936,15 @@ def bench_workload(w, args, probe, copy_gbs, graph=True, skip_probe=True):
         # the update pass's HBM-side rate (its bytes less the window's cache
         # hits) against the best probe of its 4-read / 4-write mix
         roof["hbm_frac_of_4r4w_probe"] = round(hbm_gbs / probe["4r4w"], 4)
+        mix = own_mix_probe(w, materialized)
+        if mix is not None:
+            # the same bytes per element moved by a kernel with no
+            # arithmetic (its sums, if any, read from HBM): probe time over
+            # the update pass's time on equal element counts
+            assert update_kernel_bytes_per_elem(w, materialized or w.backward_rs) == \
+                UPDATE_MIX_BYTES
+            roof["own_mix_probe"] = mix
+            roof["frac_of_own_mix_probe"] = round(design_gbs / probe[mix], 4)
     line["ms_per_step_median"] = round(per_step[len(per_step) // 2], 5)
     line["ms_per_step_min"] = round(per_step[0], 5)
     counted = counted_bytes_per_step(w)
@@ -929,6 +1017,8 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"))
     ap.add_argument("--summarize-dram32", nargs=2, metavar=("DIR", "OUT"),
                     help="summary of a run with --pmc " + " ".join(DRAM32_COUNTERS))
+    ap.add_argument("--summarize-table", nargs=2, metavar=("JSONL", "OUT"),
+                    help="markdown table of bench lines, one workload per line")
     ap.add_argument("--command", default="", help="command text recorded in a summary")
     args = ap.parse_args()
     default_run = args.workload is None and not args.set and not args.no_headline_2
@@ -937,6 +1027,9 @@ def main():
     args.workload = args.workload or DEFAULT_WORKLOAD
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace, args.command, args.bench_json)
+        return
+    if args.summarize_table:
+        summarize_table(*args.summarize_table, args.command)
         return
     if args.summarize_dram32:
         summarize_dram32(args.summarize_dram32[0], args.workload, args.summarize_dram32[1],

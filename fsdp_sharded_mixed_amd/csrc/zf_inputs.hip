@@ -264,6 +264,101 @@ extern "C" int zfi_stream_probe(const float* const* src, int32_t n_src, float* c
 }
 
 // ---------------------------------------------------------------------------
+// Update-mix probe: the update pass's bytes per element with none of its
+// arithmetic.  One quad per lane, T-thread blocks, at most `cap` resident
+// blocks per CU (dynamic LDS that no lane touches; nq is never negative).
+// MODE 2 reads two 16-bit arrays (the replicas an N = 2 update pass
+// re-reads, plain loads); MODE 0 one fp32 array (materialised sums, plain
+// loads).  Both then read three fp32 arrays with the non-temporal hint and
+// write them back, and write one 16-bit array, all stores non-temporal.
+namespace {
+
+typedef uint32_t u32x2p __attribute__((ext_vector_type(2)));
+
+struct MixArgs {
+  const uint16_t* g0;
+  const uint16_t* g1;
+  const float* sums;
+  float* p;
+  float* m;
+  float* v;
+  uint16_t* out;
+  int64_t nq;
+};
+
+template <int MODE, int T>
+__global__ __launch_bounds__(256) void update_mix_probe(MixArgs a) {
+  extern __shared__ uint32_t probe_cap_lds[];
+  if (a.nq < 0) probe_cap_lds[threadIdx.x] = 0u;
+  const int64_t q = (int64_t)blockIdx.x * T + threadIdx.x;
+  if (q >= a.nq) return;
+  f32x4p g;
+  if constexpr (MODE == 2) {
+    const u32x2p x0 = reinterpret_cast<const u32x2p*>(a.g0)[q];
+    const u32x2p x1 = reinterpret_cast<const u32x2p*>(a.g1)[q];
+    g = (f32x4p){__uint_as_float(x0.x << 16), __uint_as_float(x0.y << 16),
+                 __uint_as_float(x1.x << 16), __uint_as_float(x1.y << 16)};
+  } else {
+    g = reinterpret_cast<const f32x4p*>(a.sums)[q];
+  }
+  f32x4p p = __builtin_nontemporal_load(reinterpret_cast<const f32x4p*>(a.p) + q);
+  f32x4p m = __builtin_nontemporal_load(reinterpret_cast<const f32x4p*>(a.m) + q);
+  f32x4p v = __builtin_nontemporal_load(reinterpret_cast<const f32x4p*>(a.v) + q);
+  p = p + g;
+  m = m + g;
+  v = v + g;
+  __builtin_nontemporal_store(p, reinterpret_cast<f32x4p*>(a.p) + q);
+  __builtin_nontemporal_store(m, reinterpret_cast<f32x4p*>(a.m) + q);
+  __builtin_nontemporal_store(v, reinterpret_cast<f32x4p*>(a.v) + q);
+  const u32x2p o = {(__float_as_uint(p.x) >> 16) | (__float_as_uint(p.y) & 0xFFFF0000u),
+                    (__float_as_uint(p.z) >> 16) | (__float_as_uint(p.w) & 0xFFFF0000u)};
+  __builtin_nontemporal_store(o, reinterpret_cast<u32x2p*>(a.out) + q);
+}
+
+template <int MODE>
+void launch_mix(int threads, dim3 g, uint32_t lds, hipStream_t s, const MixArgs& a) {
+  if (threads == 128) hipLaunchKernelGGL((update_mix_probe<MODE, 128>), g, dim3(128), lds, s, a);
+  else hipLaunchKernelGGL((update_mix_probe<MODE, 256>), g, dim3(256), lds, s, a);
+}
+
+bool aligned16p(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" int zfi_update_mix_probe(const void* g0, const void* g1, const float* sums, float* p,
+                                    float* m, float* v, void* out16, int64_t n,
+                                    int32_t block_threads, int32_t blocks_per_cu,
+                                    void* stream_handle) {
+  const bool replicas = g0 != nullptr || g1 != nullptr;
+  if (replicas ? (!g0 || !g1 || sums) : !sums) return -1;
+  if (!p || !m || !v || !out16 || n <= 0 || n % 4 != 0) return -1;
+  const void* all[] = {replicas ? g0 : sums, replicas ? g1 : sums, p, m, v, out16};
+  for (const void* q : all)
+    if (!aligned16p(q)) return -1;
+  if (block_threads != 128 && block_threads != 256) return -1;
+  if (blocks_per_cu < 0 || blocks_per_cu > 8) return -1;
+  MixArgs a;
+  a.g0 = static_cast<const uint16_t*>(g0);
+  a.g1 = static_cast<const uint16_t*>(g1);
+  a.sums = sums;
+  a.p = p;
+  a.m = m;
+  a.v = v;
+  a.out = static_cast<uint16_t*>(out16);
+  a.nq = n / 4;
+  const int64_t blocks = (a.nq + block_threads - 1) / block_threads;
+  if (blocks > 0x7FFFFFFF) return -1;
+  const dim3 g((uint32_t)blocks);
+  // a CU holds 160 KiB of LDS: k blocks fit, k + 1 do not
+  const uint32_t lds = blocks_per_cu ? (uint32_t)(160 * 1024 / (blocks_per_cu + 1) + 1024) : 0u;
+  hipStream_t s = static_cast<hipStream_t>(stream_handle);
+  (void)hipGetLastError();
+  if (replicas) launch_mix<2>(block_threads, g, lds, s, a);
+  else launch_mix<0>(block_threads, g, lds, s, a);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+// ---------------------------------------------------------------------------
 // Lowering probes: binary32 square root and division as this compiler emits
 // them under the step library's flags (correctly rounded divide and sqrt,
 // no contraction), for tests that compare them with IEEE results.

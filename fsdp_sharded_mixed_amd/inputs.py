@@ -32,6 +32,10 @@ def _load():
                                             C.c_int32, C.c_int32, C.c_void_p]
     lib.zfi_stream_output.restype = C.c_uint64
     lib.zfi_stream_output.argtypes = [C.c_uint64, C.c_uint64, C.c_uint64]
+    lib.zfi_update_mix_probe.restype = C.c_int
+    lib.zfi_update_mix_probe.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                         C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64,
+                                         C.c_int32, C.c_int32, C.c_void_p]
     lib.zfi_sqrt_probe.restype = C.c_int
     lib.zfi_sqrt_probe.argtypes = [C.c_void_p, C.c_int64, C.c_uint32, C.c_void_p]
     lib.zfi_div_probe.restype = C.c_int
@@ -97,6 +101,22 @@ def stream_probe_shaped(srcs, dsts, quads, blocks_per_cu, n=None, stream=None):
                                      int(blocks_per_cu), _stream(stream))
     if rc != 0:
         raise RuntimeError(f"zfi_stream_probe_shaped failed ({rc})")
+
+
+def update_mix_probe(g, p, m, v, out16, n, block_threads, blocks_per_cu, stream=None):
+    """zfi_update_mix_probe: the update pass's bytes with no arithmetic.  `g`
+    is a pair of tensors (two 16-bit gradient replicas, read as n 16-bit
+    elements each) or one fp32 tensor (sums); p, m, v fp32; out16 holds n
+    16-bit elements."""
+    if isinstance(g, (tuple, list)):
+        g0, g1, sums = g[0].data_ptr(), g[1].data_ptr(), None
+    else:
+        g0, g1, sums = None, None, g.data_ptr()
+    rc = lib.zfi_update_mix_probe(g0, g1, sums, p.data_ptr(), m.data_ptr(), v.data_ptr(),
+                                  out16.data_ptr(), int(n), int(block_threads),
+                                  int(blocks_per_cu), _stream(stream))
+    if rc != 0:
+        raise RuntimeError(f"zfi_update_mix_probe failed ({rc})")
 
 
 def sqrt_probe(out, first_bits, n=None, stream=None):

@@ -60,6 +60,21 @@ int zfi_stream_probe_shaped(const float* const* src, int32_t n_src, float* const
                             int32_t n_dst, int64_t n, int32_t quads, int32_t blocks_per_cu,
                             void* stream_handle);
 
+/* Probe of the update pass's bytes with none of its arithmetic, so that the
+ * update pass can be compared with a kernel that only moves what it moves:
+ * per element, either two 16-bit arrays g0, g1 (the replicas an N = 2
+ * update pass re-reads; sums NULL) or one fp32 array `sums` (materialised
+ * sums; g0 = g1 = NULL) is read with plain loads, and p, m, v (fp32) are
+ * read non-temporal and written back non-temporal, p[i] += x, m[i] += x,
+ * v[i] += x (x the widened g0/g1 element, or sums[i]), with out16[i] the top
+ * 16 bits of the new p[i].  One 4-element quad per lane in blocks of
+ * block_threads (128 or 256), at most blocks_per_cu (0: no limit, 1..8)
+ * resident blocks per compute unit.  Device pointers, 16-byte aligned; n a
+ * multiple of 4.  Returns 0, -1 (bad argument) or -5. */
+int zfi_update_mix_probe(const void* g0, const void* g1, const float* sums, float* p, float* m,
+                         float* v, void* out16, int64_t n, int32_t block_threads,
+                         int32_t blocks_per_cu, void* stream_handle);
+
 /* Lowering probes for tests (no arithmetic of the step): binary32 sqrt and
  * division exactly as this compiler emits them under the step library's
  * flags (-fhip-fp32-correctly-rounded-divide-sqrt, -ffp-contract=off).

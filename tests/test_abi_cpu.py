@@ -38,7 +38,7 @@ def test_headers_declare_the_calls():
     assert _declared("zf_inputs.h") == sorted(["zfi_fill_normal16", "zfi_fill_normal32",
                                                "zfi_stream_output", "zfi_stream_probe",
                                                "zfi_stream_probe_shaped", "zfi_sqrt_probe",
-                                               "zfi_div_probe"])
+                                               "zfi_div_probe", "zfi_update_mix_probe"])
 
 
 @pytest.mark.parametrize("header,lib", [("zf.h", "libzf.so"), ("zf_inputs.h", "libzf_inputs.so")])

@@ -134,3 +134,19 @@ def test_update_pass_algorithmic_bytes(name, expected):
                                                 or w.backward_rs)
     assert design - expected == {"llama-73m-n8": 4, "llama-4.06b-n2": 4,
                                  "llama-2.1b-n2-zero3": 4}.get(name, 0)
+
+
+@pytest.mark.parametrize("name", sorted(W.ALL))
+def test_own_mix_probe_moves_the_update_pass_bytes(name):
+    """Where the bench names a probe of the update pass's own mix, that
+    probe moves the same bytes per element as the pass (30); FSDP2's fp32
+    parameters and N = 3 or 4 recomputing have none."""
+    w = W.get(name)
+    for materialized in (False, True):
+        mix = bench.own_mix_probe(w, materialized)
+        if mix is not None:
+            assert bench.update_kernel_bytes_per_elem(w, materialized or w.backward_rs) == \
+                bench.UPDATE_MIX_BYTES
+    assert bench.own_mix_probe(W.get("llama-2.1b-n2-fsdp2"), False) is None
+    assert bench.own_mix_probe(W.get("llama-654m-n2"), False) == "update_mix_replicas"
+    assert bench.own_mix_probe(W.get("llama-73m-n8"), True) == "update_mix_sums"
