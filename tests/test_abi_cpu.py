@@ -455,3 +455,36 @@ def test_noalloc_step_refuses_before_enqueueing(zf):
     assert huge.summary.policy == 0 and huge.summary.workspace_bytes > cap
     assert call(huge, huge_n) == -4
     assert Z.lib.zf_shard_step_noalloc(None, C.byref(hp), None, None) == -1
+
+
+def test_input_library_probes_refuse_before_launching():
+    """The bandwidth probes validate every argument before any HIP call: a
+    missing, misaligned or mixed gradient operand, a size that is not a
+    whole number of quads, or an unsupported shape returns -1 (the
+    addresses below are never dereferenced)."""
+    from fsdp_sharded_mixed_amd import inputs as I
+    f = I.lib.zfi_update_mix_probe
+    a, b, c, p, m, v, o = (0x10000 * k for k in range(1, 8))
+
+    def call(g0=a, g1=b, s=None, p=p, m=m, v=v, o=o, n=1024, t=128, cap=0):
+        return f(g0, g1, s, p, m, v, o, n, t, cap, None)
+
+    assert call(g1=None) == -1                       # one replica only
+    assert call(g0=None) == -1
+    assert call(s=c) == -1                           # replicas and sums both
+    assert call(g0=None, g1=None) == -1              # neither
+    assert call(g0=None, g1=None, s=c + 4) == -1     # misaligned sums
+    assert call(p=p + 8) == -1 and call(o=o + 2) == -1 and call(g1=b + 4) == -1
+    assert call(m=None) == -1 and call(o=None) == -1
+    assert call(n=0) == -1 and call(n=1026) == -1 and call(n=-4) == -1
+    assert call(t=64) == -1 and call(t=512) == -1
+    assert call(cap=-1) == -1 and call(cap=9) == -1
+    srcs = (C.c_void_p * 8)(*([a] * 8))
+    dsts = (C.c_void_p * 8)(*([b] * 8))
+    g = I.lib.zfi_stream_probe_shaped
+    assert g(srcs, 3, dsts, 1, 1024, 1, 0, None) == -1   # 3 sources
+    assert g(srcs, 1, dsts, 1, 1024, 3, 0, None) == -1   # 3 quads per lane
+    assert g(srcs, 1, dsts, 1, 1022, 1, 0, None) == -1
+    assert g(srcs, 1, dsts, 1, 1024, 1, 9, None) == -1
+    srcs[0] = a + 4
+    assert g(srcs, 1, dsts, 1, 1024, 1, 0, None) == -1
