@@ -294,10 +294,14 @@ __global__ __launch_bounds__(256) void update_mix_probe(MixArgs a) {
   if (q >= a.nq) return;
   f32x4p g;
   if constexpr (MODE == 2) {
+    // element i of each replica widened from bfloat16, the two added
     const u32x2p x0 = reinterpret_cast<const u32x2p*>(a.g0)[q];
     const u32x2p x1 = reinterpret_cast<const u32x2p*>(a.g1)[q];
-    g = (f32x4p){__uint_as_float(x0.x << 16), __uint_as_float(x0.y << 16),
-                 __uint_as_float(x1.x << 16), __uint_as_float(x1.y << 16)};
+    const f32x4p w0 = {__uint_as_float(x0.x << 16), __uint_as_float(x0.x & 0xFFFF0000u),
+                       __uint_as_float(x0.y << 16), __uint_as_float(x0.y & 0xFFFF0000u)};
+    const f32x4p w1 = {__uint_as_float(x1.x << 16), __uint_as_float(x1.x & 0xFFFF0000u),
+                       __uint_as_float(x1.y << 16), __uint_as_float(x1.y & 0xFFFF0000u)};
+    g = w0 + w1;
   } else {
     g = reinterpret_cast<const f32x4p*>(a.sums)[q];
   }

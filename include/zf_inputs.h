@@ -65,9 +65,10 @@ int zfi_stream_probe_shaped(const float* const* src, int32_t n_src, float* const
  * per element, either two 16-bit arrays g0, g1 (the replicas an N = 2
  * update pass re-reads; sums NULL) or one fp32 array `sums` (materialised
  * sums; g0 = g1 = NULL) is read with plain loads, and p, m, v (fp32) are
- * read non-temporal and written back non-temporal, p[i] += x, m[i] += x,
- * v[i] += x (x the widened g0/g1 element, or sums[i]), with out16[i] the top
- * 16 bits of the new p[i].  One 4-element quad per lane in blocks of
+ * read non-temporal and written back non-temporal: p[i] += x, m[i] += x,
+ * v[i] += x in binary32, where x = bf16(g0[i]) + bf16(g1[i]) (the 16-bit
+ * arrays read as bfloat16) or x = sums[i], and out16[i] = the top 16 bits
+ * of the new p[i].  One 4-element quad per lane in blocks of
  * block_threads (128 or 256), at most blocks_per_cu (0: no limit, 1..8)
  * resident blocks per compute unit.  Device pointers, 16-byte aligned; n a
  * multiple of 4.  Returns 0, -1 (bad argument) or -5. */
