@@ -218,6 +218,12 @@ int64_t zf_state_bytes(void);
 int zf_state_init(void* d_state, double loss_scale, int32_t dynamic, int32_t growth_interval,
                   void* stream);
 
+/* AdamW's hyperparameters as doubles; every binary32 constant of the
+ * update is rounded once from them.  beta1 and beta2 must lie in [0, 1)
+ * (ZF_EINVAL otherwise); lr, eps and weight_decay are used as given.  With
+ * eps = 0 an element whose updated exp_avg and exp_avg_sq are both zero (the
+ * zero padding, or a zero gradient on zero state) becomes NaN, as the
+ * formula says (0/0): pass eps > 0 to keep the padding zero. */
 typedef struct {
   double lr, beta1, beta2, eps, weight_decay;
   double max_norm;  /* global L2 clip threshold; <= 0 disables clipping */
@@ -264,7 +270,9 @@ typedef struct {
 
 /* One emulated step for all N ranks ([L13] 3.1 steps 3-6, 3.2, 3.3; [F6]
  * reduce_grads + step + gather_weights; [MDT] 四.3 order).  Enqueues four
- * kernels on `stream` and returns without synchronising:
+ * kernels on `stream` (three when the partials fit one reduce block: reduce
+ * and finish are then one launch, with the same bits) and returns without
+ * synchronising:
  *   pass 1  reduce-scatter sums, overflow flag, per-tile squared-norm
  *           partials (fp64), and the fp32 sums when the plan materialises;
  *   reduce  fixed contiguous ranges of the partials, in order;
