@@ -194,6 +194,17 @@ def _host_elems(x, elem_bytes):
     return nbytes // elem_bytes
 
 
+def _default_numel(arrays, what):
+    """The smallest element count of the tensors given (None entries
+    skipped).  A raw address carries no size, so with one among them the
+    caller must pass the count: refusing here keeps the library's size check
+    meaningful."""
+    arrays = [t for t in arrays if t is not None]
+    if not arrays or any(isinstance(t, int) for t in arrays):
+        raise ValueError(f"{what}: pass numel explicitly when an array is a raw address")
+    return min(t.numel() for t in arrays)
+
+
 def _ptr_array(items):
     return (C.c_void_p * len(items))(*[_ptr(t) for t in items])
 
@@ -285,6 +296,8 @@ def hparams(lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, max_norm=1.
 def _nbytes(t, nbytes):
     if nbytes is not None:
         return int(nbytes)
+    if isinstance(t, int):
+        raise ValueError("pass the size explicitly when a buffer is a raw address")
     return t.numel() * t.element_size() if t is not None else 0
 
 
@@ -300,8 +313,8 @@ def shard_step(plan, hp, grad_dtype, param_dtype, grads, master, exp_avg, exp_av
     gp = _ptr_array(grads) if grads is not None else None
     ev = (C.c_void_p * 4)(*phase_events) if phase_events is not None else None
     if numel is None:
-        arrays = list(grads or []) + [master, exp_avg, exp_avg_sq, params, grad_shards]
-        numel = min(t.numel() for t in arrays if t is not None and not isinstance(t, int))
+        numel = _default_numel(list(grads or []) + [master, exp_avg, exp_avg_sq, params,
+                                                    grad_shards], "zf_shard_step")
     args = StepArgs(int(grad_dtype), int(param_dtype), gp, _ptr(master), _ptr(exp_avg),
                     _ptr(exp_avg_sq), _ptr(params), _ptr(grad_shards), int(bool(grads_reduced)),
                     0, int(numel), _ptr(workspace), _nbytes(workspace, workspace_size),
@@ -321,8 +334,8 @@ def shard_step_noalloc(plan, hp, grad_dtype, param_dtype, grads, master, exp_avg
     gp = _ptr_array(grads) if grads is not None else None
     ev = (C.c_void_p * 4)(*phase_events) if phase_events is not None else None
     if numel is None:
-        arrays = list(grads or []) + [master, exp_avg, exp_avg_sq, params, grad_shards]
-        numel = min(t.numel() for t in arrays if t is not None and not isinstance(t, int))
+        numel = _default_numel(list(grads or []) + [master, exp_avg, exp_avg_sq, params,
+                                                    grad_shards], "zf_shard_step_noalloc")
     args = StepArgs(int(grad_dtype), int(param_dtype), gp, _ptr(master), _ptr(exp_avg),
                     _ptr(exp_avg_sq), _ptr(params), _ptr(grad_shards), int(bool(grads_reduced)),
                     0, int(numel), None, 0, _ptr(state), ev)
@@ -332,7 +345,7 @@ def shard_step_noalloc(plan, hp, grad_dtype, param_dtype, grads, master, exp_avg
 
 def reduce_scatter(plan, grad_dtype, grads, rs_out, stream=None, numel=None):
     if numel is None:
-        numel = min(t.numel() for t in list(grads) + [rs_out])
+        numel = _default_numel(list(grads) + [rs_out], "zf_reduce_scatter")
     _check(lib.zf_reduce_scatter(_handle(plan), int(grad_dtype), _ptr_array(grads),
                                  _ptr(rs_out), int(numel), _stream(stream)),
            "zf_reduce_scatter")
@@ -353,7 +366,7 @@ def bucket_reduce_scatter(plan, group, grad_dtype, grads, grad_shards, accumulat
                           stream=None, numel=None):
     """zf_bucket_reduce_scatter of group (bucket) `group` into grad_shards."""
     if numel is None:
-        numel = min(t.numel() for t in list(grads) + [grad_shards])
+        numel = _default_numel(list(grads) + [grad_shards], "zf_bucket_reduce_scatter")
     _check(lib.zf_bucket_reduce_scatter(_handle(plan), int(group), int(grad_dtype),
                                         _ptr_array(grads), _ptr(grad_shards), int(numel),
                                         int(bool(accumulate)), _stream(stream)),
@@ -363,14 +376,14 @@ def bucket_reduce_scatter(plan, group, grad_dtype, grads, grad_shards, accumulat
 def accumulate(grad_dtype, grad, acc, n=None, accumulate=True, stream=None):
     """zf_accumulate: acc (+)= f32(grad) over n elements (tensors or addresses)."""
     if n is None:
-        n = min(grad.numel(), acc.numel())
+        n = _default_numel([grad, acc], "zf_accumulate")
     _check(lib.zf_accumulate(int(grad_dtype), _ptr(grad), _ptr(acc), int(n),
                              int(bool(accumulate)), _stream(stream)), "zf_accumulate")
 
 
 def gather(plan, unit, dtype, shards, unit_buf, stream=None, unit_buf_numel=None):
     """zf_gather; unit_buf is a tensor, or an address with unit_buf_numel."""
-    n = unit_buf_numel if unit_buf_numel is not None else unit_buf.numel()
+    n = unit_buf_numel if unit_buf_numel is not None else _default_numel([unit_buf], "zf_gather")
     _check(lib.zf_gather(_handle(plan), int(unit), int(dtype), _ptr_array(shards),
                          _ptr(unit_buf), int(n), _stream(stream)), "zf_gather")
 
@@ -378,8 +391,8 @@ def gather(plan, unit, dtype, shards, unit_buf, stream=None, unit_buf_numel=None
 def gather_cast(plan, group, dtype, master, out, stream=None, master_numel=None,
                 out_numel=None):
     """zf_gather_cast (FSDP2 unshard of one group into `out`)."""
-    mn = master_numel if master_numel is not None else master.numel()
-    on = out_numel if out_numel is not None else out.numel()
+    mn = master_numel if master_numel is not None else _default_numel([master], "zf_gather_cast")
+    on = out_numel if out_numel is not None else _default_numel([out], "zf_gather_cast")
     _check(lib.zf_gather_cast(_handle(plan), int(group), int(dtype), _ptr(master), int(mn),
                               _ptr(out), int(on), _stream(stream)), "zf_gather_cast")
 
@@ -420,12 +433,15 @@ def offload_step(plan, hp, grad_dtype, param_dtype, grads, grad_shards, params, 
         # every per-element array counts, host ones included: h_grad holds
         # the sums that come down (4 bytes each, 2 with down16), h_params the
         # 16-bit parameters going up, the h_ state arrays fp32
-        sized = [(t, t.element_size()) for t in list(grads or []) + [grad_shards, params]
-                 if t is not None and not isinstance(t, int)]
+        dev = [t for t in list(grads or []) + [grad_shards, params] if t is not None]
+        sized = [(t, t.element_size() if not isinstance(t, int) else 1) for t in dev]
         sized += [(h_grad, 2 if down16 else 4), (h_master, 4), (h_exp_avg, 4),
                   (h_exp_avg_sq, 4), (h_params, 2)]
         counts = [_host_elems(t, eb) for t, eb in sized]
-        numel = min(c for c in counts if c is not None)
+        if any(c is None for c in counts):
+            raise ValueError("zf_offload_step: pass numel explicitly when an array is a raw "
+                             "address")
+        numel = min(counts)
     gp = _ptr_array(grads) if grads is not None else None
     a = OffloadArgs(int(grad_dtype), int(param_dtype), gp, _ptr(grad_shards), _ptr(params),
                     int(numel), _ptr(workspace), _nbytes(workspace, None), _ptr(state),
@@ -442,8 +458,10 @@ def reshard(plan_from, plan_to, src, dst, stream=None, elem_bytes=None, src_nume
             dst_numel=None):
     """zf_reshard of one per-element array (tensors, or addresses with the
     counts and elem_bytes)."""
+    if elem_bytes is None and isinstance(src, int):
+        raise ValueError("zf_reshard: pass elem_bytes when src is a raw address")
     eb = elem_bytes if elem_bytes is not None else src.element_size()
-    sn = src_numel if src_numel is not None else src.numel()
-    dn = dst_numel if dst_numel is not None else dst.numel()
+    sn = src_numel if src_numel is not None else _default_numel([src], "zf_reshard")
+    dn = dst_numel if dst_numel is not None else _default_numel([dst], "zf_reshard")
     _check(lib.zf_reshard(_handle(plan_from), _handle(plan_to), _ptr(src), int(sn), _ptr(dst),
                           int(dn), int(eb), _stream(stream)), "zf_reshard")

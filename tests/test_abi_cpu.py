@@ -394,13 +394,17 @@ def test_offload_default_size_counts_host_arrays(zf):
     ok = 0x10000
     ws = torch.zeros(Z.workspace_bytes(plan), dtype=torch.uint8)
 
+    # stand-ins for the device arrays: sized, never dereferenced
+    grads = [torch.zeros(100, dtype=torch.bfloat16) for _ in range(2)]
+    shards, params = torch.zeros(100), torch.zeros(100, dtype=torch.bfloat16)
+
     def call(down16=False, h_grad=100, h_master=100, h_avg=100, h_avg_sq=100, h_params=100):
         h = dict(h_state=np.zeros(256, np.uint8), h_grad=np.zeros(h_grad, np.float32),
                  h_master=np.zeros(h_master, np.float32), h_exp_avg=np.zeros(h_avg, np.float32),
                  h_exp_avg_sq=np.zeros(h_avg_sq, np.float32),
                  h_params=np.zeros(h_params, np.uint16))
         with pytest.raises(Z.ZfError) as e:
-            Z.offload_step(plan, hp, W.BF16, W.BF16, [ok, ok], ok, ok, ws, ok, stream=0,
+            Z.offload_step(plan, hp, W.BF16, W.BF16, grads, shards, params, ws, ok, stream=0,
                            down16=down16, **h)
         return e.value.status
 
@@ -411,6 +415,10 @@ def test_offload_default_size_counts_host_arrays(zf):
     assert call(h_grad=99) == -4
     # 16-bit sums come down into h_grad's first 2 bytes per element
     assert call(down16=True, h_grad=49) == -4
+    # a raw address carries no size: without numel the binding refuses
+    with pytest.raises(ValueError):
+        Z.offload_step(plan, hp, W.BF16, W.BF16, [ok, ok], ok, ok, ws, ok, ok, ok, ok, ok, ok,
+                       ok, stream=0)
     # an explicit numel is the caller's statement of every array's size
     with pytest.raises(Z.ZfError) as e:
         Z.offload_step(plan, hp, W.BF16, W.BF16, [ok, ok], ok, ok, ws, ok, ok, ok, ok, ok, ok,
@@ -488,3 +496,31 @@ def test_input_library_probes_refuse_before_launching():
     assert g(srcs, 1, dsts, 1, 1024, 1, 9, None) == -1
     srcs[0] = a + 4
     assert g(srcs, 1, dsts, 1, 1024, 1, 0, None) == -1
+
+
+def test_binding_refuses_unsized_raw_addresses(zf):
+    """A raw address carries no size, so the binding's default element
+    counts refuse it (ValueError before any library call) instead of
+    ignoring it and letting a short buffer pass the library's size check."""
+    Z = zf
+    import torch
+    plan = Z.plan_flat([(100, 0)], 2, W.GLOBAL_FLAT, 2)
+    hp = Z.hparams(1e-3)
+    t = torch.zeros(100)
+    ok = 0x10000
+    with pytest.raises(ValueError):
+        Z.shard_step(plan, hp, W.BF16, W.BF16, [t, ok], t, t, t, t, t, ok)
+    with pytest.raises(ValueError):
+        Z.shard_step_noalloc(plan, hp, W.BF16, W.BF16, [t, t], ok, t, t, t, ok)
+    with pytest.raises(ValueError):
+        Z.reduce_scatter(plan, W.BF16, [t, t], ok)
+    with pytest.raises(ValueError):
+        Z.bucket_reduce_scatter(plan, 0, W.BF16, [ok, t], t, False)
+    with pytest.raises(ValueError):
+        Z.accumulate(W.BF16, ok, t)
+    with pytest.raises(ValueError):
+        Z.gather(plan, 0, W.BF16, [ok, ok], ok)
+    with pytest.raises(ValueError):
+        Z.reshard(plan, plan, ok, t)
+    with pytest.raises(ValueError):
+        Z.shard_step(plan, hp, W.BF16, W.BF16, [t, t], t, t, t, t, ok, ok, numel=100)
