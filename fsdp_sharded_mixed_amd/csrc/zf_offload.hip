@@ -114,12 +114,22 @@ extern "C" int zf_offload_step(const zf_plan* plan, const zf_hparams* hp,
   };
   // down: the state block, then the sums chunk by chunk, each with an event
   std::vector<hipEvent_t> down(C, nullptr);
+  // (`st` may be the legacy stream, whose handle is null)
+  hipStream_t up = st;
   auto cleanup = [&]() {
     for (hipEvent_t& ev : down)
       if (ev) (void)hipEventDestroy(ev);
   };
-  if (!hip_ok(hipMemcpyAsync(a->h_state, a->state, sizeof(zf::DevState), hipMemcpyDeviceToHost, st)))
+  // an error after copies were enqueued: wait until none is still moving
+  // data into the caller's buffers, then report it
+  auto fail = [&]() {
+    (void)hipStreamSynchronize(st);
+    if (up != st) (void)hipStreamSynchronize(up);
+    cleanup();
     return ZF_EHIP;
+  };
+  if (!hip_ok(hipMemcpyAsync(a->h_state, a->state, sizeof(zf::DevState), hipMemcpyDeviceToHost, st)))
+    return fail();
   for (int64_t c = 0; c < C; ++c) {
     int64_t b, e;
     chunk(c, b, e);
@@ -127,27 +137,17 @@ extern "C" int zf_offload_step(const zf_plan* plan, const zf_hparams* hp,
         !hip_ok(hipMemcpyAsync(reinterpret_cast<char*>(a->h_grad) + b * eb,
                                reinterpret_cast<const char*>(a->grad_shards) + b * eb,
                                (e - b) * eb, hipMemcpyDeviceToHost, st)) ||
-        !hip_ok(hipEventRecord(down[c], st))) {
-      cleanup();
-      return ZF_EHIP;
-    }
+        !hip_ok(hipEventRecord(down[c], st)))
+      return fail();
   }
-  if (!record(2)) {
-    cleanup();
-    return ZF_EHIP;
-  }
+  if (!record(2)) return fail();
   // the state block arrived with the first chunk (same stream, earlier)
-  if (!hip_ok(hipEventSynchronize(down[0]))) {
-    cleanup();
-    return ZF_EHIP;
-  }
+  if (!hip_ok(hipEventSynchronize(down[0]))) return fail();
   zf::DevState h;
   std::memcpy(&h, a->h_state, sizeof(h));
-  // (`st` may be the legacy stream, whose handle is null)
-  hipStream_t up = st;
   if (!h.skipped && !(up = upload_stream())) {
-    cleanup();
-    return ZF_EHIP;
+    up = st;
+    return fail();
   }
   if (!h.skipped) {
     uint16_t* hp16 = static_cast<uint16_t*>(a->h_params);
@@ -155,28 +155,22 @@ extern "C" int zf_offload_step(const zf_plan* plan, const zf_hparams* hp,
     for (int64_t c = 0; c < C; ++c) {
       int64_t b, e;
       chunk(c, b, e);
-      if (!hip_ok(hipEventSynchronize(down[c]))) {
-        cleanup();
-        return ZF_EHIP;
-      }
+      if (!hip_ok(hipEventSynchronize(down[c]))) return fail();
       zf::cpu_adam_run(hp, h.gs, h.bc1, h.bc2, e - b,
                        reinterpret_cast<const char*>(a->h_grad) + b * eb,
                        down16 ? a->grad_dtype : ZF_F32, a->h_master + b, a->h_exp_avg + b,
                        a->h_exp_avg_sq + b, hp16 + b, a->param_dtype, a->n_threads);
       // up: this chunk's 16-bit parameters while the CPU takes the next one
       if (!hip_ok(hipMemcpyAsync(dp16 + 2 * b, hp16 + b, (e - b) * sizeof(uint16_t),
-                         hipMemcpyHostToDevice, up))) {
-        cleanup();
-        (void)hipStreamSynchronize(up);
-        return ZF_EHIP;
-      }
+                                 hipMemcpyHostToDevice, up)))
+        return fail();
     }
   }
   // every upload has landed before the caller's stream goes on
   const bool ok = hip_ok(hipStreamSynchronize(up)) && record(3) &&
                   hip_ok(hipStreamSynchronize(st));
+  if (!ok) return fail();
   cleanup();
-  if (!ok) return ZF_EHIP;
   fill_result(h, result);
   return ZF_OK;
 }
