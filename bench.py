@@ -957,6 +957,8 @@ def bench_workload(w, args, probe, copy_gbs, graph=True, skip_probe=True):
         hg = (counted - window) / (ms * 1e-3) / 1e9
         line["hbm_gbs_counted"] = round(hg, 2)
         line["pct_hbm_peak_counted"] = round(100 * hg / PEAK_HBM_GBS, 2)
+        # the same against the box's own best copy (1 read + 1 write) probe
+        line["pct_copy_probe_counted"] = round(100 * hg / probe["1r1w"], 2)
     if skip_probe:
         line["skipped_step_ms"] = skipped_step_ms(w, dev, one_step)
     if w.backward_rs:
@@ -971,7 +973,7 @@ def headline_summary(line):
     """The second headline configuration's figures, for the main line."""
     keep = ("ms_per_step", "value", "unit", "pct_hbm_peak", "params_updated_per_s",
             "algorithmic_bytes_per_param", "hbm_gbs_counted", "pct_hbm_peak_counted",
-            "l2_egress_gbs_counted", "kernels_ms", "roofline", "skipped_step_ms",
+            "pct_copy_probe_counted", "l2_egress_gbs_counted", "kernels_ms", "roofline", "skipped_step_ms",
             "ms_per_step_median", "ms_per_step_min", "steps", "warmup")
     out = {"workload": line["config"]["workload"], "config": line["config"]}
     out.update({k: line[k] for k in keep if k in line})
