@@ -33,7 +33,12 @@ Bars: the reduce-scatter sums bit for bit; master, exp_avg, exp_avg_sq
 within 4 ulp (relative 1e-6); the 16-bit parameters and every gathered unit
 within 1 ulp; padding bit-zero everywhere; the step result (overflow, skip,
 t, loss scale) exactly and the norm within 1e-5.  Each step reports the
-share of elements that match bit for bit.
+share of elements that match bit for bit, and beyond those bars every
+element must be bit-identical: the kernels and the oracle do the same IEEE
+binary32 operations in the same order (no contraction, correctly rounded
+division and square root, nearest-even casts), which is the notes'
+condition for identical bits (Lecture 13, 3.4), so any difference is a
+change of arithmetic order that the ulp bars alone would let through.
 """
 from concurrent.futures import ThreadPoolExecutor
 
@@ -161,6 +166,12 @@ class Tally:
         out = {k: round(self.exact[k] / self.total[k], 6) for k in self.exact}
         out["worst_ulp"] = self.worst
         return out
+
+    def assert_identical(self, what):
+        """Every compared element bit-identical to the oracle."""
+        off = {k: self.total[k] - self.exact[k] for k in self.exact
+               if self.exact[k] != self.total[k]}
+        assert not off, f"{what}: elements within the ulp bars but not bit-identical: {off}"
 
 
 def compare_f32(pool, t, ref, what, max_ulp=4):
@@ -460,6 +471,7 @@ def run_full(R, w, twin_sums=False, rs_first_step=True):
                   f"{res_d.scale_next} norm={res_d.norm:.6f} (oracle {res_o.norm:.6f}) "
                   f"coef={res_d.coef:.6f} sums {'bit-exact' if keep else '-'}; "
                   f"bit-identical shares {tally.shares()}")
+            tally.assert_identical(f"{w.name} step {k}")
     finally:
         orc.close()
     return dev, trace
