@@ -40,8 +40,9 @@ division and square root, nearest-even casts), which is the notes'
 condition for identical bits (Lecture 13, 3.4).  The one input that may
 differ is the binary32 gradient scale, rounded from a norm that the device
 sums in another fixed fp64 order; the two norms would have to straddle a
-binary32 rounding boundary of coef/(S*N) to move it (odds of order 1e-9 per
-clipped step), and for these seeds they do not.  So a difference here is a
+binary32 rounding boundary of coef/(S*N) to move it (their relative gap,
+about sqrt(Psi) * 2^-53, over binary32's 2^-23 spacing: odds of order 1e-5
+per clipped step at these sizes), and for these seeds they do not.  So a difference here is a
 change of arithmetic order that the ulp bars alone would let through.
 """
 from concurrent.futures import ThreadPoolExecutor
