@@ -308,7 +308,7 @@ def summarize_table(jsonl, out, command):
     bench prints them) written to `out`."""
     with open(jsonl) as f:
         rows = [json.loads(ln) for ln in f if ln.startswith("{")]
-    L = ["# bench.py on one MI355X: every workload (same box, one run)", "",
+    L = ["# bench.py on one MI355X: every workload (one GPU, one run)", "",
          f"command: `{command}`", "",
          "Columns: ms/step = K timed steps over K; algorithmic = the method's bytes per step "
          "(`algorithmic_bytes_per_param` x Psi) over the step time, and its share of 8 TB/s "
@@ -316,7 +316,7 @@ def summarize_table(jsonl, out, command):
          "kernel's algorithmic bytes per launch over its mean duration (HIP events in the "
          "same run), over 8 TB/s; design frac = the same kernel's actual bytes (with the "
          "global-norm barrier's re-read) over 8 TB/s; HBM/probe = the update pass's actual "
-         "bytes less the cache window's reads, per second, over the box's best "
+         "bytes less the cache window's reads, per second, over the GPU's best "
          "4-read/4-write probe; own-mix probe = the time of a kernel that moves the update "
          "pass's 30 bytes per element with no arithmetic (its sums read from HBM) over the "
          "update pass's time, on equal element counts; counted HBM = FETCH_SIZE + "
@@ -482,12 +482,12 @@ def dram32_for(workload, kernel="zf_pass2", per="launch"):
 
 
 # probe shapes (quads per lane, resident blocks per CU, 0: no limit); the
-# best one per access mix is the box's figure for that mix
+# best one per access mix is this GPU's figure for that mix
 PROBE_SHAPES = ((1, 0), (2, 0), (1, 3), (1, 4), (2, 3), (2, 4))
 
 
 def stream_probes(reps=10):
-    """GB/s of the box for streams in the step kernels' access pattern: a
+    """GB/s of this GPU for streams in the step kernels' access pattern: a
     copy (1 read, 1 write), the update pass's mix of 4 reads and 4 writes,
     and 8 reads + 1 write (pass 1 at N = 8).  Each mix is timed with the
     fixed-shape zfi_stream_probe and with zfi_stream_probe_shaped in every
@@ -957,7 +957,7 @@ def bench_workload(w, args, probe, copy_gbs, graph=True, skip_probe=True):
         hg = (counted - window) / (ms * 1e-3) / 1e9
         line["hbm_gbs_counted"] = round(hg, 2)
         line["pct_hbm_peak_counted"] = round(100 * hg / PEAK_HBM_GBS, 2)
-        # the same against the box's own best copy (1 read + 1 write) probe
+        # the same against this GPU's own best copy (1 read + 1 write) probe
         line["pct_copy_probe_counted"] = round(100 * hg / probe["1r1w"], 2)
     if skip_probe:
         line["skipped_step_ms"] = skipped_step_ms(w, dev, one_step)
@@ -1056,7 +1056,7 @@ def main():
     torch.cuda.set_device(0)
     print(f"bench: {w.name} Psi={w.psi:,} N={w.n_ranks} stage={w.stage}", file=sys.stderr,
           flush=True)
-    # this box's plain device-copy bandwidth (1 GiB read + 1 GiB written),
+    # this GPU's plain device-copy bandwidth (1 GiB read + 1 GiB written),
     # the practical ceiling the step's streams are compared against
     src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda:0")
     dst = torch.empty_like(src)

@@ -15,7 +15,7 @@ constexpr uint64_t kPlanMagic = 0x7a665f706c616e31ull;  // "zf_plan1"
 // kLevel2Blocks blocks reduces fixed, contiguous ranges of them; a single
 // block finishes.  The tiling depends only on the plan, so the norm's
 // rounding does not depend on the device or the run.
-// Tiling (measured on MI355X, in-process A/B over builds on one box):
+// Tiling (measured on MI355X, in-process A/B over builds on one GPU):
 //  - pass 1 streams the N replicas with the non-temporal load hint, one
 //    8-byte quad per lane per replica (16-byte loads of quad pairs cost
 //    +50% at N = 8, where the sums' stores become strided, and +8% at N = 2).  With

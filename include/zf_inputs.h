@@ -46,12 +46,12 @@ uint64_t zfi_stream_output(uint64_t seed, uint64_t stream, uint64_t j);
  * non-temporal 16-byte stores per lane, 4-element quads 256 apart per lane,
  * one tile of 512 quads per block), so that a plain copy (1 source, 1
  * destination) and the update pass's mix (4 and 4) can be timed on the
- * box that runs the step.  n_src and n_dst in 1..8; every pointer 16-byte
+ * GPU that runs the step.  n_src and n_dst in 1..8; every pointer 16-byte
  * aligned; n a multiple of 4.  Returns 0, -1 (bad argument) or -5. */
 int zfi_stream_probe(const float* const* src, int32_t n_src, float* const* dst, int32_t n_dst,
                      int64_t n, void* stream_handle);
 
-/* The same probe in a chosen shape, to find the box's best figure for an
+/* The same probe in a chosen shape, to find the GPU's best figure for an
  * access mix: `quads` (1, 2 or 4) quads per lane per 256-thread block,
  * non-temporal loads as well as stores, and at most `blocks_per_cu` (1..8;
  * 0: no limit) resident blocks per compute unit.  Arguments otherwise as

@@ -1,5 +1,6 @@
 """Performance smoke: the kernels keep their measured bandwidth, relative to
-the same box's own stream ceiling (so box-to-box variance does not matter).
+the same GPU's own stream ceiling (so machine-to-machine variance does not
+matter).
 
 The ceiling of an access mix is the best of the fixed-shape zfi_stream_probe
 and zfi_stream_probe_shaped in six shapes, measured in the same process.
@@ -9,7 +10,7 @@ on the 73M workload (materialised sums) and the 654M one (recomputed sums);
 73M's pass 1 (8 replicas in, the fp32 sums out) 85% of the best
 8-read/1-write figure.  They run at 97% or more today.  The update pass
 must also reach an absolute 70% of the MI355X's 8 TB/s on the bytes it
-moves, so that a box-wide slowdown that lowers the probes too (placement,
+moves, so that a device-wide slowdown that lowers the probes too (placement,
 clocks) still fails; it runs at 78-86% today.  And it must reach 90% of
 zfi_update_mix_probe, a kernel that moves the update pass's own 30 bytes
 per element (the fp32 sums, or two 16-bit replicas, in; the state in and
