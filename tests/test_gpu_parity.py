@@ -335,29 +335,6 @@ def test_phase_events_and_no_sync(R):
     assert dev.result().t == 1
 
 
-def test_stream_probe_sums(R):
-    """The bench's bandwidth probe computes what it claims (dst = sum of the
-    sources), so its timing measures real loads and stores."""
-    from fsdp_sharded_mixed_amd import inputs as I
-    g = torch.Generator(device="cpu").manual_seed(3)
-    for r, wr in ((1, 1), (4, 4), (8, 1), (2, 2)):
-        n = 4 * 5000
-        src = [torch.randn(n, generator=g).cuda() for _ in range(r)]
-        dst = [torch.zeros(n, device="cuda") for _ in range(wr)]
-        I.stream_probe(src, dst)
-        want = src[0].clone()
-        for t in src[1:]:
-            want = want + t
-        for d in dst:
-            assert torch.equal(d, want)
-        for quads, cap in ((1, 0), (2, 4), (4, 3)):
-            for d in dst:
-                d.zero_()
-            I.stream_probe_shaped(src, dst, quads, cap)
-            for d in dst:
-                assert torch.equal(d, want), (r, wr, quads, cap)
-
-
 @pytest.mark.parametrize("dtype", [W.F16, W.BF16])
 def test_rs_pair_sweep(R, dtype):
     """The N = 2 reduce-scatter over every 16-bit value of replica 0 against
