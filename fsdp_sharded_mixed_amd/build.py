@@ -10,6 +10,9 @@ libzf_window_test.so
                  stores (non-temporal below the window, cache-allocating in
                  it) and the update pass's backward walk on small plans
 
+Every translation unit compiles on its own (in parallel) into _build/ at the
+repository root, and each library is linked from its objects.
+
 Flags that matter for the arithmetic contract:
   -ffp-contract=off                        no a*b+c -> fma fusion
   -fhip-fp32-correctly-rounded-divide-sqrt correctly rounded / and sqrtf
@@ -18,6 +21,7 @@ fp32 denormals are kept (the HIP default; nothing flushes them).
 """
 import os
 import subprocess
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -29,36 +33,65 @@ LIB_INPUTS = os.path.join(PKG, "libzf_inputs.so")
 LIB_WINDOW_TEST = os.path.join(PKG, "libzf_window_test.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+BUILD_DIR = os.path.join(ROOT, "_build")  # objects; the libraries go in-tree
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-command-line-argument", "-pthread",
     "-I", INCLUDE, "-I", CSRC,
 ]
+LINK = ["--offload-arch=gfx950", "-shared", "-fPIC", "-pthread"]
 
 
-def _hipcc(out, sources, host_sources=(), defines=()):
-    """Link `sources` (HIP) and `host_sources` (plain host C++) into `out`."""
-    tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, *defines, "-o", tmp]
-    if host_sources:
-        cmd += ["-x", "c++", *host_sources]
-    cmd += ["-x", "hip", *sources]
+def _run(cmd):
     subprocess.run(cmd, check=True)
-    os.replace(tmp, out)
-    return out
 
 
-def build():
-    """Build the libraries; returns their paths."""
-    zf = _hipcc(LIB_ZF, [os.path.join(CSRC, f) for f in
-                         ("zf_step.hip", "zf_backward.hip", "zf_gather.hip", "zf_offload.hip")],
-                [os.path.join(CSRC, f) for f in ("zf_plan.cpp", "zf_cpu_adam.cpp")])
-    inputs = _hipcc(LIB_INPUTS, [os.path.join(CSRC, "zf_inputs.hip")])
-    window = _hipcc(LIB_WINDOW_TEST, [os.path.join(CSRC, "zf_step.hip")],
-                    [os.path.join(CSRC, "zf_plan.cpp")], defines=["-DZF_TEST_CACHED_SUMS_MB=1"])
-    return zf, inputs, window
+def _object(src, lang, defines=(), tag=""):
+    """(output, command) compiling one source (lang "hip" or "c++")."""
+    name = os.path.splitext(os.path.basename(src))[0]
+    out = os.path.join(BUILD_DIR, f"{name}{tag}.o")
+    return out, [HIPCC, *FLAGS, *defines, "-c", "-x", lang, src, "-o", out]
+
+
+def _libraries():
+    """Each library: (path, [(source, lang, defines, tag), ...])."""
+    def c(f):
+        return os.path.join(CSRC, f)
+    step = [(c(f), "hip", (), "") for f in
+            ("zf_step.hip", "zf_backward.hip", "zf_gather.hip", "zf_offload.hip")]
+    host = [(c(f), "c++", (), "") for f in ("zf_plan.cpp", "zf_cpu_adam.cpp")]
+    window = ("-DZF_TEST_CACHED_SUMS_MB=1",)
+    return [
+        (LIB_ZF, step + host),
+        (LIB_INPUTS, [(c("zf_inputs.hip"), "hip", (), "")]),
+        (LIB_WINDOW_TEST, [(c("zf_step.hip"), "hip", window, "_window"),
+                           (c("zf_plan.cpp"), "c++", window, "_window")]),
+    ]
+
+
+def build(jobs=None):
+    """Compile every translation unit (in parallel) and link the libraries;
+    returns their paths."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    libs = _libraries()
+    units = {}
+    for _, srcs in libs:
+        for src, lang, defines, tag in srcs:
+            out, cmd = _object(src, lang, defines, tag)
+            units[out] = cmd
+    jobs = jobs or min(8, os.cpu_count() or 1, len(units))
+    with ThreadPoolExecutor(jobs) as ex:
+        list(ex.map(_run, units.values()))  # raises the first failure
+    paths = []
+    for path, srcs in libs:
+        objs = [_object(src, lang, defines, tag)[0] for src, lang, defines, tag in srcs]
+        tmp = path + ".tmp"
+        _run([HIPCC, *LINK, *objs, "-o", tmp])
+        os.replace(tmp, path)
+        paths.append(path)
+    return tuple(paths)
 
 
 if __name__ == "__main__":
